@@ -1,0 +1,239 @@
+"""Benchmark of the exact blockwise attention hot path on one MI355X.
+
+One step = one pass of the whole forward hot path over one batch of synthetic input.
+For the headline workload (a Qwen2.5-7B-shaped GQA layer, 28 query / 4 key-value heads
+x 128, one rank's share of a 4-way Ulysses split at 32K tokens):
+
+    ulysses_permute(q), (k), (v)   sequence shards -> rank 0's head shard
+    attn_fwd                       causal, GQA 7:1, S = 32768, bf16 in, fp32 accumulate
+    ulysses_permute(o)             head shard -> sequence shards
+
+Prints ONE JSON line.  ``value`` is the algorithmic attention TFLOP/s of the whole step
+(inputs resident in HBM; flops use the causal S^2/2 convention, 2 flops per MAC);
+``roofline`` reports the attention kernel alone, timed with HIP events on the stream it
+runs on; ``cpu_baseline`` times the fp64 CPU oracle on a bounded sample of the same
+workload.  Other workloads can be selected with --workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+METRIC = "causal bf16 attention fwd TFLOP/s + % of MFMA peak at S=32K, 1 GPU"
+PEAK_BF16_TFLOPS = 2516.6     # 256 CU x 2.4 GHz x 4096 flop/clk/CU (dense bf16 MFMA)
+PEAK_F32_TFLOPS = 157.3
+PEAK_HBM_GBPS = 8000.0
+
+
+def visible_pairs(Sq, Skv, num_chunks, causal, q_offset, kv_offset):
+    """(query, key) pairs counted for flops: all pairs if non-causal; with the causal
+    mask, chunk by chunk with the continuous S^2/2 convention (a chunk entirely in the
+    future counts 0, one entirely in the past counts Sq*L, a straddling one its area)."""
+    if not causal:
+        return float(Sq) * Skv
+    L = Skv // num_chunks
+
+    def G(x, c, m):  # integral of clamp(t - c, 0, m) dt from -inf to x
+        t = x - c
+        if t <= 0:
+            return 0.0
+        if t <= m:
+            return 0.5 * t * t
+        return 0.5 * m * m + (t - m) * m
+
+    total = 0.0
+    for ch in range(num_chunks):
+        c = kv_offset + ch * L
+        total += G(q_offset + Sq, c, L) - G(q_offset, c, L)
+    return total
+
+
+def attn_flops(B, Hq, Sq, Skv, D, num_chunks=1, causal=True, q_offset=0, kv_offset=0):
+    return 4.0 * B * Hq * D * visible_pairs(Sq, Skv, num_chunks, causal, q_offset, kv_offset)
+
+
+def blas_threads() -> int:
+    try:
+        from threadpoolctl import threadpool_info
+        n = [d.get("num_threads", 0) for d in threadpool_info() if d.get("user_api") == "blas"]
+        if n:
+            return int(max(n))
+    except Exception:
+        pass
+    return len(os.sched_getaffinity(0))
+
+
+def cpu_baseline(w, budget_s: float = 15.0):
+    """Time the fp64 oracle on blocks of query rows spread over the sequence."""
+    import oracle
+    import seeded_inputs as si
+
+    B, Hq, Sq, D = w.q_shape
+    Skv = w.kv_shape[2]
+    rng = np.random.Generator(np.random.PCG64(w.seed + 7))
+    k = rng.standard_normal((1, 1, Skv, D), dtype=np.float32)
+    v = rng.standard_normal((1, 1, Skv, D), dtype=np.float32)
+    k64 = si.bf16_bits_to_f32(si.bf16_bits(k)).astype(np.float64)
+    v64 = si.bf16_bits_to_f32(si.bf16_bits(v)).astype(np.float64)
+    blk = 128
+    starts = list(range(0, Sq, max(blk, Sq // 64)))
+    rng.shuffle(starts)
+    done_flops, rows, t0 = 0.0, 0, time.perf_counter()
+    for a in starts:
+        qb = si.bf16_bits_to_f32(si.bf16_bits(
+            rng.standard_normal((1, 1, blk, D), dtype=np.float32))).astype(np.float64)
+        oracle.full_attention(qb, k64, v64, causal=w.causal, q_offset=w.q_offset + a,
+                              kv_offset=w.kv_offset)
+        done_flops += attn_flops(1, 1, blk, Skv, D, 1, w.causal, w.q_offset + a, w.kv_offset)
+        rows += blk
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {
+        "value": done_flops / dt / 1e12, "unit": "TFLOP/s", "cores": blas_threads(),
+        "kind": "oracle",
+        "sample": f"{rows} query rows ({len(starts) and rows // blk} blocks of {blk}, spread "
+                  f"over the sequence) of one head against the full {Skv}-key causal context, "
+                  f"fp64 NumPy, {dt:.1f} s",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="qwen7b_ulysses4_rank0_32k")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: every box here has a single MI355X, and the multi-GPU "
+              "ring/Ulysses exchange is not part of this build (run with --gpus 1).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import long_context_exact_tiled_amd as ra
+    import seeded_inputs as si
+
+    w = si.WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    B, Hq, Sq, D = w.q_shape
+    Skv = w.kv_shape[2]
+
+    def to_dev(x):
+        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).to(dev) \
+            if w.dtype == "bf16" else torch.from_numpy(x).to(dev)
+
+    flops = attn_flops(B, Hq, Sq, Skv, D, w.num_chunks, w.causal, w.q_offset, w.kv_offset)
+    extra = {}
+    if w.ulysses_P:
+        qs, ks, vs = (to_dev(x) for x in si.draw_ulysses_sources(w.seed))
+        P, r = w.ulysses_P, w.ulysses_rank
+        o_seq = torch.zeros_like(qs)
+        qh = torch.empty(qs.shape[2] // P, P * qs.shape[1], D, dtype=qs.dtype, device=dev)
+        kh = torch.empty(ks.shape[2] // P, P * ks.shape[1], D, dtype=ks.dtype, device=dev)
+        vh = torch.empty_like(kh)
+        o = torch.empty_like(qh)
+        lse = torch.empty(1, qh.shape[0], qh.shape[1], dtype=torch.float32, device=dev)
+        moved = 2 * (qh.numel() + 2 * kh.numel() + o.numel()) * qh.element_size()
+
+        def pre():
+            ra.ulysses_permute(qs, P, r, 0, out=qh)
+            ra.ulysses_permute(ks, P, r, 0, out=kh)
+            ra.ulysses_permute(vs, P, r, 0, out=vh)
+
+        def attn():
+            ra.attn_fwd(qh.unsqueeze(0), kh.unsqueeze(0), vh.unsqueeze(0), causal=True,
+                        out=o.unsqueeze(0), lse=lse)
+
+        def post():
+            ra.ulysses_permute(o, P, r, 1, out=o_seq)
+    else:
+        q, k, v = (to_dev(x) for x in si.draw_qkv(w.seed, w.q_shape, w.kv_shape, w.dtype))
+        o = torch.empty_like(q)
+        lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+        moved = 0
+
+        def pre():
+            pass
+
+        def attn():
+            ra.attn_fwd(q, k, v, causal=w.causal, num_chunks=w.num_chunks,
+                        start_chunk=w.start_chunk, q_offset=w.q_offset, kv_offset=w.kv_offset,
+                        out=o, lse=lse)
+
+        def post():
+            pass
+
+    stream = torch.cuda.current_stream(dev)
+    for _ in range(args.warmup):
+        pre(); attn(); post()
+    torch.cuda.synchronize()
+
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    t_start.record(stream)
+    for s in range(args.steps):
+        ev[s][0].record(stream)
+        pre()
+        ev[s][1].record(stream)
+        attn()
+        ev[s][2].record(stream)
+        post()
+        ev[s][3].record(stream)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_end)
+    ms_step = total_ms / args.steps
+    attn_ms = [e[1].elapsed_time(e[2]) for e in ev]
+    perm_ms = [e[0].elapsed_time(e[1]) + e[2].elapsed_time(e[3]) for e in ev]
+    attn_avg = float(np.mean(attn_ms))
+    achieved = flops / (attn_avg * 1e-3) / 1e12
+    peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
+    if moved:
+        extra["permute_ms_per_step"] = float(np.mean(perm_ms))
+        extra["permute_GBps"] = moved / (np.mean(perm_ms) * 1e-3) / 1e9
+    extra["attn_fwd_ms"] = attn_avg
+    extra["attn_fwd_ms_min"] = float(np.min(attn_ms))
+    extra["attn_flops"] = flops
+
+    line = {
+        "metric": METRIC,
+        "value": flops / (ms_step * 1e-3) / 1e12,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic: N(0,1) from PCG64(seed), rounded to bf16 (RNE)",
+        "config": {"workload": w.name, "q_shape": list(w.q_shape), "kv_shape": list(w.kv_shape),
+                   "causal": w.causal, "num_chunks": w.num_chunks, "start_chunk": w.start_chunk,
+                   "q_offset": w.q_offset, "ulysses_P": w.ulysses_P,
+                   "ulysses_rank": w.ulysses_rank, "parallelism": "1 GPU (one rank's share)"},
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
+                     "frac": achieved / peak, "traffic": None, "kernel": "attn_fwd"},
+        "cpu_baseline": None,
+        **extra,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

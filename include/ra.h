@@ -1,0 +1,189 @@
+/*
+ * ra.h -- C ABI of libra: exact blockwise (ring) softmax attention on MI355X (gfx950).
+ *
+ * Sources (page title, host), cited by section below:
+ *   [P1] "ms-swift支持Ulysses与Ring-Attention降低长文本显存占用" (bjdmk.com.cn)
+ *   [P2] "Ulysses与Ring-Attention序列并行技术详解" (cnvsn.com)
+ *   [P4] "ms-swift集成FlashAttention 2/3，长文本训练更高效" (maplevalley.com.cn)
+ *
+ * General rules for every entry point
+ * -----------------------------------
+ * - Tensors are described by ra_tensor: a device pointer, a dtype, a rank and
+ *   per-axis shape and stride counted in ELEMENTS.  The innermost stride must be 1.
+ *   Every data pointer must be 16-byte aligned and every outer stride must be a
+ *   whole number of 16-byte units (rows are moved with 16-byte vector accesses).
+ * - The caller owns and allocates every buffer (inputs, outputs, workspace).  The
+ *   library allocates nothing, keeps no global state and never synchronises.
+ * - Work is enqueued on `stream` (a hipStream_t; NULL is the null stream).  Outputs
+ *   are valid once the stream's work has completed.  Inputs must stay alive and
+ *   unmodified until then.  Calls are thread-safe.
+ * - The return value is a ra_status.  Argument errors (negative codes other than
+ *   RA_ERR_HIP) are detected on the host before anything is enqueued, so nothing is
+ *   written on error.  RA_ERR_HIP reports a failed kernel launch.  No C++ exception
+ *   crosses this boundary.
+ * - The *_validate functions run the same host-side checks without touching the
+ *   device, so they can be called on a machine with no GPU.
+ */
+#ifndef RA_H_
+#define RA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define RA_VERSION 100 /* 0.1.0 */
+#define RA_MAX_MERGE_PARTS 64
+
+typedef enum {
+  RA_OK = 0,
+  RA_ERR_NULL = -1,        /* a required pointer is NULL */
+  RA_ERR_DTYPE = -2,       /* dtype not allowed for this argument or mismatched */
+  RA_ERR_SHAPE = -3,       /* ranks or extents inconsistent */
+  RA_ERR_STRIDE = -4,      /* innermost stride != 1, negative/overlapping strides */
+  RA_ERR_ALIGN = -5,       /* pointer or stride not a multiple of 16 bytes */
+  RA_ERR_RANGE = -6,       /* a scalar parameter out of range */
+  RA_ERR_UNSUPPORTED = -7, /* valid request this build does not implement */
+  RA_ERR_HIP = -8,         /* kernel launch failed */
+  RA_ERR_WORKSPACE = -9    /* workspace missing or smaller than required */
+} ra_status;
+
+typedef enum { RA_F32 = 0, RA_BF16 = 1 } ra_dtype;
+
+typedef struct {
+  void *data;        /* device pointer, 16-byte aligned */
+  int32_t dtype;     /* ra_dtype */
+  int32_t ndim;      /* 1..4 */
+  int64_t shape[4];  /* extents of the first ndim axes */
+  int64_t stride[4]; /* element strides; stride[ndim-1] must be 1 */
+} ra_tensor;
+
+typedef struct {
+  uint32_t struct_size; /* sizeof(ra_attn_params); lets the struct grow */
+  int32_t causal;       /* 0: every key visible; 1: key j visible to query i iff
+                           kv_offset + j <= q_offset + i (global positions) */
+  int32_t num_chunks;   /* P >= 1: the key axis is split into P equal chunks */
+  int32_t start_chunk;  /* first chunk visited; order (start + t) mod P */
+  int64_t q_offset;     /* global position of query row 0 (>= 0) */
+  int64_t kv_offset;    /* global position of key row 0 (>= 0) */
+  float scale;          /* score scale; <= 0 selects 1/sqrt(D) */
+} ra_attn_params;
+
+typedef void *ra_stream; /* a hipStream_t */
+
+/*
+ * ra_attn_fwd -- exact softmax attention of a local query block over P key/value
+ * chunks visited in ring order, carrying the running row max and exponential sum
+ * (log-sum-exp) from chunk to chunk.
+ *
+ * Defines: o = softmax(scale * q k^T) v over the visible keys, lse = natural log of
+ * the row's sum of exp(scale * q k^T).  [P2] listing ulysses_attention_forward (the
+ * full softmax of a local Q against every key, scale 1/sqrt(head dim), [B,H,L,D]
+ * layout); [P2] listing ring_attention_forward and [P1] section
+ * "Ring-Attention：面向大规模部署的工程利器" (a device holds one chunk at a time,
+ * visits all P chunks and folds each into log-space running statistics); [P4]
+ * section "FlashAttention 如何破局？不只是融合内核" (tiles on chip, online max and
+ * normaliser, only the output written back).  Causal masking and grouped heads are
+ * not on the pages; their meaning is fixed by ra_attn_params above and the mapping
+ * below.
+ *
+ * q   [B, Hq, Sq, D]   RA_F32 or RA_BF16
+ * k,v [B, Hkv, Skv, D] same dtype as q; Hq % Hkv == 0; query head h reads
+ *                      key/value head h / (Hq / Hkv); Skv % num_chunks == 0
+ * o   [B, Hq, Sq, D]   dtype of q, or RA_F32 (e.g. partials for ra_lse_merge)
+ * lse [B, Hq, Sq]      RA_F32
+ * D must be 64 or 128 (else RA_ERR_UNSUPPORTED).  A row with no visible key gets
+ * o = 0 and lse = -inf.  Sq == 0 or B*Hq == 0 is a no-op.  o must not overlap q, k, v.
+ * Chunks with no visible key (causal) are skipped; skipping is exact.
+ * Deterministic: the same inputs give bitwise the same outputs.
+ */
+int ra_attn_fwd(const ra_tensor *q, const ra_tensor *k, const ra_tensor *v,
+                const ra_attn_params *p, ra_tensor *o, ra_tensor *lse, ra_stream stream);
+int ra_attn_fwd_validate(const ra_tensor *q, const ra_tensor *k, const ra_tensor *v,
+                         const ra_attn_params *p, const ra_tensor *o, const ra_tensor *lse);
+
+/*
+ * ra_lse_merge -- combine n partial results (o_i, lse_i) of the same queries over
+ * disjoint key sets into the result over their union.
+ *
+ * Defines ([P1] section "Ring-Attention：面向大规模部署的工程利器": global max of the
+ * local maxima, then the global normaliser Z of all exponentials shifted by it):
+ *   m = max_i lse_i, lse = m + ln sum_i exp(lse_i - m), o = sum_i exp(lse_i - lse) o_i.
+ * A partial with lse = -inf has weight 0; if all are -inf the row gets o = 0,
+ * lse = -inf.
+ *
+ * o_parts   array of n tensors [B, H, S, D], RA_F32 or RA_BF16, all the same shape,
+ *           dtype and strides
+ * lse_parts array of n tensors [B, H, S], RA_F32, all the same strides
+ * o         [B, H, S, D] RA_F32 or RA_BF16;  lse [B, H, S] RA_F32
+ * 1 <= n <= RA_MAX_MERGE_PARTS.  o (lse) may be the very same view as one of the
+ * o_parts (lse_parts) -- in place; any other overlap is undefined.  D: any multiple of
+ * 8 up to 256.
+ */
+int ra_lse_merge(int32_t n, const ra_tensor *o_parts, const ra_tensor *lse_parts, ra_tensor *o,
+                 ra_tensor *lse, ra_stream stream);
+int ra_lse_merge_validate(int32_t n, const ra_tensor *o_parts, const ra_tensor *lse_parts,
+                          const ra_tensor *o, const ra_tensor *lse);
+
+/*
+ * ra_ulysses_permute -- the local layout step of Ulysses sequence parallelism:
+ * sequence shards <-> head shards (a pure element move, bit-exact).
+ *
+ * [P4] section "Ulysses：强互联下的高速通路": the sequence is cut into per-device
+ * shards [B, S_local] x N; an all-to-all before attention gives each device the
+ * whole sequence, another after it restores the output's sequence order.  Which
+ * axis is traded is not on the pages; here it is the head axis.
+ *
+ * dir = 0 (sequence -> head):
+ *   src [P, S/P, H, D]  (shard s, token t of the shard, head, dim)
+ *   dst [H/P, S, D]     heads rank*H/P .. of the whole sequence, tokens in shard
+ *                       order: dst[h', s*(S/P) + t, :] = src[s, t, rank*H/P + h', :]
+ *   rank = -1 does every rank at once: dst [P, H/P, S, D].
+ * dir = 1 (head -> sequence): the inverse; src is [H/P, S, D] (or [P, H/P, S, D] with
+ *   rank = -1) and only the head slice of `rank` in dst [P, S/P, H, D] is written.
+ * H % P == 0; src and dst have the same dtype (RA_F32 or RA_BF16) and must not
+ * overlap; D * element size must be a multiple of 16 bytes.
+ */
+int ra_ulysses_permute(const ra_tensor *src, ra_tensor *dst, int32_t P, int32_t rank, int32_t dir,
+                       ra_stream stream);
+int ra_ulysses_permute_validate(const ra_tensor *src, const ra_tensor *dst, int32_t P, int32_t rank,
+                                int32_t dir);
+
+/*
+ * ra_attn_bwd -- gradients dq, dk, dv of L = sum(dout * o) for the attention of
+ * ra_attn_fwd, recomputing the attention weights from the saved lse instead of
+ * storing them ([P4] section "为什么传统注意力这么“吃”显存？": the backward pass either
+ * keeps the intermediates or recomputes them).  The gradient formulas are the
+ * textbook ones (not on the pages): P = exp(scale q k^T - lse), D_i = rowsum(dout*o),
+ * dv = P^T dout, dS = P * (dout v^T - D), dq = scale dS k, dk = scale dS^T q; with
+ * grouped heads dk, dv sum over the query heads of a group.
+ *
+ * q, o, dout [B, Hq, Sq, D]; k, v [B, Hkv, Skv, D]; all RA_BF16 (RA_F32 returns
+ * RA_ERR_UNSUPPORTED in this build); lse [B, Hq, Sq] RA_F32 from ra_attn_fwd with
+ * the same p.  dq like q, dk and dv like k, same dtype as q.  The ring parameters
+ * fix the order in which dq accumulates over chunks.  Outputs must not overlap the
+ * inputs.  workspace: device memory of at least ra_attn_bwd_workspace_size bytes,
+ * 256-byte aligned, overwritten.  Deterministic.
+ */
+int ra_attn_bwd(const ra_tensor *q, const ra_tensor *k, const ra_tensor *v, const ra_tensor *o,
+                const ra_tensor *dout, const ra_tensor *lse, const ra_attn_params *p,
+                ra_tensor *dq, ra_tensor *dk, ra_tensor *dv, void *workspace,
+                size_t workspace_bytes, ra_stream stream);
+int ra_attn_bwd_validate(const ra_tensor *q, const ra_tensor *k, const ra_tensor *v,
+                         const ra_tensor *o, const ra_tensor *dout, const ra_tensor *lse,
+                         const ra_attn_params *p, const ra_tensor *dq, const ra_tensor *dk,
+                         const ra_tensor *dv);
+/* Bytes of workspace ra_attn_bwd needs for these shapes (0 if the shapes are invalid). */
+size_t ra_attn_bwd_workspace_size(const ra_tensor *q, const ra_tensor *k, const ra_attn_params *p);
+
+/* Static message for a status code (never NULL). */
+const char *ra_status_string(int status);
+/* RA_VERSION of the loaded library. */
+int ra_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* RA_H_ */

@@ -1,0 +1,292 @@
+"""Exact blockwise (ring) softmax attention on MI355X -- Python binding of libra.
+
+Every step of the computation runs in libra's gfx950 HIP kernels; this module only
+marshals torch tensors (device memory) and the current HIP stream into the C ABI
+declared in ``include/ra.h``.  There is no fallback: if ``libra.so`` is missing or a
+call fails, an exception is raised.
+
+Calls (names as in the C ABI, without the ``ra_`` prefix):
+
+* ``attn_fwd(q, k, v, causal=..., num_chunks=..., start_chunk=..., q_offset=...,
+  kv_offset=..., scale=...) -> (o, lse)``
+* ``lse_merge(o_parts, lse_parts) -> (o, lse)``
+* ``ulysses_permute(src, P, rank, dir) -> dst``
+* ``attn_bwd(q, k, v, o, dout, lse, ...) -> (dq, dk, dv)``
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional, Sequence, Tuple
+
+import torch
+
+__all__ = [
+    "attn_fwd", "lse_merge", "ulysses_permute", "attn_bwd", "attn_bwd_workspace_size",
+    "attn_fwd_validate", "lse_merge_validate", "ulysses_permute_validate", "attn_bwd_validate",
+    "status_string", "version", "lib", "LIB_PATH", "RaError", "STATUS",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libra.so")
+
+STATUS = {
+    0: "RA_OK", -1: "RA_ERR_NULL", -2: "RA_ERR_DTYPE", -3: "RA_ERR_SHAPE", -4: "RA_ERR_STRIDE",
+    -5: "RA_ERR_ALIGN", -6: "RA_ERR_RANGE", -7: "RA_ERR_UNSUPPORTED", -8: "RA_ERR_HIP",
+    -9: "RA_ERR_WORKSPACE",
+}
+RA_F32, RA_BF16 = 0, 1
+MAX_MERGE_PARTS = 64
+
+
+class RaError(RuntimeError):
+    """A libra call returned a non-zero status."""
+
+    def __init__(self, status: int, message: str):
+        super().__init__(message)
+        self.status = status
+        self.name = STATUS.get(status, str(status))
+
+
+class RaTensor(ctypes.Structure):
+    _fields_ = [("data", ctypes.c_void_p), ("dtype", ctypes.c_int32), ("ndim", ctypes.c_int32),
+                ("shape", ctypes.c_int64 * 4), ("stride", ctypes.c_int64 * 4)]
+
+
+class RaAttnParams(ctypes.Structure):
+    _fields_ = [("struct_size", ctypes.c_uint32), ("causal", ctypes.c_int32),
+                ("num_chunks", ctypes.c_int32), ("start_chunk", ctypes.c_int32),
+                ("q_offset", ctypes.c_int64), ("kv_offset", ctypes.c_int64),
+                ("scale", ctypes.c_float)]
+
+
+_LIB = None
+_P = ctypes.POINTER
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libra.so (raises if it has not been built)."""
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"libra.so not found at {LIB_PATH}; build it with "
+                               "`python -m long_context_exact_tiled_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        T, PP = _P(RaTensor), _P(RaAttnParams)
+        vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+        sigs = {
+            "ra_attn_fwd": [T, T, T, PP, T, T, vp],
+            "ra_attn_fwd_validate": [T, T, T, PP, T, T],
+            "ra_lse_merge": [i32, T, T, T, T, vp],
+            "ra_lse_merge_validate": [i32, T, T, T, T],
+            "ra_ulysses_permute": [T, T, i32, i32, i32, vp],
+            "ra_ulysses_permute_validate": [T, T, i32, i32, i32],
+            "ra_attn_bwd": [T, T, T, T, T, T, PP, T, T, T, vp, sz, vp],
+            "ra_attn_bwd_validate": [T, T, T, T, T, T, PP, T, T, T],
+            "ra_attn_bwd_workspace_size": [T, T, PP],
+            "ra_status_string": [ctypes.c_int],
+            "ra_version": [],
+        }
+        for name, args in sigs.items():
+            fn = getattr(L, name)
+            fn.argtypes = args
+            fn.restype = ctypes.c_int
+        L.ra_attn_bwd_workspace_size.restype = ctypes.c_size_t
+        L.ra_status_string.restype = ctypes.c_char_p
+        _LIB = L
+    return _LIB
+
+
+def status_string(status: int) -> str:
+    return lib().ra_status_string(int(status)).decode()
+
+
+def version() -> int:
+    return int(lib().ra_version())
+
+
+def _check(status: int):
+    if status != 0:
+        raise RaError(status, status_string(status))
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return RA_F32
+    if t.dtype == torch.bfloat16:
+        return RA_BF16
+    raise RaError(-2, f"RA_ERR_DTYPE: unsupported torch dtype {t.dtype}")
+
+
+def desc(t: torch.Tensor) -> RaTensor:
+    """ra_tensor view of a torch tensor (no copy)."""
+    if t.dim() > 4 or t.dim() < 1:
+        raise RaError(-3, "RA_ERR_SHAPE: tensors must have 1..4 dimensions")
+    d = RaTensor()
+    d.data = t.data_ptr() if t.numel() else None
+    d.dtype = _dtype_code(t)
+    d.ndim = t.dim()
+    for i in range(t.dim()):
+        d.shape[i] = t.shape[i]
+        d.stride[i] = t.stride(i)
+    return d
+
+
+def _params(causal, num_chunks, start_chunk, q_offset, kv_offset, scale) -> RaAttnParams:
+    p = RaAttnParams()
+    p.struct_size = ctypes.sizeof(RaAttnParams)
+    p.causal = int(bool(causal))
+    p.num_chunks = int(num_chunks)
+    p.start_chunk = int(start_chunk)
+    p.q_offset = int(q_offset)
+    p.kv_offset = int(kv_offset)
+    p.scale = 0.0 if scale is None else float(scale)
+    return p
+
+
+def _stream(t: torch.Tensor) -> int:
+    if not t.is_cuda:
+        raise RaError(-1, "RA_ERR_NULL: tensors must live in GPU memory")
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: bool = False,
+             num_chunks: int = 1, start_chunk: int = 0, q_offset: int = 0, kv_offset: int = 0,
+             scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
+             lse: Optional[torch.Tensor] = None,
+             out_dtype: Optional[torch.dtype] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Exact attention of q [B,Hq,Sq,D] over k, v [B,Hkv,Skv,D] split into ``num_chunks``
+    chunks visited from ``start_chunk`` in ring order.  Returns (o, lse)."""
+    if out is None:
+        out = torch.empty(q.shape, dtype=out_dtype or q.dtype, device=q.device)
+    if lse is None:
+        lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+    p = _params(causal, num_chunks, start_chunk, q_offset, kv_offset, scale)
+    dq, dk, dv, do, dl = desc(q), desc(k), desc(v), desc(out), desc(lse)
+    _check(lib().ra_attn_fwd(dq, dk, dv, ctypes.byref(p), do, dl, _stream(q)))
+    return out, lse
+
+
+def attn_fwd_validate(q, k, v, out, lse, *, causal=False, num_chunks=1, start_chunk=0,
+                      q_offset=0, kv_offset=0, scale=None) -> int:
+    """Host-side argument check of attn_fwd (no device access); returns the status."""
+    p = _params(causal, num_chunks, start_chunk, q_offset, kv_offset, scale)
+    return int(lib().ra_attn_fwd_validate(desc(q), desc(k), desc(v), ctypes.byref(p),
+                                          desc(out), desc(lse)))
+
+
+def _parts_arrays(o_parts, lse_parts):
+    n = len(o_parts)
+    oa = (RaTensor * max(n, 1))(*[desc(t) for t in o_parts])
+    la = (RaTensor * max(len(lse_parts), 1))(*[desc(t) for t in lse_parts])
+    return n, oa, la
+
+
+def lse_merge(o_parts: Sequence[torch.Tensor], lse_parts: Sequence[torch.Tensor], *,
+              out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+              out_dtype: Optional[torch.dtype] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Merge partial (o_i, lse_i) over disjoint key sets.  Returns (o, lse)."""
+    if len(o_parts) != len(lse_parts):
+        raise RaError(-3, "RA_ERR_SHAPE: o_parts and lse_parts differ in length")
+    ref = o_parts[0]
+    if out is None:
+        out = torch.empty(ref.shape, dtype=out_dtype or ref.dtype, device=ref.device)
+    if lse is None:
+        lse = torch.empty(ref.shape[:3], dtype=torch.float32, device=ref.device)
+    n, oa, la = _parts_arrays(o_parts, lse_parts)
+    _check(lib().ra_lse_merge(n, oa, la, desc(out), desc(lse), _stream(ref)))
+    return out, lse
+
+
+def lse_merge_validate(o_parts, lse_parts, out, lse) -> int:
+    n, oa, la = _parts_arrays(o_parts, lse_parts)
+    return int(lib().ra_lse_merge_validate(n, oa, la, desc(out), desc(lse)))
+
+
+def _permute_out_shape(src: torch.Tensor, P: int, rank: int, dir: int):
+    if dir == 0:
+        P_, Sl, H, D = src.shape
+        shape = (H // P, P * Sl, D)
+        return shape if rank >= 0 else (P,) + shape
+    raise ValueError("dir=1 needs an explicit `out` of shape [P, S/P, H, D]")
+
+
+def ulysses_permute(src: torch.Tensor, P: int, rank: int, dir: int = 0, *,
+                    out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Sequence shards [P,S/P,H,D] -> head shard [H/P,S,D] (dir 0) or back (dir 1)."""
+    if out is None:
+        out = torch.empty(_permute_out_shape(src, P, rank, dir), dtype=src.dtype,
+                          device=src.device)
+    _check(lib().ra_ulysses_permute(desc(src), desc(out), int(P), int(rank), int(dir),
+                                    _stream(src)))
+    return out
+
+
+def ulysses_permute_validate(src, out, P, rank, dir) -> int:
+    return int(lib().ra_ulysses_permute_validate(desc(src), desc(out), int(P), int(rank),
+                                                 int(dir)))
+
+
+def attn_bwd_workspace_size(q: torch.Tensor, k: torch.Tensor, *, causal=False, num_chunks=1,
+                            start_chunk=0, q_offset=0, kv_offset=0, scale=None) -> int:
+    p = _params(causal, num_chunks, start_chunk, q_offset, kv_offset, scale)
+    return int(lib().ra_attn_bwd_workspace_size(desc(q), desc(k), ctypes.byref(p)))
+
+
+def attn_bwd(q, k, v, o, dout, lse, *, causal=False, num_chunks=1, start_chunk=0, q_offset=0,
+             kv_offset=0, scale=None, dq=None, dk=None, dv=None,
+             workspace: Optional[torch.Tensor] = None):
+    """Gradients (dq, dk, dv) of sum(dout * o), recomputing P from the saved lse."""
+    p = _params(causal, num_chunks, start_chunk, q_offset, kv_offset, scale)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    need = int(lib().ra_attn_bwd_workspace_size(desc(q), desc(k), ctypes.byref(p)))
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    _check(lib().ra_attn_bwd(desc(q), desc(k), desc(v), desc(o), desc(dout), desc(lse),
+                             ctypes.byref(p), desc(dq), desc(dk), desc(dv),
+                             workspace.data_ptr(), workspace.numel(), _stream(q)))
+    return dq, dk, dv
+
+
+def attn_bwd_validate(q, k, v, o, dout, lse, dq, dk, dv, *, causal=False, num_chunks=1,
+                      start_chunk=0, q_offset=0, kv_offset=0, scale=None) -> int:
+    p = _params(causal, num_chunks, start_chunk, q_offset, kv_offset, scale)
+    return int(lib().ra_attn_bwd_validate(desc(q), desc(k), desc(v), desc(o), desc(dout),
+                                          desc(lse), ctypes.byref(p), desc(dq), desc(dk),
+                                          desc(dv)))
+
+
+def ring_visible_chunks(Sq: int, Skv: int, *, num_chunks: int, start_chunk: int = 0,
+                        causal: bool = False, q_offset: int = 0, kv_offset: int = 0):
+    """Chunks in ring order (start + t) mod P that hold at least one key visible to the
+    last query row; the rest are skipped (their partial would be (0, -inf))."""
+    L = Skv // num_chunks
+    order = [(start_chunk + t) % num_chunks for t in range(num_chunks)]
+    if not causal:
+        return order
+    last_q = q_offset + Sq - 1
+    return [c for c in order if kv_offset + c * L <= last_q]
+
+
+def ring_attn_chunked(q, k, v, *, num_chunks: int, start_chunk: int = 0, causal: bool = False,
+                      q_offset: int = 0, kv_offset: int = 0, scale: Optional[float] = None,
+                      out_dtype: Optional[torch.dtype] = None):
+    """One ring rank's share computed chunk by chunk, as a ring would deliver the chunks:
+    one attn_fwd per visible chunk into fp32 partials, then one lse_merge."""
+    Skv = k.shape[2]
+    L = Skv // num_chunks
+    chunks = ring_visible_chunks(q.shape[2], Skv, num_chunks=num_chunks,
+                                 start_chunk=start_chunk, causal=causal, q_offset=q_offset,
+                                 kv_offset=kv_offset)
+    if not chunks:
+        chunks = [start_chunk]  # every row empty: one call yields o = 0, lse = -inf
+    o_parts, lse_parts = [], []
+    for c in chunks:
+        o_c, l_c = attn_fwd(q, k[:, :, c * L:(c + 1) * L], v[:, :, c * L:(c + 1) * L],
+                            causal=causal, q_offset=q_offset, kv_offset=kv_offset + c * L,
+                            scale=scale, out_dtype=torch.float32)
+        o_parts.append(o_c)
+        lse_parts.append(l_c)
+    return lse_merge(o_parts, lse_parts, out_dtype=out_dtype or q.dtype)

@@ -1,0 +1,361 @@
+// The exported C ABI of libra (declared in include/ra.h): host-side argument
+// validation, then dispatch to the kernel launchers.  Validation touches no device
+// state, so the *_validate entry points run on machines without a GPU.
+#include <math.h>
+#include <string.h>
+
+#include <algorithm>
+
+#include "internal.h"
+
+namespace ra {
+namespace {
+
+int64_t esize(int32_t dtype) { return dtype == RA_F32 ? 4 : (dtype == RA_BF16 ? 2 : 0); }
+
+bool known_dtype(int32_t dtype) { return dtype == RA_F32 || dtype == RA_BF16; }
+
+int64_t numel(const ra_tensor *t) {
+  int64_t n = 1;
+  for (int i = 0; i < t->ndim; ++i) n *= t->shape[i];
+  return n;
+}
+
+// Rank, extents, innermost stride, non-negative strides and (for outputs) a layout in
+// which no two elements share an address.  `vec_align`: the data pointer and outer
+// strides must be multiples of this many bytes.
+int check_tensor(const ra_tensor *t, int ndim, int64_t vec_align, bool is_output) {
+  if (!t) return RA_ERR_NULL;
+  if (!known_dtype(t->dtype)) return RA_ERR_DTYPE;
+  if (t->ndim != ndim) return RA_ERR_SHAPE;
+  for (int i = 0; i < ndim; ++i)
+    if (t->shape[i] < 0 || t->shape[i] > (int64_t)INT32_MAX) return RA_ERR_SHAPE;
+  const int64_t n = numel(t);
+  if (n == 0) return RA_OK;
+  if (!t->data) return RA_ERR_NULL;
+  for (int i = 0; i < ndim; ++i)
+    if (t->stride[i] < 0) return RA_ERR_STRIDE;
+  if (t->stride[ndim - 1] != 1 && t->shape[ndim - 1] > 1) return RA_ERR_STRIDE;
+  const int64_t es = esize(t->dtype);
+  if (((uintptr_t)t->data) % (uintptr_t)vec_align) return RA_ERR_ALIGN;
+  for (int i = 0; i < ndim - 1; ++i)
+    if (t->shape[i] > 1 && (t->stride[i] * es) % vec_align) return RA_ERR_ALIGN;
+  if (is_output) {
+    // sufficient non-overlap test: visiting axes by increasing stride, each stride
+    // exceeds the span of the axes already visited.
+    int order[4] = {0, 1, 2, 3};
+    std::sort(order, order + ndim, [&](int x, int y) { return t->stride[x] < t->stride[y]; });
+    int64_t span = 0;
+    for (int j = 0; j < ndim; ++j) {
+      const int ax = order[j];
+      if (t->shape[ax] <= 1) continue;
+      if (t->stride[ax] <= span) return RA_ERR_STRIDE;
+      span += (t->shape[ax] - 1) * t->stride[ax];
+    }
+  }
+  return RA_OK;
+}
+
+bool same_shape(const ra_tensor *a, const ra_tensor *b) {
+  if (a->ndim != b->ndim) return false;
+  for (int i = 0; i < a->ndim; ++i)
+    if (a->shape[i] != b->shape[i]) return false;
+  return true;
+}
+
+bool same_strides(const ra_tensor *a, const ra_tensor *b) {
+  for (int i = 0; i < a->ndim; ++i)
+    if (a->shape[i] > 1 && a->stride[i] != b->stride[i]) return false;
+  return true;
+}
+
+#define RA_TRY(expr)             \
+  do {                           \
+    int rc_ = (expr);            \
+    if (rc_ != RA_OK) return rc_; \
+  } while (0)
+
+int check_params(const ra_attn_params *p, int64_t Skv) {
+  if (!p) return RA_ERR_NULL;
+  if (p->struct_size < sizeof(ra_attn_params)) return RA_ERR_RANGE;
+  if (p->causal != 0 && p->causal != 1) return RA_ERR_RANGE;
+  if (p->num_chunks < 1) return RA_ERR_RANGE;
+  if (p->start_chunk < 0 || p->start_chunk >= p->num_chunks) return RA_ERR_RANGE;
+  if (p->q_offset < 0 || p->kv_offset < 0) return RA_ERR_RANGE;
+  if (p->q_offset > ((int64_t)1 << 40) || p->kv_offset > ((int64_t)1 << 40)) return RA_ERR_RANGE;
+  if (!isfinite(p->scale)) return RA_ERR_RANGE;
+  if (Skv % p->num_chunks) return RA_ERR_SHAPE;
+  return RA_OK;
+}
+
+float effective_scale(const ra_attn_params *p, int64_t D) {
+  return p->scale > 0.f ? p->scale : (float)(1.0 / sqrt((double)D));
+}
+
+// q [B,Hq,Sq,D], k/v [B,Hkv,Skv,D]; returns the shared checks of fwd and bwd.
+int check_qkv(const ra_tensor *q, const ra_tensor *k, const ra_tensor *v) {
+  if (!q || !k || !v) return RA_ERR_NULL;
+  RA_TRY(check_tensor(q, 4, 16, false));
+  RA_TRY(check_tensor(k, 4, 16, false));
+  RA_TRY(check_tensor(v, 4, 16, false));
+  if (k->dtype != q->dtype || v->dtype != q->dtype) return RA_ERR_DTYPE;
+  if (!same_shape(k, v)) return RA_ERR_SHAPE;
+  if (k->shape[0] != q->shape[0] || k->shape[3] != q->shape[3]) return RA_ERR_SHAPE;
+  const int64_t Hq = q->shape[1], Hkv = k->shape[1];
+  if (Hq > 0 && (Hkv == 0 || Hq % Hkv)) return RA_ERR_SHAPE;
+  return RA_OK;
+}
+
+int check_lse(const ra_tensor *lse, const ra_tensor *q, bool is_output) {
+  if (!lse) return RA_ERR_NULL;
+  RA_TRY(check_tensor(lse, 3, 4, is_output));
+  if (lse->dtype != RA_F32) return RA_ERR_DTYPE;
+  for (int i = 0; i < 3; ++i)
+    if (lse->shape[i] != q->shape[i]) return RA_ERR_SHAPE;
+  return RA_OK;
+}
+
+int check_grid(const ra_tensor *q) {
+  const int64_t tiles = (q->shape[2] + 127) / 128;
+  if (tiles * q->shape[1] * q->shape[0] > (int64_t)INT32_MAX) return RA_ERR_SHAPE;
+  return RA_OK;
+}
+
+int fwd_validate(const ra_tensor *q, const ra_tensor *k, const ra_tensor *v,
+                 const ra_attn_params *p, const ra_tensor *o, const ra_tensor *lse) {
+  if (!o || !lse || !p) return RA_ERR_NULL;
+  RA_TRY(check_qkv(q, k, v));
+  RA_TRY(check_params(p, k->shape[2]));
+  RA_TRY(check_tensor(o, 4, 16, true));
+  if (o->dtype != q->dtype && o->dtype != RA_F32) return RA_ERR_DTYPE;
+  if (!same_shape(o, q)) return RA_ERR_SHAPE;
+  RA_TRY(check_lse(lse, q, true));
+  RA_TRY(check_grid(q));
+  const int64_t D = q->shape[3];
+  if (D != 64 && D != 128) return RA_ERR_UNSUPPORTED;
+  return RA_OK;
+}
+
+int merge_validate(int32_t n, const ra_tensor *o_parts, const ra_tensor *lse_parts,
+                   const ra_tensor *o, const ra_tensor *lse) {
+  if (!o_parts || !lse_parts || !o || !lse) return RA_ERR_NULL;
+  if (n < 1 || n > RA_MAX_MERGE_PARTS) return RA_ERR_RANGE;
+  RA_TRY(check_tensor(o, 4, 16, true));
+  RA_TRY(check_lse(lse, o, true));
+  for (int i = 0; i < n; ++i) {
+    RA_TRY(check_tensor(&o_parts[i], 4, 16, false));
+    RA_TRY(check_tensor(&lse_parts[i], 3, 4, false));
+    if (o_parts[i].dtype != o_parts[0].dtype) return RA_ERR_DTYPE;
+    if (lse_parts[i].dtype != RA_F32) return RA_ERR_DTYPE;
+    if (!same_shape(&o_parts[i], o)) return RA_ERR_SHAPE;
+    for (int d = 0; d < 3; ++d)
+      if (lse_parts[i].shape[d] != o->shape[d]) return RA_ERR_SHAPE;
+    if (!same_strides(&o_parts[i], &o_parts[0])) return RA_ERR_STRIDE;
+    if (!same_strides(&lse_parts[i], &lse_parts[0])) return RA_ERR_STRIDE;
+  }
+  const int64_t D = o->shape[3];
+  if (D % 8 || D > 256) return RA_ERR_UNSUPPORTED;
+  return RA_OK;
+}
+
+int permute_validate(const ra_tensor *src, const ra_tensor *dst, int32_t P, int32_t rank,
+                     int32_t dir) {
+  if (!src || !dst) return RA_ERR_NULL;
+  if (dir != 0 && dir != 1) return RA_ERR_RANGE;
+  if (P < 1) return RA_ERR_RANGE;
+  if (rank < -1 || rank >= P) return RA_ERR_RANGE;
+  const ra_tensor *seq = dir == 0 ? src : dst;
+  const ra_tensor *head = dir == 0 ? dst : src;
+  const int head_nd = rank == -1 ? 4 : 3;
+  RA_TRY(check_tensor(seq, 4, 16, dir == 1));
+  RA_TRY(check_tensor(head, head_nd, 16, dir == 0));
+  if (src->dtype != dst->dtype) return RA_ERR_DTYPE;
+  if (seq->shape[0] != P) return RA_ERR_SHAPE;
+  const int64_t Sl = seq->shape[1], H = seq->shape[2], D = seq->shape[3];
+  if (H % P) return RA_ERR_SHAPE;
+  const int64_t hs[3] = {H / P, P * Sl, D};
+  const int off = head_nd - 3;
+  if (rank == -1 && head->shape[0] != P) return RA_ERR_SHAPE;
+  for (int i = 0; i < 3; ++i)
+    if (head->shape[off + i] != hs[i]) return RA_ERR_SHAPE;
+  if ((D * esize(src->dtype)) % 16) return RA_ERR_ALIGN;
+  if (P * Sl > (int64_t)INT32_MAX) return RA_ERR_SHAPE;
+  return RA_OK;
+}
+
+int bwd_validate(const ra_tensor *q, const ra_tensor *k, const ra_tensor *v, const ra_tensor *o,
+                 const ra_tensor *dout, const ra_tensor *lse, const ra_attn_params *p,
+                 const ra_tensor *dq, const ra_tensor *dk, const ra_tensor *dv) {
+  if (!o || !dout || !lse || !p || !dq || !dk || !dv) return RA_ERR_NULL;
+  RA_TRY(check_qkv(q, k, v));
+  RA_TRY(check_params(p, k->shape[2]));
+  RA_TRY(check_tensor(o, 4, 16, false));
+  RA_TRY(check_tensor(dout, 4, 16, false));
+  RA_TRY(check_tensor(dq, 4, 16, true));
+  RA_TRY(check_tensor(dk, 4, 16, true));
+  RA_TRY(check_tensor(dv, 4, 16, true));
+  for (const ra_tensor *t : {o, dout, dq, dk, dv})
+    if (t->dtype != q->dtype) return RA_ERR_DTYPE;
+  if (!same_shape(o, q) || !same_shape(dout, q) || !same_shape(dq, q)) return RA_ERR_SHAPE;
+  if (!same_shape(dk, k) || !same_shape(dv, k)) return RA_ERR_SHAPE;
+  RA_TRY(check_lse(lse, q, false));
+  RA_TRY(check_grid(q));
+  RA_TRY(check_grid(k));
+  const int64_t D = q->shape[3];
+  if (q->dtype != RA_BF16) return RA_ERR_UNSUPPORTED;
+  if (D != 64 && D != 128) return RA_ERR_UNSUPPORTED;
+  return RA_OK;
+}
+
+}  // namespace
+}  // namespace ra
+
+using namespace ra;
+
+extern "C" {
+
+int ra_version(void) { return RA_VERSION; }
+
+const char *ra_status_string(int status) {
+  switch (status) {
+    case RA_OK: return "RA_OK: success";
+    case RA_ERR_NULL: return "RA_ERR_NULL: a required pointer is NULL";
+    case RA_ERR_DTYPE: return "RA_ERR_DTYPE: dtype not allowed or mismatched";
+    case RA_ERR_SHAPE: return "RA_ERR_SHAPE: ranks or extents are inconsistent";
+    case RA_ERR_STRIDE: return "RA_ERR_STRIDE: innermost stride must be 1, strides non-negative, outputs non-overlapping";
+    case RA_ERR_ALIGN: return "RA_ERR_ALIGN: pointer or row stride not a multiple of 16 bytes";
+    case RA_ERR_RANGE: return "RA_ERR_RANGE: a scalar parameter is out of range";
+    case RA_ERR_UNSUPPORTED: return "RA_ERR_UNSUPPORTED: valid request not implemented (head dim or dtype)";
+    case RA_ERR_HIP: return "RA_ERR_HIP: kernel launch failed";
+    case RA_ERR_WORKSPACE: return "RA_ERR_WORKSPACE: workspace missing, misaligned or too small";
+    default: return "unknown ra_status";
+  }
+}
+
+int ra_attn_fwd_validate(const ra_tensor *q, const ra_tensor *k, const ra_tensor *v,
+                         const ra_attn_params *p, const ra_tensor *o, const ra_tensor *lse) {
+  return fwd_validate(q, k, v, p, o, lse);
+}
+
+int ra_attn_fwd(const ra_tensor *q, const ra_tensor *k, const ra_tensor *v,
+                const ra_attn_params *p, ra_tensor *o, ra_tensor *lse, ra_stream stream) {
+  RA_TRY(fwd_validate(q, k, v, p, o, lse));
+  if (numel(q) == 0) return RA_OK;
+  FwdArgs a{};
+  a.q = q->data; a.k = k->data; a.v = v->data; a.o = o->data; a.lse = (float *)lse->data;
+  a.q_sb = q->stride[0]; a.q_sh = q->stride[1]; a.q_ss = q->stride[2];
+  a.k_sb = k->stride[0]; a.k_sh = k->stride[1]; a.k_ss = k->stride[2];
+  a.v_sb = v->stride[0]; a.v_sh = v->stride[1]; a.v_ss = v->stride[2];
+  a.o_sb = o->stride[0]; a.o_sh = o->stride[1]; a.o_ss = o->stride[2];
+  a.l_sb = lse->stride[0]; a.l_sh = lse->stride[1];
+  a.B = (int32_t)q->shape[0]; a.Hq = (int32_t)q->shape[1]; a.Sq = (int32_t)q->shape[2];
+  a.Hkv = (int32_t)k->shape[1]; a.Skv = (int32_t)k->shape[2];
+  a.group = a.Hq / a.Hkv;
+  a.num_chunks = p->num_chunks; a.start_chunk = p->start_chunk;
+  a.chunk_len = a.Skv / a.num_chunks;
+  a.q_offset = p->q_offset; a.kv_offset = p->kv_offset;
+  a.scale_log2 = effective_scale(p, q->shape[3]) * kLog2eHost;
+  a.o_is_f32 = o->dtype == RA_F32;
+  return launch_attn_fwd(a, q->dtype, (int)q->shape[3], p->causal, (hipStream_t)stream);
+}
+
+int ra_lse_merge_validate(int32_t n, const ra_tensor *o_parts, const ra_tensor *lse_parts,
+                          const ra_tensor *o, const ra_tensor *lse) {
+  return merge_validate(n, o_parts, lse_parts, o, lse);
+}
+
+int ra_lse_merge(int32_t n, const ra_tensor *o_parts, const ra_tensor *lse_parts, ra_tensor *o,
+                 ra_tensor *lse, ra_stream stream) {
+  RA_TRY(merge_validate(n, o_parts, lse_parts, o, lse));
+  if (numel(o) == 0) return RA_OK;
+  MergeArgs a{};
+  for (int i = 0; i < n; ++i) {
+    a.o_parts[i] = o_parts[i].data;
+    a.lse_parts[i] = (const float *)lse_parts[i].data;
+  }
+  a.o = o->data; a.lse = (float *)lse->data;
+  a.p_sb = o_parts[0].stride[0]; a.p_sh = o_parts[0].stride[1]; a.p_ss = o_parts[0].stride[2];
+  a.pl_sb = lse_parts[0].stride[0]; a.pl_sh = lse_parts[0].stride[1];
+  a.o_sb = o->stride[0]; a.o_sh = o->stride[1]; a.o_ss = o->stride[2];
+  a.l_sb = lse->stride[0]; a.l_sh = lse->stride[1];
+  a.n = n; a.B = (int32_t)o->shape[0]; a.H = (int32_t)o->shape[1];
+  a.S = (int32_t)o->shape[2]; a.D = (int32_t)o->shape[3];
+  a.parts_f32 = o_parts[0].dtype == RA_F32;
+  a.out_f32 = o->dtype == RA_F32;
+  return launch_lse_merge(a, (hipStream_t)stream);
+}
+
+int ra_ulysses_permute_validate(const ra_tensor *src, const ra_tensor *dst, int32_t P,
+                                int32_t rank, int32_t dir) {
+  return permute_validate(src, dst, P, rank, dir);
+}
+
+int ra_ulysses_permute(const ra_tensor *src, ra_tensor *dst, int32_t P, int32_t rank, int32_t dir,
+                       ra_stream stream) {
+  RA_TRY(permute_validate(src, dst, P, rank, dir));
+  if (numel(src) == 0) return RA_OK;
+  const ra_tensor *seq = dir == 0 ? src : dst;
+  const ra_tensor *head = dir == 0 ? dst : src;
+  PermuteArgs a{};
+  a.src = src->data; a.dst = dst->data;
+  a.seq_s0 = seq->stride[0]; a.seq_s1 = seq->stride[1]; a.seq_s2 = seq->stride[2];
+  const int off = head->ndim - 3;
+  a.head_s0 = off ? head->stride[0] : 0;
+  a.head_s1 = head->stride[off + 0]; a.head_s2 = head->stride[off + 1];
+  a.P = P; a.Sl = (int32_t)seq->shape[1]; a.H = (int32_t)seq->shape[2]; a.Hl = a.H / P;
+  a.elem_bytes = (int32_t)esize(src->dtype);
+  a.row_bytes = (int32_t)(seq->shape[3] * a.elem_bytes);
+  a.rank0 = rank == -1 ? 0 : rank;
+  a.nranks = rank == -1 ? P : 1;
+  a.dir = dir;
+  return launch_ulysses_permute(a, (hipStream_t)stream);
+}
+
+int ra_attn_bwd_validate(const ra_tensor *q, const ra_tensor *k, const ra_tensor *v,
+                         const ra_tensor *o, const ra_tensor *dout, const ra_tensor *lse,
+                         const ra_attn_params *p, const ra_tensor *dq, const ra_tensor *dk,
+                         const ra_tensor *dv) {
+  return bwd_validate(q, k, v, o, dout, lse, p, dq, dk, dv);
+}
+
+size_t ra_attn_bwd_workspace_size(const ra_tensor *q, const ra_tensor *k, const ra_attn_params *p) {
+  if (!q || !k || !p) return 0;
+  if (check_qkv(q, k, k) != RA_OK || check_params(p, k->shape[2]) != RA_OK) return 0;
+  return bwd_workspace_bytes(q->shape[0], q->shape[1], q->shape[2]);
+}
+
+int ra_attn_bwd(const ra_tensor *q, const ra_tensor *k, const ra_tensor *v, const ra_tensor *o,
+                const ra_tensor *dout, const ra_tensor *lse, const ra_attn_params *p,
+                ra_tensor *dq, ra_tensor *dk, ra_tensor *dv, void *workspace,
+                size_t workspace_bytes, ra_stream stream) {
+  RA_TRY(bwd_validate(q, k, v, o, dout, lse, p, dq, dk, dv));
+  const size_t need = bwd_workspace_bytes(q->shape[0], q->shape[1], q->shape[2]);
+  if (need > 0 && (!workspace || workspace_bytes < need || ((uintptr_t)workspace) % 256))
+    return RA_ERR_WORKSPACE;
+  if (numel(q) == 0 && numel(k) == 0) return RA_OK;
+  BwdArgs a{};
+  a.q = q->data; a.k = k->data; a.v = v->data; a.o = o->data; a.dout = dout->data;
+  a.lse = (const float *)lse->data;
+  a.dq = dq->data; a.dk = dk->data; a.dv = dv->data;
+  a.delta = (float *)workspace;
+  a.q_sb = q->stride[0]; a.q_sh = q->stride[1]; a.q_ss = q->stride[2];
+  a.k_sb = k->stride[0]; a.k_sh = k->stride[1]; a.k_ss = k->stride[2];
+  a.v_sb = v->stride[0]; a.v_sh = v->stride[1]; a.v_ss = v->stride[2];
+  a.o_sb = o->stride[0]; a.o_sh = o->stride[1]; a.o_ss = o->stride[2];
+  a.do_sb = dout->stride[0]; a.do_sh = dout->stride[1]; a.do_ss = dout->stride[2];
+  a.l_sb = lse->stride[0]; a.l_sh = lse->stride[1];
+  a.dq_sb = dq->stride[0]; a.dq_sh = dq->stride[1]; a.dq_ss = dq->stride[2];
+  a.dk_sb = dk->stride[0]; a.dk_sh = dk->stride[1]; a.dk_ss = dk->stride[2];
+  a.dv_sb = dv->stride[0]; a.dv_sh = dv->stride[1]; a.dv_ss = dv->stride[2];
+  a.B = (int32_t)q->shape[0]; a.Hq = (int32_t)q->shape[1]; a.Sq = (int32_t)q->shape[2];
+  a.Hkv = (int32_t)k->shape[1]; a.Skv = (int32_t)k->shape[2];
+  a.group = a.Hkv ? a.Hq / a.Hkv : 1;
+  a.num_chunks = p->num_chunks; a.start_chunk = p->start_chunk;
+  a.chunk_len = a.Skv / a.num_chunks;
+  a.q_offset = p->q_offset; a.kv_offset = p->kv_offset;
+  a.scale = effective_scale(p, q->shape[3]);
+  a.scale_log2 = a.scale * kLog2eHost;
+  return launch_attn_bwd(a, (int)q->shape[3], p->causal, (hipStream_t)stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,70 @@
+// Device-side helpers shared by the gfx950 kernels of libra.
+//
+// Register layouts of the two matrix-core instructions used here (CDNA3/CDNA4
+// MFMA, 64-lane wavefront, lane l, half h = l / 32):
+//
+//   v_mfma_f32_32x32x16_bf16   A: 32(M) x 16(K), lane holds 8 bf16 of row m = l%32
+//                              B: 16(K) x 32(N), lane holds 8 bf16 of column n = l%32
+//                              (lanes of half h hold the K-slice h; A and B must agree
+//                              on which k each register element is, nothing else)
+//   v_mfma_f32_32x32x2_f32     A, B: one float per lane, k = h
+//   C/D (both): 16 floats per lane; element i is row (i/4)*8 + 4h + i%4, column l%32.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ra {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+__device__ __forceinline__ f32x16 mfma_bf16(const bf16x8 &a, const bf16x8 &b, const f32x16 &c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x16 mfma_f32(float a, float b, const f32x16 &c) {
+  return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+}
+
+// Combine a value across the two 32-lane halves of the wavefront.  v_permlane32_swap
+// with the same register as both operands returns {value of lane l%32, value of lane
+// 32 + l%32} in every lane, so max / sum of the pair is the same in both halves (and the
+// sum is formed in the same order in both halves, so the halves agree bitwise).
+__device__ __forceinline__ float halves_max(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+__device__ __forceinline__ float halves_sum(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Two floats -> two bf16 (round to nearest even) packed in one dword, first in the low half.
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  __bf16 x = (__bf16)a;
+  __bf16 y = (__bf16)b;
+  return (uint32_t)__builtin_bit_cast(uint16_t, x) | ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
+}
+
+__device__ __forceinline__ float bf16_bits_to_float(uint32_t bits16) {
+  return __uint_as_float(bits16 << 16);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(const u32x4 &u) { return __builtin_bit_cast(bf16x8, u); }
+
+// Byte select across two dwords (v_perm_b32): selector bytes 0-3 pick from `lo`, 4-7 from `hi`.
+__device__ __forceinline__ uint32_t perm_b32(uint32_t hi, uint32_t lo, uint32_t sel) {
+  return __builtin_amdgcn_perm(hi, lo, sel);
+}
+
+}  // namespace ra

@@ -1,0 +1,90 @@
+// Internal (non-exported) interfaces between the C ABI layer and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/ra.h"
+
+namespace ra {
+
+constexpr float kLog2eHost = 1.4426950408889634f;
+
+// Forward attention problem after validation: raw pointers and element strides.
+struct FwdArgs {
+  const void *q;
+  const void *k;
+  const void *v;
+  void *o;
+  float *lse;
+  int64_t q_sb, q_sh, q_ss;
+  int64_t k_sb, k_sh, k_ss;
+  int64_t v_sb, v_sh, v_ss;
+  int64_t o_sb, o_sh, o_ss;
+  int64_t l_sb, l_sh;
+  int32_t B, Hq, Hkv, Sq, Skv;
+  int32_t group;        // Hq / Hkv
+  int32_t num_chunks;   // P
+  int32_t start_chunk;
+  int32_t chunk_len;    // Skv / P
+  int32_t num_q_tiles;
+  int64_t q_offset, kv_offset;
+  float scale_log2;     // scale * log2(e)
+  int32_t o_is_f32;     // output dtype: 1 = fp32, 0 = same as inputs (bf16 path)
+};
+
+int launch_attn_fwd(const FwdArgs &a, int dtype, int D, int causal, hipStream_t stream);
+
+struct MergeArgs {
+  const void *o_parts[RA_MAX_MERGE_PARTS];
+  const float *lse_parts[RA_MAX_MERGE_PARTS];
+  void *o;
+  float *lse;
+  int64_t p_sb, p_sh, p_ss;   // strides of every o part
+  int64_t pl_sb, pl_sh;       // strides of every lse part (seq stride 1)
+  int64_t o_sb, o_sh, o_ss;
+  int64_t l_sb, l_sh;
+  int32_t n, B, H, S, D;
+  int32_t parts_f32, out_f32;
+};
+
+int launch_lse_merge(const MergeArgs &a, hipStream_t stream);
+
+struct PermuteArgs {
+  const void *src;
+  void *dst;
+  // Sequence-sharded side [P, S/P, H, D] and head-sharded side [R, H/P, S, D] (R = 1 or P).
+  int64_t seq_s0, seq_s1, seq_s2;       // strides of the shard, token, head axes
+  int64_t head_s0, head_s1, head_s2;    // strides of the rank, head, token axes
+  int32_t P, Sl, H, Hl, row_bytes, elem_bytes;
+  int32_t rank0, nranks;                // ranks rank0 .. rank0 + nranks - 1
+  int32_t dir;                          // 0: seq -> head, 1: head -> seq
+};
+
+int launch_ulysses_permute(const PermuteArgs &a, hipStream_t stream);
+
+struct BwdArgs {
+  const void *q, *k, *v, *o, *dout;
+  const float *lse;
+  void *dq, *dk, *dv;
+  float *delta;  // workspace: D_i = rowsum(dout * o), [B, Hq, Sq] contiguous
+  int64_t q_sb, q_sh, q_ss;
+  int64_t k_sb, k_sh, k_ss;
+  int64_t v_sb, v_sh, v_ss;
+  int64_t o_sb, o_sh, o_ss;
+  int64_t do_sb, do_sh, do_ss;
+  int64_t l_sb, l_sh;
+  int64_t dq_sb, dq_sh, dq_ss;
+  int64_t dk_sb, dk_sh, dk_ss;
+  int64_t dv_sb, dv_sh, dv_ss;
+  int32_t B, Hq, Hkv, Sq, Skv, group;
+  int32_t num_chunks, start_chunk, chunk_len;
+  int64_t q_offset, kv_offset;
+  float scale, scale_log2;
+};
+
+size_t bwd_workspace_bytes(int64_t B, int64_t Hq, int64_t Sq);
+int launch_attn_bwd(const BwdArgs &a, int D, int causal, hipStream_t stream);
+
+}  // namespace ra

@@ -1,0 +1,150 @@
+"""The C-ABI library loads, exports what include/ra.h declares, and rejects bad
+arguments on the host (no GPU needed: only the *_validate entry points and calls
+that fail validation are made, neither of which touches the device)."""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def ra():
+    import long_context_exact_tiled_amd as m
+    if not os.path.exists(m.LIB_PATH):
+        from long_context_exact_tiled_amd.build import build
+        build()
+    m.lib()
+    return m
+
+
+def _declared_symbols():
+    text = open(os.path.join(ROOT, "include", "ra.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ra_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(ra):
+    names = _declared_symbols()
+    assert {"ra_attn_fwd", "ra_lse_merge", "ra_ulysses_permute", "ra_attn_bwd"} <= set(names)
+    L = ctypes.CDLL(ra.LIB_PATH)
+    for name in names:
+        assert hasattr(L, name), name
+
+
+def test_version_and_status_strings(ra):
+    assert ra.version() == 100
+    for code, name in ra.STATUS.items():
+        assert ra.status_string(code).startswith(name)
+    assert ra.status_string(12345) == "unknown ra_status"
+
+
+def _t(shape, dtype=torch.bfloat16):
+    return torch.zeros(shape, dtype=dtype)
+
+
+def _fwd(ra, q, k, v, o=None, lse=None, **kw):
+    o = torch.zeros(q.shape, dtype=q.dtype) if o is None else o
+    lse = torch.zeros(q.shape[:3], dtype=torch.float32) if lse is None else lse
+    return ra.STATUS[ra.attn_fwd_validate(q, k, v, o, lse, **kw)]
+
+
+def test_fwd_validation(ra):
+    q, k, v = _t((1, 4, 64, 128)), _t((1, 2, 64, 128)), _t((1, 2, 64, 128))
+    assert _fwd(ra, q, k, v) == "RA_OK"
+    assert _fwd(ra, q, k, v, causal=True, num_chunks=4, start_chunk=3, q_offset=7) == "RA_OK"
+    assert _fwd(ra, q, k, v.float()) == "RA_ERR_DTYPE"
+    assert _fwd(ra, q, k, v, lse=torch.zeros((1, 4, 64), dtype=torch.bfloat16)) == "RA_ERR_DTYPE"
+    assert _fwd(ra, q, k, v, o=torch.zeros(q.shape)) == "RA_OK"  # fp32 partial output
+    assert _fwd(ra, q, _t((1, 3, 64, 128)), _t((1, 3, 64, 128))) == "RA_ERR_SHAPE"  # Hq % Hkv
+    assert _fwd(ra, q, k, _t((1, 2, 63, 128))) == "RA_ERR_SHAPE"
+    assert _fwd(ra, q, k, v, num_chunks=3) == "RA_ERR_SHAPE"  # 64 % 3
+    assert _fwd(ra, q, k, v, num_chunks=0) == "RA_ERR_RANGE"
+    assert _fwd(ra, q, k, v, num_chunks=4, start_chunk=4) == "RA_ERR_RANGE"
+    assert _fwd(ra, q, k, v, start_chunk=-1) == "RA_ERR_RANGE"
+    assert _fwd(ra, q, k, v, q_offset=-1) == "RA_ERR_RANGE"
+    assert _fwd(ra, q, k, v, scale=float("nan")) == "RA_ERR_RANGE"
+    assert _fwd(ra, _t((1, 4, 64, 96)), _t((1, 2, 64, 96)), _t((1, 2, 64, 96))) \
+        == "RA_ERR_UNSUPPORTED"
+    # innermost stride != 1
+    qt = _t((1, 4, 128, 64)).transpose(2, 3)
+    assert _fwd(ra, qt, _t((1, 2, 64, 128)), _t((1, 2, 64, 128))) == "RA_ERR_STRIDE"
+    # overlapping output rows
+    o_bad = _t((1, 4, 1, 128)).expand(1, 4, 64, 128)
+    assert _fwd(ra, q, k, v, o=o_bad) == "RA_ERR_STRIDE"
+    # misaligned pointer (2-byte offset) and misaligned row stride
+    base = _t((1 * 4 * 64 * 128 + 8,))
+    q_mis = base[1:1 + 4 * 64 * 128].view(1, 4, 64, 128)
+    assert _fwd(ra, q_mis, k, v) == "RA_ERR_ALIGN"
+    wide = _t((1, 4, 64, 132))[..., :128]
+    assert _fwd(ra, wide, k, v) == "RA_ERR_ALIGN"
+    # a BSHD view (heads strided inside a token row) is a valid layout
+    qb = _t((1, 64, 4, 128)).transpose(1, 2)
+    assert _fwd(ra, qb, k, v) == "RA_OK"
+    # empty problems are valid
+    assert _fwd(ra, _t((1, 4, 0, 128)), k, v) == "RA_OK"
+    assert _fwd(ra, q, _t((1, 2, 0, 128)), _t((1, 2, 0, 128))) == "RA_OK"
+
+
+def test_fwd_rejects_before_launch(ra):
+    """A failing call returns its code without touching the device (CPU tensors here)."""
+    q, k = _t((1, 4, 64, 128)), _t((1, 3, 64, 128))
+    with pytest.raises(ra.RaError) as e:
+        ra.lib()  # loaded
+        o = torch.zeros(q.shape, dtype=q.dtype)
+        lse = torch.zeros(q.shape[:3])
+        p = ra._params(False, 1, 0, 0, 0, None)
+        ra._check(ra.lib().ra_attn_fwd(ra.desc(q), ra.desc(k), ra.desc(k), ctypes.byref(p),
+                                       ra.desc(o), ra.desc(lse), None))
+    assert e.value.name == "RA_ERR_SHAPE"
+    assert ra.lib().ra_attn_fwd(None, None, None, None, None, None, None) == -1
+
+
+def test_merge_validation(ra):
+    parts = [torch.zeros(1, 2, 10, 128) for _ in range(3)]
+    lses = [torch.zeros(1, 2, 10) for _ in range(3)]
+    out, lse = torch.zeros(1, 2, 10, 128, dtype=torch.bfloat16), torch.zeros(1, 2, 10)
+    v = lambda p, l, o=out, ls=lse: ra.STATUS[ra.lse_merge_validate(p, l, o, ls)]
+    assert v(parts, lses) == "RA_OK"
+    assert v([], []) == "RA_ERR_RANGE"
+    assert v(parts * 22, lses * 22) == "RA_ERR_RANGE"  # 66 > 64 parts
+    assert v(parts[:2] + [parts[2].bfloat16()], lses) == "RA_ERR_DTYPE"
+    assert v(parts, lses[:2] + [lses[2].bfloat16()]) == "RA_ERR_DTYPE"
+    assert v(parts[:2] + [torch.zeros(1, 2, 11, 128)], lses) == "RA_ERR_SHAPE"
+    strided = torch.zeros(1, 2, 10, 256)[..., :128]
+    assert v(parts[:2] + [strided], lses) == "RA_ERR_STRIDE"
+    assert v([torch.zeros(1, 2, 10, 12)] * 3, lses, torch.zeros(1, 2, 10, 12)) \
+        == "RA_ERR_UNSUPPORTED"
+
+
+def test_permute_validation(ra):
+    src = _t((4, 16, 28, 128))
+    dst = _t((7, 64, 128))
+    v = lambda s, d, P, r, dr: ra.STATUS[ra.ulysses_permute_validate(s, d, P, r, dr)]
+    assert v(src, dst, 4, 0, 0) == "RA_OK"
+    assert v(src, _t((4, 7, 64, 128)), 4, -1, 0) == "RA_OK"
+    assert v(dst, src, 4, 3, 1) == "RA_OK"
+    assert v(src, dst, 4, 4, 0) == "RA_ERR_RANGE"
+    assert v(src, dst, 4, -2, 0) == "RA_ERR_RANGE"
+    assert v(src, dst, 4, 0, 2) == "RA_ERR_RANGE"
+    assert v(src, dst.float(), 4, 0, 0) == "RA_ERR_DTYPE"
+    assert v(_t((4, 16, 30, 128)), dst, 4, 0, 0) == "RA_ERR_SHAPE"  # H % P
+    assert v(src, _t((7, 63, 128)), 4, 0, 0) == "RA_ERR_SHAPE"
+    assert v(_t((4, 16, 28, 4)), _t((7, 64, 4)), 4, 0, 0) == "RA_ERR_ALIGN"  # 8-byte rows
+
+
+def test_bwd_validation(ra):
+    q, k, v = _t((1, 4, 64, 128)), _t((1, 2, 64, 128)), _t((1, 2, 64, 128))
+    o, do, lse = _t(q.shape), _t(q.shape), torch.zeros(1, 4, 64)
+    dq, dk, dv = _t(q.shape), _t(k.shape), _t(k.shape)
+    val = lambda *a, **kw: ra.STATUS[ra.attn_bwd_validate(*a, **kw)]
+    assert val(q, k, v, o, do, lse, dq, dk, dv, causal=True) == "RA_OK"
+    assert val(q, k, v, o, do, lse, dq, dk, dv.float()) == "RA_ERR_DTYPE"
+    assert val(q, k, v, o, do, lse, dq, _t((1, 2, 65, 128)), dv) == "RA_ERR_SHAPE"
+    f = lambda t: t.float()
+    assert val(f(q), f(k), f(v), f(o), f(do), lse, f(dq), f(dk), f(dv)) == "RA_ERR_UNSUPPORTED"
+    assert ra.attn_bwd_workspace_size(q, k) >= 4 * 64 * 4
+    assert ra.attn_bwd_workspace_size(q, _t((1, 3, 64, 128))) == 0
