@@ -82,7 +82,7 @@ def cpu_baseline(w, budget_s: float = 15.0):
     k64 = si.bf16_bits_to_f32(si.bf16_bits(k)).astype(np.float64)
     v64 = si.bf16_bits_to_f32(si.bf16_bits(v)).astype(np.float64)
     blk = 128
-    starts = list(range(0, Sq, max(blk, Sq // 64)))
+    starts = list(range(0, Sq, blk))
     rng.shuffle(starts)
     done_flops, rows, t0 = 0.0, 0, time.perf_counter()
     for a in starts:

@@ -13,20 +13,33 @@
 //        each block keeps a Q tile on chip while K/V tiles stream through, the online
 //        softmax keeps a running max and normaliser, only the output is written back.
 //
-// Design on gfx950 (CDNA4):
-//   * one workgroup = 4 wavefronts = 128 query rows (32 per wave) of one (batch, head);
-//   * K/V tiles of 64 keys are double-buffered in LDS; the next tile's global loads
-//     are issued before the current tile's math and land in the other buffer after it;
-//   * scores are computed transposed, S^T = K Q^T, so each lane owns ONE query row
-//     (column l%32 of the MFMA output) and 16 of the 32 keys of each 32-key block:
-//     the row max / row sum are 32 in-register ops plus one v_permlane32_swap;
-//   * P^T stays in registers and feeds O^T += V^T P^T directly (the MFMA output
-//     layout of S^T is the B-operand layout of the next MFMA once the k order of V^T
-//     is chosen to match); V is transposed on its way into LDS for the bf16 path;
-//   * exponentials are base 2 with scale*log2(e) folded into one FMA per score;
+// Design on gfx950 (CDNA4), from measured rates (MFMA 32x32x16 bf16 ~37 clk/SIMD;
+// v_exp_f32 ~5x a plain VALU op; ds_read_b128 ~190 B/clk/CU vs ~120 for b64):
+//   * one workgroup = 8 wavefronts = 256 query rows (32 per wave) of one (batch, head);
+//     two waves per SIMD, so one wave's softmax (VALU) runs under the other's MFMAs;
+//     all 8 waves share each K/V tile in LDS (one global read of K/V per 256 rows);
+//   * K/V tiles of 64 keys, double-buffered in LDS: the next tile's global loads are
+//     issued before the current tile's math and stored to the other buffer after it;
+//     waves 0-3 fetch V, waves 4-7 fetch K; loads are unconditional (rows past the end
+//     are clamped and masked), so the compiler's memory counters stay exact;
+//   * scores are computed transposed, S^T = K Q^T (Q stays in registers as the B
+//     operand): each lane owns ONE query row and 16 of each 32 keys, so the row max is
+//     in-register v_max3 plus one v_permlane32_swap and the row sum needs no shuffle;
+//   * P^T feeds O^T += V^T P^T straight from registers.  V is transposed on its way into
+//     LDS with its keys permuted so that the 8 keys a lane needs for one MFMA are
+//     contiguous: every MFMA operand is a single conflict-free ds_read_b128;
+//   * exp2 with scale*log2(e) folded into one FMA per score; P rounded to bf16 with one
+//     v_cvt_pk per pair for the PV MFMA, while the row sum adds the fp32 values;
+//   * lazy rescale: the running max only moves (and O, l are only rescaled) when a
+//     tile's max exceeds it by more than 2^8; otherwise P <= 256, which fp32 and bf16
+//     hold exactly as well as P <= 1.  The final o = O / l and lse = m + log2 l use the
+//     same max, so the result is unchanged;
 //   * the ring walk skips chunks (and tiles) that lie entirely after the block's last
 //     query position under the causal mask; only tiles that straddle the diagonal or a
-//     chunk end pay for the element mask.
+//     chunk end pay for the element mask; waves whose rows all precede a tile skip it;
+//   * heaviest query tiles are dispatched first (causal work grows with the tile
+//     index), and heads are grouped so that consecutive workgroups -- which the
+//     dispatcher spreads over the 8 XCDs -- land on XCDs that share key/value heads.
 #include <math.h>
 
 #include "common.h"
@@ -35,127 +48,94 @@
 namespace ra {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kWaves = 4;
-constexpr int BM = 128;  // query rows per workgroup
-constexpr int BN = 64;   // keys per tile
+constexpr int kWaves = 8;
+constexpr int kThreads = 64 * kWaves;
+constexpr int BM = 32 * kWaves;  // query rows per workgroup
+constexpr int BN = 64;           // keys per tile
+constexpr float kLazyRescale = 8.0f;  // log2 units
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 // ---------------------------------------------------------------------------------
-// Ring walk: tiles of BN keys, chunk by chunk in the order (start + t) mod P.  Inside
-// a chunk, tiles stop at the last key any query row of the block can see.
-// ---------------------------------------------------------------------------------
-struct RingWalk {
-  int P, start, L;
-  bool causal;
-  int64_t vis_lim;  // keys with local index < vis_lim are visible to the block's last row
-
-  int t, kb, kend, cend;  // ring step, tile start, visible end of chunk, chunk end
-
-  __device__ void init(const FwdArgs &a, bool causal_, int64_t qpos_hi) {
-    P = a.num_chunks;
-    start = a.start_chunk;
-    L = a.chunk_len;
-    causal = causal_;
-    vis_lim = qpos_hi - a.kv_offset + 1;
-    t = -1;
-    kb = 0;
-    kend = 0;
-    cend = 0;
-    advance();
-  }
-  __device__ bool valid() const { return t < P; }
-  __device__ void advance() {
-    kb += BN;
-    while (kb >= kend) {
-      ++t;
-      if (t >= P) return;
-      int c = start + t;
-      if (c >= P) c -= P;
-      kb = c * L;
-      cend = kb + L;
-      kend = cend;
-      if (causal && vis_lim < (int64_t)kend) kend = vis_lim > kb ? (int)vis_lim : kb;
-    }
-  }
-};
-
-// ---------------------------------------------------------------------------------
-// bf16 traits: 32x32x16 bf16 MFMA; K row-major in LDS, V transposed in LDS.
+// bf16 path: 32x32x16 bf16 MFMA; K row-major in LDS, V transposed + key-permuted in LDS.
 // ---------------------------------------------------------------------------------
 template <int D>
 struct Bf16Path {
   using elem_t = uint16_t;
-  static constexpr int KSTR = D + 8;    // K row stride (elements): 16-byte pad
-  static constexpr int VSTR = BN + 4;   // V^T row stride: 34 dwords, conflict-free reads
+  static constexpr int KSTR = D + 8;    // K row stride (elements): 68 dwords for D=128
+  static constexpr int VSTR = BN + 8;   // V^T row stride: 36 dwords -> b128 reads conflict-free
   static constexpr int K_ELEMS = BN * KSTR;
   static constexpr int V_ELEMS = D * VSTR;
   static constexpr int BUF_BYTES = (K_ELEMS + V_ELEMS) * 2;
-  static constexpr int KCH = BN * D / 8 / kThreads;  // 16-byte K chunks per thread
-  static constexpr int VBC = D / 8;                   // 8-wide column groups of V
-  static constexpr int VBLK = (BN / 4) * VBC;         // 4x8 V blocks per tile
+  static constexpr int KCH = BN * D / 8 / 256;  // 16-byte K chunks per K-loading thread
+  static constexpr int VBC = D / 8;              // 8-wide column groups of V
+  static constexpr int NST = KCH > 4 ? KCH : 4;  // staging registers (16-byte units)
 
   struct QFrag { bf16x8 x[D / 16]; };
-  struct Stage { u32x4 k[KCH]; u32x4 v[4]; };
+  struct Stage { u32x4 x[NST]; };
+  struct PFrag { u32x4 x[4]; };
 
   __device__ static void load_q(QFrag &qf, const FwdArgs &a, const elem_t *qbase, int qrow, int h) {
+    const int row = min(qrow, a.Sq - 1);
 #pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks) {
-      u32x4 u = {0u, 0u, 0u, 0u};
-      if (qrow < a.Sq) u = *(const u32x4 *)(qbase + (int64_t)qrow * a.q_ss + ks * 16 + 8 * h);
-      qf.x[ks] = as_bf16x8(u);
-    }
+    for (int ks = 0; ks < D / 16; ++ks)
+      qf.x[ks] = as_bf16x8(*(const u32x4 *)(qbase + (int64_t)row * a.q_ss + ks * 16 + 8 * h));
   }
 
+  // Threads 0..255 fetch V as 4-key x 8-dim blocks (key fastest across lanes);
+  // threads 256..511 fetch K as 16-byte row chunks.  Rows >= Skv are clamped.
   __device__ static void load_tile(Stage &st, const FwdArgs &a, const elem_t *kbase,
                                    const elem_t *vbase, int kb, int tid) {
+    if (tid < 256) {
+      if (tid < 16 * VBC) {
+        const int r = tid & 15, c = tid >> 4;
 #pragma unroll
-    for (int i = 0; i < KCH; ++i) {
-      int id = tid + kThreads * i;
-      int row = id / (D / 8), c8 = id % (D / 8);
-      int kv = kb + row;
-      u32x4 u = {0u, 0u, 0u, 0u};
-      if (kv < a.Skv) u = *(const u32x4 *)(kbase + (int64_t)kv * a.k_ss + c8 * 8);
-      st.k[i] = u;
-    }
-    if (tid < VBLK) {
-      int r = tid / VBC, c = tid % VBC;
+        for (int i = 0; i < 4; ++i) {
+          const int kv = min(kb + 4 * r + i, a.Skv - 1);
+          st.x[i] = *(const u32x4 *)(vbase + (int64_t)kv * a.v_ss + c * 8);
+        }
+      }
+    } else {
+      const int t = tid - 256;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        int kv = kb + 4 * r + i;
-        u32x4 u = {0u, 0u, 0u, 0u};
-        if (kv < a.Skv) u = *(const u32x4 *)(vbase + (int64_t)kv * a.v_ss + c * 8);
-        st.v[i] = u;
+      for (int i = 0; i < KCH; ++i) {
+        const int id = t + 256 * i;
+        const int row = id / (D / 8), c8 = id % (D / 8);
+        const int kv = min(kb + row, a.Skv - 1);
+        st.x[i] = *(const u32x4 *)(kbase + (int64_t)kv * a.k_ss + c8 * 8);
       }
     }
   }
 
   __device__ static void store_tile(const Stage &st, elem_t *buf, int tid) {
-    elem_t *Ks = buf;
-    elem_t *Vt = buf + K_ELEMS;
+    if (tid < 256) {
+      if (tid < 16 * VBC) {
+        elem_t *Vt = buf + K_ELEMS;
+        const int r = tid & 15, c = tid >> 4;
+        // keys 4r..4r+3 = 16*ks + 8*a + 4*hh + (0..3) go to positions 16*ks + 8*hh + 4*a
+        const int pos = 16 * (r >> 2) + 8 * (r & 1) + 4 * ((r >> 1) & 1);
 #pragma unroll
-    for (int i = 0; i < KCH; ++i) {
-      int id = tid + kThreads * i;
-      int row = id / (D / 8), c8 = id % (D / 8);
-      *(u32x4 *)(Ks + row * KSTR + c8 * 8) = st.k[i];
-    }
-    if (tid < VBLK) {
-      int r = tid / VBC, c = tid % VBC;
-      // 4 keys x 8 dims -> 8 dims x 4 keys (transpose through byte permutes)
+        for (int j = 0; j < 8; ++j) {
+          const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;
+          const int w = j >> 1;
+          const uint32_t lo = perm_b32(st.x[1][w], st.x[0][w], sel);
+          const uint32_t hi = perm_b32(st.x[3][w], st.x[2][w], sel);
+          *(u32x2 *)(Vt + (c * 8 + j) * VSTR + pos) = u32x2{lo, hi};
+        }
+      }
+    } else {
+      const int t = tid - 256;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;
-        const int w = j >> 1;
-        uint32_t lo = perm_b32(st.v[1][w], st.v[0][w], sel);
-        uint32_t hi = perm_b32(st.v[3][w], st.v[2][w], sel);
-        u32x2 pr = {lo, hi};
-        *(u32x2 *)(Vt + (c * 8 + j) * VSTR + 4 * r) = pr;
+      for (int i = 0; i < KCH; ++i) {
+        const int id = t + 256 * i;
+        const int row = id / (D / 8), c8 = id % (D / 8);
+        *(u32x4 *)(buf + row * KSTR + c8 * 8) = st.x[i];
       }
     }
   }
 
   // S^T[32 keys x 32 queries] for the two 32-key halves of the tile.
   __device__ static void qk(f32x16 (&s)[2], const QFrag &qf, const elem_t *buf, int lane) {
-    const elem_t *Ks = buf;
     const int r = lane & 31, h = lane >> 5;
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) s[mt] = f32x16{};
@@ -163,41 +143,50 @@ struct Bf16Path {
     for (int ks = 0; ks < D / 16; ++ks) {
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt) {
-        u32x4 kf = *(const u32x4 *)(Ks + (32 * mt + r) * KSTR + ks * 16 + 8 * h);
+        const u32x4 kf = *(const u32x4 *)(buf + (32 * mt + r) * KSTR + ks * 16 + 8 * h);
         s[mt] = mfma_bf16(as_bf16x8(kf), qf.x[ks], s[mt]);
       }
     }
   }
 
-  // O^T[D x 32 queries] += V^T P^T, P^T taken from the S^T registers (already exp'd).
-  __device__ static void pv(f32x16 (&o)[D / 32], const f32x16 (&p)[2], const elem_t *buf,
-                            int lane) {
-    const elem_t *Vt = buf + K_ELEMS;
-    const int r = lane & 31, h = lane >> 5;
-    u32x4 pf[4];
+  // p = exp2(s*c - m) -> bf16 pairs (the B operand of PV); returns this lane's sum of
+  // the fp32 values (the sum must not carry the bf16 rounding of single terms: rows
+  // with few visible keys would show it directly in lse).
+  __device__ static float exp_pack(const f32x16 (&s)[2], float c, float mneg, PFrag &pf) {
+    float acc0 = 0.f, acc1 = 0.f;
 #pragma unroll
     for (int kstep = 0; kstep < 4; ++kstep) {
       const int mt = kstep >> 1, s2 = kstep & 1;
 #pragma unroll
-      for (int w = 0; w < 4; ++w)
-        pf[kstep][w] = pack_bf16x2(p[mt][8 * s2 + 2 * w], p[mt][8 * s2 + 2 * w + 1]);
+      for (int w = 0; w < 4; ++w) {
+        const float p0 = fast_exp2(fmaf(s[mt][8 * s2 + 2 * w], c, mneg));
+        const float p1 = fast_exp2(fmaf(s[mt][8 * s2 + 2 * w + 1], c, mneg));
+        const bf16x2 pk = __builtin_convertvector((f32x2){p0, p1}, bf16x2);
+        pf.x[kstep][w] = __builtin_bit_cast(uint32_t, pk);
+        acc0 += p0;
+        acc1 += p1;
+      }
     }
+    return acc0 + acc1;
+  }
+
+  // O^T[D x 32 queries] += V^T P^T.
+  __device__ static void pv(f32x16 (&o)[D / 32], const PFrag &pf, const elem_t *buf, int lane) {
+    const elem_t *Vt = buf + K_ELEMS;
+    const int r = lane & 31, h = lane >> 5;
 #pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt) {
+    for (int kstep = 0; kstep < 4; ++kstep) {
 #pragma unroll
-      for (int kstep = 0; kstep < 4; ++kstep) {
-        const elem_t *row = Vt + (32 * dt + r) * VSTR + 16 * kstep + 4 * h;
-        u32x2 a0 = *(const u32x2 *)row;
-        u32x2 a1 = *(const u32x2 *)(row + 8);
-        u32x4 af = {a0[0], a0[1], a1[0], a1[1]};
-        o[dt] = mfma_bf16(as_bf16x8(af), as_bf16x8(pf[kstep]), o[dt]);
+      for (int dt = 0; dt < D / 32; ++dt) {
+        const u32x4 af = *(const u32x4 *)(Vt + (32 * dt + r) * VSTR + 16 * kstep + 8 * h);
+        o[dt] = mfma_bf16(as_bf16x8(af), as_bf16x8(pf.x[kstep]), o[dt]);
       }
     }
   }
 };
 
 // ---------------------------------------------------------------------------------
-// fp32 traits: 32x32x2 fp32 MFMA; K and V row-major in LDS.
+// fp32 path: 32x32x2 fp32 MFMA; K and V row-major in LDS; P stays fp32.
 // ---------------------------------------------------------------------------------
 template <int D>
 struct F32Path {
@@ -211,39 +200,33 @@ struct F32Path {
 
   struct QFrag { f32x2 x[D / 4]; };
   struct Stage { u32x4 k[CH]; u32x4 v[CH]; };
+  struct PFrag { f32x16 x[2]; };
 
   // MFMA step 2j+e of half h uses head dim 4j + 2h + e (A and B agree).
   __device__ static void load_q(QFrag &qf, const FwdArgs &a, const elem_t *qbase, int qrow, int h) {
+    const int row = min(qrow, a.Sq - 1);
 #pragma unroll
-    for (int j = 0; j < D / 4; ++j) {
-      f32x2 u = {0.f, 0.f};
-      if (qrow < a.Sq) u = *(const f32x2 *)(qbase + (int64_t)qrow * a.q_ss + 4 * j + 2 * h);
-      qf.x[j] = u;
-    }
+    for (int j = 0; j < D / 4; ++j)
+      qf.x[j] = *(const f32x2 *)(qbase + (int64_t)row * a.q_ss + 4 * j + 2 * h);
   }
 
   __device__ static void load_tile(Stage &st, const FwdArgs &a, const elem_t *kbase,
                                    const elem_t *vbase, int kb, int tid) {
 #pragma unroll
     for (int i = 0; i < CH; ++i) {
-      int id = tid + kThreads * i;
-      int row = id / (D / 4), c4 = id % (D / 4);
-      int kv = kb + row;
-      u32x4 uk = {0u, 0u, 0u, 0u}, uv = {0u, 0u, 0u, 0u};
-      if (kv < a.Skv) {
-        uk = *(const u32x4 *)(kbase + (int64_t)kv * a.k_ss + c4 * 4);
-        uv = *(const u32x4 *)(vbase + (int64_t)kv * a.v_ss + c4 * 4);
-      }
-      st.k[i] = uk;
-      st.v[i] = uv;
+      const int id = tid + kThreads * i;
+      const int row = id / (D / 4), c4 = id % (D / 4);
+      const int kv = min(kb + row, a.Skv - 1);
+      st.k[i] = *(const u32x4 *)(kbase + (int64_t)kv * a.k_ss + c4 * 4);
+      st.v[i] = *(const u32x4 *)(vbase + (int64_t)kv * a.v_ss + c4 * 4);
     }
   }
 
   __device__ static void store_tile(const Stage &st, elem_t *buf, int tid) {
 #pragma unroll
     for (int i = 0; i < CH; ++i) {
-      int id = tid + kThreads * i;
-      int row = id / (D / 4), c4 = id % (D / 4);
+      const int id = tid + kThreads * i;
+      const int row = id / (D / 4), c4 = id % (D / 4);
       *(u32x4 *)(buf + row * KSTR + c4 * 4) = st.k[i];
       *(u32x4 *)(buf + K_ELEMS + row * VSTR + c4 * 4) = st.v[i];
     }
@@ -257,15 +240,27 @@ struct F32Path {
     for (int j = 0; j < D / 4; ++j) {
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt) {
-        f32x2 kf = *(const f32x2 *)(buf + (32 * mt + r) * KSTR + 4 * j + 2 * h);
+        const f32x2 kf = *(const f32x2 *)(buf + (32 * mt + r) * KSTR + 4 * j + 2 * h);
         s[mt] = mfma_f32(kf[0], qf.x[j][0], s[mt]);
         s[mt] = mfma_f32(kf[1], qf.x[j][1], s[mt]);
       }
     }
   }
 
-  __device__ static void pv(f32x16 (&o)[D / 32], const f32x16 (&p)[2], const elem_t *buf,
-                            int lane) {
+  __device__ static float exp_pack(const f32x16 (&s)[2], float c, float mneg, PFrag &pf) {
+    float acc = 0.f;
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float p = fast_exp2(fmaf(s[mt][i], c, mneg));
+        pf.x[mt][i] = p;
+        acc += p;
+      }
+    return acc;
+  }
+
+  __device__ static void pv(f32x16 (&o)[D / 32], const PFrag &pf, const elem_t *buf, int lane) {
     const elem_t *Vs = buf + K_ELEMS;
     const int r = lane & 31, h = lane >> 5;
 #pragma unroll
@@ -275,11 +270,29 @@ struct F32Path {
         const int kv = 32 * mt + (i >> 2) * 8 + 4 * h + (i & 3);
 #pragma unroll
         for (int dt = 0; dt < D / 32; ++dt)
-          o[dt] = mfma_f32(Vs[kv * VSTR + 32 * dt + r], p[mt][i], o[dt]);
+          o[dt] = mfma_f32(Vs[kv * VSTR + 32 * dt + r], pf.x[mt][i], o[dt]);
       }
     }
   }
 };
+
+// Next tile of the ring walk: tiles of BN keys, chunk by chunk in the order
+// (start + t) mod P; inside a chunk, tiles stop at the last key visible to the
+// block's last query row (vis_lim).  t == P means done.
+__device__ __forceinline__ void ring_next(const FwdArgs &a, bool causal, int64_t vis_lim,
+                                          int &t, int &kb, int &kend, int &cend) {
+  kb += BN;
+  while (kb >= kend) {
+    ++t;
+    if (t >= a.num_chunks) return;
+    int c = a.start_chunk + t;
+    if (c >= a.num_chunks) c -= a.num_chunks;
+    kb = c * a.chunk_len;
+    cend = kb + a.chunk_len;
+    kend = cend;
+    if (causal && vis_lim < (int64_t)kend) kend = vis_lim > kb ? (int)vis_lim : kb;
+  }
+}
 
 // ---------------------------------------------------------------------------------
 // The kernel.
@@ -288,7 +301,6 @@ template <class Path, int D, bool CAUSAL>
 __global__ void __launch_bounds__(kThreads) attn_fwd_kernel(FwdArgs a) {
   using elem_t = typename Path::elem_t;
   __shared__ __attribute__((aligned(16))) unsigned char smem[2 * Path::BUF_BYTES];
-  auto buf_at = [&](int i) { return (elem_t *)(smem + i * Path::BUF_BYTES); };
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -296,13 +308,16 @@ __global__ void __launch_bounds__(kThreads) attn_fwd_kernel(FwdArgs a) {
   const int r32 = lane & 31;
   const int h = lane >> 5;
 
-  // Heaviest query tiles first (causal work grows with the tile index), heads fastest.
+  // Workgroup -> (query tile, head, batch): heaviest tiles first; when the head count
+  // is a multiple of 8, the heads a workgroup id maps to are grouped by id % 8 (the XCD).
+  const int HB = a.Hq * a.B;
   const int bid = blockIdx.x;
-  const int per_tile = a.Hq * a.B;
-  const int qt = a.num_q_tiles - 1 - bid / per_tile;
-  const int rest = bid % per_tile;
-  const int hq = rest % a.Hq;
-  const int b = rest / a.Hq;
+  const int trank = bid / HB;
+  int j = bid - trank * HB;
+  if ((HB & 7) == 0) j = (j & 7) * (HB >> 3) + (j >> 3);
+  const int hq = j % a.Hq;
+  const int b = j / a.Hq;
+  const int qt = a.num_q_tiles - 1 - trank;
   const int hk = hq / a.group;
 
   const int q0 = qt * BM;
@@ -317,6 +332,7 @@ __global__ void __launch_bounds__(kThreads) attn_fwd_kernel(FwdArgs a) {
   const int64_t wpos_first = a.q_offset + q0 + 32 * wave;
   const int64_t wpos_last = wpos_first + 31;
   const bool wave_active = (q0 + 32 * wave) < a.Sq;
+  const float c = a.scale_log2;
 
   typename Path::QFrag qf;
   Path::load_q(qf, a, qbase, qrow, h);
@@ -324,77 +340,80 @@ __global__ void __launch_bounds__(kThreads) attn_fwd_kernel(FwdArgs a) {
   f32x16 o[D / 32];
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt) o[dt] = f32x16{};
-  float m_run = -INFINITY;  // running max, scaled log2 domain (scale*log2e*s)
-  float l_run = 0.f;        // running exp-sum of this lane's keys (halves summed at the end)
+  float m_run = -INFINITY;  // running max in the scaled log2 domain (c * s)
+  float l_run = 0.f;        // this lane's share of the exp-sum (halves summed at the end)
 
-  RingWalk walk;
-  walk.init(a, CAUSAL, a.q_offset + qlast);
+  const int64_t vis_lim = a.q_offset + qlast - a.kv_offset + 1;
+  int t = -1, kb = 0, kend = 0, cend = 0;
+  ring_next(a, CAUSAL, vis_lim, t, kb, kend, cend);
 
   typename Path::Stage st;
-  if (walk.valid()) {
-    Path::load_tile(st, a, kbase, vbase, walk.kb, tid);
-    Path::store_tile(st, buf_at(0), tid);
+  if (t < a.num_chunks) {
+    Path::load_tile(st, a, kbase, vbase, kb, tid);
+    Path::store_tile(st, (elem_t *)smem, tid);
   }
+  // All prologue loads (Q included) have landed: without this the compiler keeps Q's
+  // loads "pending" on the no-tile path and the loop's first MFMAs would wait on the
+  // freshly issued prefetch as well (vmcnt counts in order).
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
   __syncthreads();
 
   int cur = 0;
-  while (walk.valid()) {
-    const int kb = walk.kb;
-    const int cend = walk.cend;
-    RingWalk nxt = walk;
-    nxt.advance();
-    if (nxt.valid()) Path::load_tile(st, a, kbase, vbase, nxt.kb, tid);
+  while (t < a.num_chunks) {
+    const int kb_cur = kb, cend_cur = cend;
+    ring_next(a, CAUSAL, vis_lim, t, kb, kend, cend);
+    const bool has_next = t < a.num_chunks;
+    if (has_next) Path::load_tile(st, a, kbase, vbase, kb, tid);
 
-    const int64_t kpos0 = a.kv_offset + kb;
-    const int kvalid = min(BN, cend - kb);  // keys of this tile inside the chunk
+    const elem_t *buf = (const elem_t *)(smem + cur * Path::BUF_BYTES);
+    const int64_t kpos0 = a.kv_offset + kb_cur;
+    const int kvalid = min(BN, cend_cur - kb_cur);  // keys of this tile inside the chunk
     const bool skip = !wave_active || (CAUSAL && kpos0 > wpos_last);
     if (!skip) {
       f32x16 s[2];
-      Path::qk(s, qf, buf_at(cur), lane);
+      Path::qk(s, qf, buf, lane);
 
-      const bool need_mask =
-          (kvalid < BN) || (CAUSAL && kpos0 + kvalid - 1 > wpos_first);
+      const bool need_mask = (kvalid < BN) || (CAUSAL && kpos0 + kvalid - 1 > wpos_first);
       if (need_mask) {
+        // keys kk < lim are visible to this lane's row
+        int64_t lim64 = kvalid;
+        if (CAUSAL) lim64 = min(lim64, qpos - kpos0 + 1);
+        const int lim = (int)max<int64_t>(lim64, 0) - 4 * h;
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
-            const int kk = 32 * mt + (i >> 2) * 8 + 4 * h + (i & 3);
-            bool vis = kk < kvalid;
-            if (CAUSAL) vis = vis && (kpos0 + kk <= qpos);
-            s[mt][i] = vis ? s[mt][i] : -INFINITY;
+            const int kk = 32 * mt + (i >> 2) * 8 + (i & 3);  // minus the 4h offset
+            s[mt][i] = kk < lim ? s[mt][i] : -INFINITY;
           }
       }
-      // online softmax (base 2)
-      float mx = s[0][0];
+      // tile row max (max3 tree), combined across the two halves
+      float mx = fmaxf(fmaxf(s[0][0], s[0][1]), s[0][2]);
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
+      for (int i = 3; i < 15; i += 2) mx = fmaxf(fmaxf(mx, s[0][i]), s[0][i + 1]);
+      mx = fmaxf(mx, s[0][15]);
 #pragma unroll
-        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[mt][i]);
-      mx = halves_max(mx);
-      const float m_new = fmaxf(m_run, mx * a.scale_log2);
-      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-      const float alpha = fast_exp2(m_run - m_use);
-      float rs = 0.f;
+      for (int i = 0; i < 16; i += 2) mx = fmaxf(fmaxf(mx, s[1][i]), s[1][i + 1]);
+      mx = halves_max(mx) * c;
+
+      // lazy rescale: only when some row's max grew by more than kLazyRescale
+      if (__builtin_amdgcn_ballot_w64(mx > m_run + kLazyRescale) != 0) {
+        const float m_new = fmaxf(m_run, mx);
+        const float alpha = m_new == -INFINITY ? 1.f : fast_exp2(m_run - m_new);
+        l_run *= alpha;
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          float pv = fast_exp2(fmaf(s[mt][i], a.scale_log2, -m_use));
-          s[mt][i] = pv;
-          rs += pv;
-        }
-      l_run = fmaf(l_run, alpha, rs);
-      m_run = m_new;
-#pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt) o[dt] *= alpha;
-      Path::pv(o, s, buf_at(cur), lane);
+        for (int dt = 0; dt < D / 32; ++dt) o[dt] *= alpha;
+        m_run = m_new;
+      }
+      const float mneg = m_run == -INFINITY ? 0.f : -m_run;
+      typename Path::PFrag pf;
+      l_run += Path::exp_pack(s, c, mneg, pf);
+      Path::pv(o, pf, buf, lane);
     }
 
-    if (nxt.valid()) Path::store_tile(st, buf_at(cur ^ 1), tid);
+    if (has_next) Path::store_tile(st, (elem_t *)(smem + (cur ^ 1) * Path::BUF_BYTES), tid);
     __syncthreads();
     cur ^= 1;
-    walk = nxt;
   }
 
   // Epilogue: o = O / l, lse = ln(sum) = (m + log2 l) * ln 2.
@@ -402,7 +421,7 @@ __global__ void __launch_bounds__(kThreads) attn_fwd_kernel(FwdArgs a) {
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   if (qrow < a.Sq) {
     if (h == 0) {
-      float lse = l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
+      const float lse = l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
       a.lse[b * a.l_sb + hq * a.l_sh + qrow] = lse;
     }
     const int64_t orow = b * a.o_sb + hq * a.o_sh + (int64_t)qrow * a.o_ss;
@@ -411,14 +430,15 @@ __global__ void __launch_bounds__(kThreads) attn_fwd_kernel(FwdArgs a) {
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int d = 32 * dt + 8 * g + 4 * h;
-        float x0 = o[dt][4 * g + 0] * inv, x1 = o[dt][4 * g + 1] * inv;
-        float x2 = o[dt][4 * g + 2] * inv, x3 = o[dt][4 * g + 3] * inv;
+        const float x0 = o[dt][4 * g + 0] * inv, x1 = o[dt][4 * g + 1] * inv;
+        const float x2 = o[dt][4 * g + 2] * inv, x3 = o[dt][4 * g + 3] * inv;
         if (a.o_is_f32) {
-          float4 w = {x0, x1, x2, x3};
-          *(float4 *)((float *)a.o + orow + d) = w;
+          *(float4 *)((float *)a.o + orow + d) = float4{x0, x1, x2, x3};
         } else {
-          u32x2 w = {pack_bf16x2(x0, x1), pack_bf16x2(x2, x3)};
-          *(u32x2 *)((uint16_t *)a.o + orow + d) = w;
+          const bf16x2 lo = __builtin_convertvector((f32x2){x0, x1}, bf16x2);
+          const bf16x2 hi = __builtin_convertvector((f32x2){x2, x3}, bf16x2);
+          *(u32x2 *)((uint16_t *)a.o + orow + d) =
+              u32x2{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
         }
       }
   }
