@@ -48,32 +48,94 @@
 namespace ra {
 namespace {
 
-constexpr int kWaves = 8;
-constexpr int kThreads = 64 * kWaves;
-constexpr int BM = 32 * kWaves;  // query rows per workgroup
 constexpr int BN = 64;           // keys per tile
 constexpr float kLazyRescale = 8.0f;  // log2 units
+#ifndef RA_FWD_BF16_WAVES
+#define RA_FWD_BF16_WAVES 8
+#endif
+constexpr int kBf16Waves = RA_FWD_BF16_WAVES;  // 8 measured faster than 2 x 4
+#ifndef RA_FWD_PIPELINE
+#define RA_FWD_PIPELINE 0
+#endif
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 // ---------------------------------------------------------------------------------
 // bf16 path: 32x32x16 bf16 MFMA; K row-major in LDS, V transposed + key-permuted in LDS.
 // ---------------------------------------------------------------------------------
-template <int D>
+template <int D, int NW>
 struct Bf16Path {
   using elem_t = uint16_t;
+  static constexpr int kWaves = NW;           // 32 query rows per wave
+  static constexpr int kThreads = 64 * NW;
   static constexpr int KSTR = D + 8;    // K row stride (elements): 68 dwords for D=128
   static constexpr int VSTR = BN + 8;   // V^T row stride: 36 dwords -> b128 reads conflict-free
   static constexpr int K_ELEMS = BN * KSTR;
   static constexpr int V_ELEMS = D * VSTR;
   static constexpr int BUF_BYTES = (K_ELEMS + V_ELEMS) * 2;
-  static constexpr int KCH = BN * D / 8 / 256;  // 16-byte K chunks per K-loading thread
-  static constexpr int VBC = D / 8;              // 8-wide column groups of V
-  static constexpr int NST = KCH > 4 ? KCH : 4;  // staging registers (16-byte units)
+  // With 8 waves, threads 0..255 fetch V and 256..511 fetch K; with 4 waves every
+  // thread fetches one V block and its share of K.
+  static constexpr int KT = NW == 8 ? 256 : 64 * NW;  // threads fetching K
+  static constexpr int KCH = BN * D / 8 / KT;          // 16-byte K chunks per such thread
+  static constexpr int VBC = D / 8;                    // 8-wide column groups of V
+  static constexpr int VOFF = NW == 8 ? 0 : 4;         // first staging slot of K
+  static constexpr int NST = NW == 8 ? (KCH > 4 ? KCH : 4) : 4 + KCH;
 
   struct QFrag { bf16x8 x[D / 16]; };
   struct Stage { u32x4 x[NST]; };
   struct PFrag { u32x4 x[4]; };
+  static constexpr bool kPipelined = RA_FWD_PIPELINE;  // three LDS tiles fit (105 KiB)
+
+  // One pipelined step: S^T of the NEXT tile (QK MFMAs, K from slot bn) interleaved by
+  // hand with the softmax of the CURRENT tile (sc -> bf16 P), then O^T += V^T P^T with V
+  // from slot bc.  Each QK MFMA is paired with one pair of exponentials and the K read
+  // kDepth steps ahead; the fences keep the scheduler from regrouping them.  Returns
+  // this lane's share of the current tile's exp-sum.
+  __device__ static float fused_step(f32x16 (&sn)[2], const QFrag &qf, const elem_t *bn,
+                                     const f32x16 (&sc)[2], float c, float mneg,
+                                     f32x16 (&o)[D / 32], const elem_t *bc, int lane) {
+    const int r = lane & 31, h = lane >> 5;
+    constexpr int NQK = 2 * (D / 16), NPV = 4 * (D / 32);
+    constexpr int PPS = 16 / NQK;  // softmax pairs per QK MFMA (16 pairs per tile)
+    u32x4 kf[kDepth];
+    VPre vp;
+#pragma unroll
+    for (int i = 0; i < kDepth; ++i) kf[i] = k_frag(bn, i, r, h);
+#pragma unroll
+    for (int i = 0; i < kDepth; ++i) vp.x[i] = v_frag(bc, i, r, h);
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) sn[mt] = f32x16{};
+    PFrag pf;
+    float acc0 = 0.f, acc1 = 0.f;
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int step = 0; step < NQK; ++step) {
+      const int ks = step >> 1, mt = step & 1;
+      sn[mt] = mfma_bf16(as_bf16x8(kf[step % kDepth]), qf.x[ks], sn[mt]);
+      if (step + kDepth < NQK) kf[step % kDepth] = k_frag(bn, step + kDepth, r, h);
+#pragma unroll
+      for (int j = 0; j < PPS; ++j) {
+        const int pair = step * PPS + j;
+        const int kstep = pair >> 2, w = pair & 3;
+        const int m2 = kstep >> 1, s2 = kstep & 1;
+        const float p0 = fast_exp2(fmaf(sc[m2][8 * s2 + 2 * w], c, mneg));
+        const float p1 = fast_exp2(fmaf(sc[m2][8 * s2 + 2 * w + 1], c, mneg));
+        const bf16x2 pk = __builtin_convertvector((f32x2){p0, p1}, bf16x2);
+        pf.x[kstep][w] = __builtin_bit_cast(uint32_t, pk);
+        acc0 += p0;
+        acc1 += p1;
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int step = 0; step < NPV; ++step) {
+      const int kstep = step / (D / 32), dt = step % (D / 32);
+      o[dt] = mfma_bf16(as_bf16x8(vp.x[step % kDepth]), as_bf16x8(pf.x[kstep]), o[dt]);
+      if (step + kDepth < NPV) vp.x[step % kDepth] = v_frag(bc, step + kDepth, r, h);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    return acc0 + acc1;
+  }
 
   __device__ static void load_q(QFrag &qf, const FwdArgs &a, const elem_t *qbase, int qrow, int h) {
     const int row = min(qrow, a.Sq - 1);
@@ -82,70 +144,80 @@ struct Bf16Path {
       qf.x[ks] = as_bf16x8(*(const u32x4 *)(qbase + (int64_t)row * a.q_ss + ks * 16 + 8 * h));
   }
 
-  // Threads 0..255 fetch V as 4-key x 8-dim blocks (key fastest across lanes);
-  // threads 256..511 fetch K as 16-byte row chunks.  Rows >= Skv are clamped.
+  // V is fetched as 4-key x 8-dim blocks (key fastest across lanes), K as 16-byte row
+  // chunks.  Rows >= Skv are clamped (and masked later).
   __device__ static void load_tile(Stage &st, const FwdArgs &a, const elem_t *kbase,
                                    const elem_t *vbase, int kb, int tid) {
-    if (tid < 256) {
-      if (tid < 16 * VBC) {
-        const int r = tid & 15, c = tid >> 4;
+    const bool v_role = NW == 8 ? tid < 256 : true;
+    const bool k_role = NW == 8 ? tid >= 256 : true;
+    if (v_role && tid < 16 * VBC) {
+      const int r = tid & 15, c = tid >> 4;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int kv = min(kb + 4 * r + i, a.Skv - 1);
-          st.x[i] = *(const u32x4 *)(vbase + (int64_t)kv * a.v_ss + c * 8);
-        }
+      for (int i = 0; i < 4; ++i) {
+        const int kv = min(kb + 4 * r + i, a.Skv - 1);
+        st.x[i] = *(const u32x4 *)(vbase + (int64_t)kv * a.v_ss + c * 8);
       }
-    } else {
-      const int t = tid - 256;
+    }
+    if (k_role) {
+      const int t = NW == 8 ? tid - 256 : tid;
 #pragma unroll
       for (int i = 0; i < KCH; ++i) {
-        const int id = t + 256 * i;
+        const int id = t + KT * i;
         const int row = id / (D / 8), c8 = id % (D / 8);
         const int kv = min(kb + row, a.Skv - 1);
-        st.x[i] = *(const u32x4 *)(kbase + (int64_t)kv * a.k_ss + c8 * 8);
+        st.x[VOFF + i] = *(const u32x4 *)(kbase + (int64_t)kv * a.k_ss + c8 * 8);
       }
     }
   }
 
   __device__ static void store_tile(const Stage &st, elem_t *buf, int tid) {
-    if (tid < 256) {
-      if (tid < 16 * VBC) {
-        elem_t *Vt = buf + K_ELEMS;
-        const int r = tid & 15, c = tid >> 4;
-        // keys 4r..4r+3 = 16*ks + 8*a + 4*hh + (0..3) go to positions 16*ks + 8*hh + 4*a
-        const int pos = 16 * (r >> 2) + 8 * (r & 1) + 4 * ((r >> 1) & 1);
+    const bool v_role = NW == 8 ? tid < 256 : true;
+    const bool k_role = NW == 8 ? tid >= 256 : true;
+    if (v_role && tid < 16 * VBC) {
+      elem_t *Vt = buf + K_ELEMS;
+      const int r = tid & 15, c = tid >> 4;
+      // keys 4r..4r+3 = 16*ks + 8*a + 4*hh + (0..3) go to positions 16*ks + 8*hh + 4*a
+      const int pos = 16 * (r >> 2) + 8 * (r & 1) + 4 * ((r >> 1) & 1);
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;
-          const int w = j >> 1;
-          const uint32_t lo = perm_b32(st.x[1][w], st.x[0][w], sel);
-          const uint32_t hi = perm_b32(st.x[3][w], st.x[2][w], sel);
-          *(u32x2 *)(Vt + (c * 8 + j) * VSTR + pos) = u32x2{lo, hi};
-        }
+      for (int j = 0; j < 8; ++j) {
+        const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;
+        const int w = j >> 1;
+        const uint32_t lo = perm_b32(st.x[1][w], st.x[0][w], sel);
+        const uint32_t hi = perm_b32(st.x[3][w], st.x[2][w], sel);
+        *(u32x2 *)(Vt + (c * 8 + j) * VSTR + pos) = u32x2{lo, hi};
       }
-    } else {
-      const int t = tid - 256;
+    }
+    if (k_role) {
+      const int t = NW == 8 ? tid - 256 : tid;
 #pragma unroll
       for (int i = 0; i < KCH; ++i) {
-        const int id = t + 256 * i;
+        const int id = t + KT * i;
         const int row = id / (D / 8), c8 = id % (D / 8);
-        *(u32x4 *)(buf + row * KSTR + c8 * 8) = st.x[i];
+        *(u32x4 *)(buf + row * KSTR + c8 * 8) = st.x[VOFF + i];
       }
     }
   }
 
-  // S^T[32 keys x 32 queries] for the two 32-key halves of the tile.
+  // S^T[32 keys x 32 queries] for the two 32-key halves of the tile.  K fragments are
+  // read from LDS kDepth MFMAs ahead of their use (an LDS round trip is several MFMAs).
+  static constexpr int kDepth = 2;
+  __device__ static u32x4 k_frag(const elem_t *buf, int step, int r, int h) {
+    const int ks = step >> 1, mt = step & 1;
+    return *(const u32x4 *)(buf + (32 * mt + r) * KSTR + ks * 16 + 8 * h);
+  }
   __device__ static void qk(f32x16 (&s)[2], const QFrag &qf, const elem_t *buf, int lane) {
     const int r = lane & 31, h = lane >> 5;
+    constexpr int NSTEP = 2 * (D / 16);
+    u32x4 kf[kDepth];
+#pragma unroll
+    for (int i = 0; i < kDepth; ++i) kf[i] = k_frag(buf, i, r, h);
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) s[mt] = f32x16{};
 #pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks) {
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
-        const u32x4 kf = *(const u32x4 *)(buf + (32 * mt + r) * KSTR + ks * 16 + 8 * h);
-        s[mt] = mfma_bf16(as_bf16x8(kf), qf.x[ks], s[mt]);
-      }
+    for (int step = 0; step < NSTEP; ++step) {
+      const int ks = step >> 1, mt = step & 1;
+      s[mt] = mfma_bf16(as_bf16x8(kf[step % kDepth]), qf.x[ks], s[mt]);
+      if (step + kDepth < NSTEP) kf[step % kDepth] = k_frag(buf, step + kDepth, r, h);
     }
   }
 
@@ -170,17 +242,27 @@ struct Bf16Path {
     return acc0 + acc1;
   }
 
-  // O^T[D x 32 queries] += V^T P^T.
-  __device__ static void pv(f32x16 (&o)[D / 32], const PFrag &pf, const elem_t *buf, int lane) {
-    const elem_t *Vt = buf + K_ELEMS;
+  // O^T[D x 32 queries] += V^T P^T.  V^T fragments run kDepth MFMAs ahead; the first
+  // kDepth are read by pv_prefetch before the softmax so its VALU work hides them.
+  struct VPre { u32x4 x[kDepth]; };
+  __device__ static u32x4 v_frag(const elem_t *buf, int step, int r, int h) {
+    const int kstep = step / (D / 32), dt = step % (D / 32);
+    return *(const u32x4 *)(buf + K_ELEMS + (32 * dt + r) * VSTR + 16 * kstep + 8 * h);
+  }
+  __device__ static void pv_prefetch(VPre &vp, const elem_t *buf, int lane) {
     const int r = lane & 31, h = lane >> 5;
 #pragma unroll
-    for (int kstep = 0; kstep < 4; ++kstep) {
+    for (int i = 0; i < kDepth; ++i) vp.x[i] = v_frag(buf, i, r, h);
+  }
+  __device__ static void pv(f32x16 (&o)[D / 32], const PFrag &pf, VPre &vp, const elem_t *buf,
+                            int lane) {
+    const int r = lane & 31, h = lane >> 5;
+    constexpr int NSTEP = 4 * (D / 32);
 #pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt) {
-        const u32x4 af = *(const u32x4 *)(Vt + (32 * dt + r) * VSTR + 16 * kstep + 8 * h);
-        o[dt] = mfma_bf16(as_bf16x8(af), as_bf16x8(pf.x[kstep]), o[dt]);
-      }
+    for (int step = 0; step < NSTEP; ++step) {
+      const int kstep = step / (D / 32), dt = step % (D / 32);
+      o[dt] = mfma_bf16(as_bf16x8(vp.x[step % kDepth]), as_bf16x8(pf.x[kstep]), o[dt]);
+      if (step + kDepth < NSTEP) vp.x[step % kDepth] = v_frag(buf, step + kDepth, r, h);
     }
   }
 };
@@ -191,6 +273,8 @@ struct Bf16Path {
 template <int D>
 struct F32Path {
   using elem_t = float;
+  static constexpr int kWaves = 8;
+  static constexpr int kThreads = 64 * kWaves;
   static constexpr int KSTR = D + 4;
   static constexpr int VSTR = D + 4;
   static constexpr int K_ELEMS = BN * KSTR;
@@ -201,6 +285,12 @@ struct F32Path {
   struct QFrag { f32x2 x[D / 4]; };
   struct Stage { u32x4 k[CH]; u32x4 v[CH]; };
   struct PFrag { f32x16 x[2]; };
+  static constexpr bool kPipelined = false;  // three fp32 tiles would not fit in LDS
+  __device__ static float fused_step(f32x16 (&)[2], const QFrag &, const elem_t *,
+                                     const f32x16 (&)[2], float, float, f32x16 (&)[D / 32],
+                                     const elem_t *, int) {
+    return 0.f;  // never called: the fp32 path uses the double-buffered loop
+  }
 
   // MFMA step 2j+e of half h uses head dim 4j + 2h + e (A and B agree).
   __device__ static void load_q(QFrag &qf, const FwdArgs &a, const elem_t *qbase, int qrow, int h) {
@@ -260,7 +350,10 @@ struct F32Path {
     return acc;
   }
 
-  __device__ static void pv(f32x16 (&o)[D / 32], const PFrag &pf, const elem_t *buf, int lane) {
+  struct VPre {};
+  __device__ static void pv_prefetch(VPre &, const elem_t *, int) {}
+  __device__ static void pv(f32x16 (&o)[D / 32], const PFrag &pf, VPre &, const elem_t *buf,
+                            int lane) {
     const elem_t *Vs = buf + K_ELEMS;
     const int r = lane & 31, h = lane >> 5;
 #pragma unroll
@@ -298,9 +391,12 @@ __device__ __forceinline__ void ring_next(const FwdArgs &a, bool causal, int64_t
 // The kernel.
 // ---------------------------------------------------------------------------------
 template <class Path, int D, bool CAUSAL>
-__global__ void __launch_bounds__(kThreads) attn_fwd_kernel(FwdArgs a) {
+__global__ void __launch_bounds__(Path::kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+attn_fwd_kernel(FwdArgs a) {
   using elem_t = typename Path::elem_t;
-  __shared__ __attribute__((aligned(16))) unsigned char smem[2 * Path::BUF_BYTES];
+  constexpr int BM = 32 * Path::kWaves;  // query rows per workgroup
+  constexpr int NBUF = Path::kPipelined ? 3 : 2;
+  __shared__ __attribute__((aligned(16))) unsigned char smem[NBUF * Path::BUF_BYTES];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -343,77 +439,150 @@ __global__ void __launch_bounds__(kThreads) attn_fwd_kernel(FwdArgs a) {
   float m_run = -INFINITY;  // running max in the scaled log2 domain (c * s)
   float l_run = 0.f;        // this lane's share of the exp-sum (halves summed at the end)
 
+  auto tile_buf = [&](int i) { return (elem_t *)(smem + i * Path::BUF_BYTES); };
+  // A wave skips a tile when every key of it is in the future of all its rows.
+  auto skips = [&](int kbx) {
+    return !wave_active || (CAUSAL && a.kv_offset + kbx > wpos_last);
+  };
+  // Mask a tile's scores (only tiles that straddle the diagonal or a chunk end), return
+  // the row max in the scaled log2 domain and apply the lazy rescale to O and l.
+  auto mask_max_rescale = [&](f32x16 (&s)[2], int kbx, int cendx) {
+    const int64_t kpos0 = a.kv_offset + kbx;
+    const int kvalid = min(BN, cendx - kbx);
+    const bool need_mask = (kvalid < BN) || (CAUSAL && kpos0 + kvalid - 1 > wpos_first);
+    if (need_mask) {
+      int lim = kvalid;  // keys kk < lim are visible to this lane's row
+      if (CAUSAL) {
+        const int64_t vis = qpos - kpos0 + 1;  // may be <= 0 or > BN
+        lim = vis < (int64_t)lim ? (vis > 0 ? (int)vis : 0) : lim;
+      }
+      lim -= 4 * h;
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int kk = 32 * mt + (i >> 2) * 8 + (i & 3);  // minus the 4h offset
+          s[mt][i] = kk < lim ? s[mt][i] : -INFINITY;
+        }
+    }
+    float mx = fmaxf(fmaxf(s[0][0], s[0][1]), s[0][2]);
+#pragma unroll
+    for (int i = 3; i < 15; i += 2) mx = fmaxf(fmaxf(mx, s[0][i]), s[0][i + 1]);
+    mx = fmaxf(mx, s[0][15]);
+#pragma unroll
+    for (int i = 0; i < 16; i += 2) mx = fmaxf(fmaxf(mx, s[1][i]), s[1][i + 1]);
+    mx = halves_max(mx) * c;
+    // lazy rescale: only when some row's max grew by more than kLazyRescale
+    if (__builtin_amdgcn_ballot_w64(mx > m_run + kLazyRescale) != 0) {
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = m_new == -INFINITY ? 1.f : fast_exp2(m_run - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt) o[dt] *= alpha;
+      m_run = m_new;
+    }
+  };
+
   const int64_t vis_lim = a.q_offset + qlast - a.kv_offset + 1;
   int t = -1, kb = 0, kend = 0, cend = 0;
   ring_next(a, CAUSAL, vis_lim, t, kb, kend, cend);
-
   typename Path::Stage st;
-  if (t < a.num_chunks) {
-    Path::load_tile(st, a, kbase, vbase, kb, tid);
-    Path::store_tile(st, (elem_t *)smem, tid);
-  }
-  // All prologue loads (Q included) have landed: without this the compiler keeps Q's
-  // loads "pending" on the no-tile path and the loop's first MFMAs would wait on the
-  // freshly issued prefetch as well (vmcnt counts in order).
-  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-  __syncthreads();
 
-  int cur = 0;
-  while (t < a.num_chunks) {
-    const int kb_cur = kb, cend_cur = cend;
-    ring_next(a, CAUSAL, vis_lim, t, kb, kend, cend);
-    const bool has_next = t < a.num_chunks;
-    if (has_next) Path::load_tile(st, a, kbase, vbase, kb, tid);
-
-    const elem_t *buf = (const elem_t *)(smem + cur * Path::BUF_BYTES);
-    const int64_t kpos0 = a.kv_offset + kb_cur;
-    const int kvalid = min(BN, cend_cur - kb_cur);  // keys of this tile inside the chunk
-    const bool skip = !wave_active || (CAUSAL && kpos0 > wpos_last);
-    if (!skip) {
-      f32x16 s[2];
-      Path::qk(s, qf, buf, lane);
-
-      const bool need_mask = (kvalid < BN) || (CAUSAL && kpos0 + kvalid - 1 > wpos_first);
-      if (need_mask) {
-        // keys kk < lim are visible to this lane's row
-        int64_t lim64 = kvalid;
-        if (CAUSAL) lim64 = min(lim64, qpos - kpos0 + 1);
-        const int lim = (int)max<int64_t>(lim64, 0) - 4 * h;
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int kk = 32 * mt + (i >> 2) * 8 + (i & 3);  // minus the 4h offset
-            s[mt][i] = kk < lim ? s[mt][i] : -INFINITY;
-          }
-      }
-      // tile row max (max3 tree), combined across the two halves
-      float mx = fmaxf(fmaxf(s[0][0], s[0][1]), s[0][2]);
-#pragma unroll
-      for (int i = 3; i < 15; i += 2) mx = fmaxf(fmaxf(mx, s[0][i]), s[0][i + 1]);
-      mx = fmaxf(mx, s[0][15]);
-#pragma unroll
-      for (int i = 0; i < 16; i += 2) mx = fmaxf(fmaxf(mx, s[1][i]), s[1][i + 1]);
-      mx = halves_max(mx) * c;
-
-      // lazy rescale: only when some row's max grew by more than kLazyRescale
-      if (__builtin_amdgcn_ballot_w64(mx > m_run + kLazyRescale) != 0) {
-        const float m_new = fmaxf(m_run, mx);
-        const float alpha = m_new == -INFINITY ? 1.f : fast_exp2(m_run - m_new);
-        l_run *= alpha;
-#pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt) o[dt] *= alpha;
-        m_run = m_new;
-      }
-      const float mneg = m_run == -INFINITY ? 0.f : -m_run;
-      typename Path::PFrag pf;
-      l_run += Path::exp_pack(s, c, mneg, pf);
-      Path::pv(o, pf, buf, lane);
+  if constexpr (!Path::kPipelined) {
+    // ---- double-buffered loop: load next tile | QK, softmax, PV of this tile | store.
+    if (t < a.num_chunks) {
+      Path::load_tile(st, a, kbase, vbase, kb, tid);
+      Path::store_tile(st, tile_buf(0), tid);
     }
-
-    if (has_next) Path::store_tile(st, (elem_t *)(smem + (cur ^ 1) * Path::BUF_BYTES), tid);
+    // All prologue loads (Q included) have landed: without this the compiler keeps Q's
+    // loads "pending" on the no-tile path and the loop's first MFMAs would wait on the
+    // freshly issued prefetch as well (vmcnt counts in order).
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
     __syncthreads();
-    cur ^= 1;
+    int cur = 0;
+    while (t < a.num_chunks) {
+      const int kb_cur = kb, cend_cur = cend;
+      ring_next(a, CAUSAL, vis_lim, t, kb, kend, cend);
+      const bool has_next = t < a.num_chunks;
+      if (has_next) Path::load_tile(st, a, kbase, vbase, kb, tid);
+      const elem_t *buf = tile_buf(cur);
+      if (!skips(kb_cur)) {
+        f32x16 s[2];
+        Path::qk(s, qf, buf, lane);
+        typename Path::VPre vp;
+        Path::pv_prefetch(vp, buf, lane);
+        mask_max_rescale(s, kb_cur, cend_cur);
+        const float mneg = m_run == -INFINITY ? 0.f : -m_run;
+        typename Path::PFrag pf;
+        l_run += Path::exp_pack(s, c, mneg, pf);
+        Path::pv(o, pf, vp, buf, lane);
+      }
+      if (has_next) Path::store_tile(st, tile_buf(cur ^ 1), tid);
+      __syncthreads();
+      cur ^= 1;
+    }
+  } else {
+    // ---- software-pipelined loop over a ring of three LDS tiles.  Iteration i holds
+    // tile i (scores already masked, max applied) and tile i+1 (resident in LDS):
+    //   issue global loads of tile i+2
+    //   QK(i+1) MFMAs  interleaved with  softmax(i) VALU;  then PV(i) MFMAs
+    //   store tile i+2 to LDS; barrier; mask + max + lazy rescale of tile i+1
+    const bool v0 = t < a.num_chunks;
+    const int kb0 = kb, ce0 = cend;
+    if (v0) {
+      Path::load_tile(st, a, kbase, vbase, kb0, tid);
+      Path::store_tile(st, tile_buf(0), tid);
+    }
+    ring_next(a, CAUSAL, vis_lim, t, kb, kend, cend);
+    bool vn = t < a.num_chunks;
+    int kbn = kb, cen = cend;
+    if (vn) {
+      Path::load_tile(st, a, kbase, vbase, kbn, tid);
+      Path::store_tile(st, tile_buf(1), tid);
+    }
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): Q and both tiles have landed
+    __syncthreads();
+
+    f32x16 sn[2];  // scores of the next tile to be exponentiated
+    if (v0 && !skips(kb0)) {
+      Path::qk(sn, qf, tile_buf(0), lane);
+      mask_max_rescale(sn, kb0, ce0);
+    }
+    float mneg = m_run == -INFINITY ? 0.f : -m_run;
+    bool vc = v0;
+    int kbc = kb0;
+    int bi = 0;  // LDS slot of the current tile
+    while (vc) {
+      ring_next(a, CAUSAL, vis_lim, t, kb, kend, cend);
+      const bool v2 = t < a.num_chunks;
+      if (v2) Path::load_tile(st, a, kbase, vbase, kb, tid);
+      const int bn_i = bi == 2 ? 0 : bi + 1;
+      const int b2_i = bn_i == 2 ? 0 : bn_i + 1;
+      const elem_t *bc = tile_buf(bi);
+      const elem_t *bnx = tile_buf(bn_i);
+      const bool skip_c = skips(kbc);
+      const bool skip_n = !vn || skips(kbn);
+      f32x16 sc[2] = {sn[0], sn[1]};
+      if (!skip_c) {
+        // One straight-line block (QK of the next slot runs even when that tile is
+        // skipped or absent: the slot holds in-bounds data and the scores are unused).
+        l_run += Path::fused_step(sn, qf, bnx, sc, c, mneg, o, bc, lane);
+      } else if (!skip_n) {
+        Path::qk(sn, qf, bnx, lane);
+      }
+      if (v2) Path::store_tile(st, tile_buf(b2_i), tid);
+      __syncthreads();
+      if (!skip_n) {
+        mask_max_rescale(sn, kbn, cen);
+        mneg = m_run == -INFINITY ? 0.f : -m_run;
+      }
+      vc = vn;
+      kbc = kbn;
+      vn = v2;
+      kbn = kb;
+      cen = cend;
+      bi = bn_i;
+    }
   }
 
   // Epilogue: o = O / l, lse = ln(sum) = (m + log2 l) * ln 2.
@@ -445,24 +614,24 @@ __global__ void __launch_bounds__(kThreads) attn_fwd_kernel(FwdArgs a) {
 }
 
 template <class Path, int D, bool CAUSAL>
-int launch_one(const FwdArgs &a, hipStream_t stream) {
+int launch_one(const FwdArgs &args, hipStream_t stream) {
+  FwdArgs a = args;
+  a.num_q_tiles = (a.Sq + 32 * Path::kWaves - 1) / (32 * Path::kWaves);
   const int64_t blocks = (int64_t)a.num_q_tiles * a.Hq * a.B;
   if (blocks <= 0) return RA_OK;
-  hipLaunchKernelGGL((attn_fwd_kernel<Path, D, CAUSAL>), dim3((unsigned)blocks), dim3(kThreads),
-                     0, stream, a);
+  hipLaunchKernelGGL((attn_fwd_kernel<Path, D, CAUSAL>), dim3((unsigned)blocks),
+                     dim3(Path::kThreads), 0, stream, a);
   return hipGetLastError() == hipSuccess ? RA_OK : RA_ERR_HIP;
 }
 
 }  // namespace
 
-int launch_attn_fwd(const FwdArgs &args, int dtype, int D, int causal, hipStream_t stream) {
-  FwdArgs a = args;
-  a.num_q_tiles = (a.Sq + BM - 1) / BM;
+int launch_attn_fwd(const FwdArgs &a, int dtype, int D, int causal, hipStream_t stream) {
   if (dtype == RA_BF16) {
-    if (D == 128) return causal ? launch_one<Bf16Path<128>, 128, true>(a, stream)
-                                : launch_one<Bf16Path<128>, 128, false>(a, stream);
-    if (D == 64) return causal ? launch_one<Bf16Path<64>, 64, true>(a, stream)
-                               : launch_one<Bf16Path<64>, 64, false>(a, stream);
+    if (D == 128) return causal ? launch_one<Bf16Path<128, kBf16Waves>, 128, true>(a, stream)
+                                : launch_one<Bf16Path<128, kBf16Waves>, 128, false>(a, stream);
+    if (D == 64) return causal ? launch_one<Bf16Path<64, kBf16Waves>, 64, true>(a, stream)
+                               : launch_one<Bf16Path<64, kBf16Waves>, 64, false>(a, stream);
   } else if (dtype == RA_F32) {
     if (D == 128) return causal ? launch_one<F32Path<128>, 128, true>(a, stream)
                                 : launch_one<F32Path<128>, 128, false>(a, stream);
