@@ -54,6 +54,15 @@ constexpr float kLazyRescale = 8.0f;  // log2 units
 #define RA_FWD_BF16_WAVES 8
 #endif
 constexpr int kBf16Waves = RA_FWD_BF16_WAVES;  // 8 measured faster than 2 x 4
+#ifndef RA_FWD_DIRECT
+#define RA_FWD_DIRECT 1
+#endif
+#ifndef RA_FWD_DMA_ASM
+#define RA_FWD_DMA_ASM 1
+#endif
+#ifndef RA_FWD_DMA_LATE
+#define RA_FWD_DMA_LATE 0
+#endif
 #ifndef RA_FWD_PIPELINE
 #define RA_FWD_PIPELINE 0
 #endif
@@ -263,6 +272,201 @@ struct Bf16Path {
       const int kstep = step / (D / 32), dt = step % (D / 32);
       o[dt] = mfma_bf16(as_bf16x8(vp.x[step % kDepth]), as_bf16x8(pf.x[kstep]), o[dt]);
       if (step + kDepth < NSTEP) vp.x[step % kDepth] = v_frag(buf, step + kDepth, r, h);
+    }
+  }
+};
+
+// ---------------------------------------------------------------------------------
+// bf16 direct path: K and V go straight from global memory into LDS
+// (global_load_lds_dwordx4: lane l's 16 bytes land at LDS base + 16*l), dense and
+// XOR-swizzled so that every MFMA operand read is bank-conflict free.  V stays
+// row-major; its transposed MFMA operand comes from ds_read_b64_tr_b16, which within
+// each 16-lane group hands lane 4a+b the b-th 16-bit element of the 8-byte pieces
+// addressed by lanes a, a+4, a+8, a+12.  No staging registers, no transpose ALU work
+// and no LDS store instructions.
+// ---------------------------------------------------------------------------------
+typedef __attribute__((address_space(3))) unsigned char lds_u8;
+typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+// 32-bit LDS offset of a __shared__ object (generic -> local address space).
+__device__ __forceinline__ uint32_t lds_offset(const void *p) {
+  return (uint32_t)(size_t)(const lds_u8 *)p;
+}
+__device__ __forceinline__ u32x4 lds_read_b128(uint32_t addr) {
+  return *(const lds_u32x4 *)(size_t)addr;
+}
+__device__ __forceinline__ s16x4 lds_read_tr16_b64(uint32_t addr) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(size_t)addr);
+}
+
+// One 16-byte-per-lane direct load from global memory into LDS: lane l's bytes land at
+// LDS offset lds + 16*l.  Issued through inline assembly so the compiler's wait analysis
+// does not see an LDS write in flight (it would otherwise drain every LDS read queue);
+// every consumer of the slot waits explicitly (vmcnt(0) + barrier) instead.  The loop
+// that uses it issues no other vector-memory operation.  M0 needs one wait state
+// before the load reads it.
+__device__ __forceinline__ void dma_b128(const void *tile_base, int lane_off, uint32_t lds) {
+  asm volatile(
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %0, %1"
+      :
+      : "v"(lane_off), "s"(tile_base), "s"(lds)
+      : "memory", "m0");
+}
+
+template <int D>
+struct Bf16DirectPath {
+  using elem_t = uint16_t;
+  static constexpr int kWaves = 8;
+  static constexpr int kThreads = 512;
+  static constexpr int RB = 2 * D;                 // row bytes
+  static constexpr int TILE_BYTES = BN * RB;       // one of K or V
+  static constexpr int BUF_BYTES = 2 * TILE_BYTES; // K then V
+  static constexpr int NBLK = TILE_BYTES / 1024;   // 1-KiB load blocks per tensor
+  static constexpr int BPW = NBLK / kWaves;        // blocks per wave per tensor
+  static constexpr int kDepth = 4;                 // K operand reads in flight
+  static constexpr int kVDepth = 2;                // V operand MFMAs in flight
+  static_assert(NBLK % kWaves == 0, "tile must split evenly over the waves");
+
+  // swizzles (16-byte chunk index within a row)
+  __device__ static int ksw(int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); }
+  __device__ static int vsw(int r) { return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1); }
+
+  struct QFrag { bf16x8 x[D / 16]; };
+  struct PFrag { u32x4 x[4]; };
+  struct Lane {
+    int k_goff[BPW], v_goff[BPW];  // byte offsets of this lane's 16 B in the tile (row 0 = kb)
+    int k_row[BPW], v_row[BPW];    // tile rows this lane loads (for the clamped tail)
+    int k_chunk[BPW], v_chunk[BPW];
+    uint32_t ka;                   // K operand read address (before the ks XOR), slot 0
+    uint32_t vb;                   // V operand read address (before the dt XOR), slot 0
+  };
+
+  __device__ static void setup(Lane &L, const FwdArgs &a, int tid, uint32_t smem_base) {
+    const int lane = tid & 63, wave = tid >> 6;
+#pragma unroll
+    for (int i = 0; i < BPW; ++i) {
+      const int blk = wave + kWaves * i;
+      const int byte = blk * 1024 + 16 * lane;
+      const int r = byte / RB, p = (byte % RB) / 16;
+      L.k_row[i] = r;
+      L.k_chunk[i] = p ^ ksw(r);
+      L.k_goff[i] = (int)(r * a.k_ss * 2) + 16 * L.k_chunk[i];
+      L.v_row[i] = r;
+      L.v_chunk[i] = p ^ vsw(r);
+      L.v_goff[i] = (int)(r * a.v_ss * 2) + 16 * L.v_chunk[i];
+    }
+    const int r = lane & 31, h = lane >> 5;
+    L.ka = smem_base + (uint32_t)(r * RB + 16 * (ksw(r) ^ h));
+    const int g = lane >> 4, ap = lane & 15, z = ap >> 2;
+    const int w = 2 * (g & 1) + ((ap & 3) >> 1);
+    const int zz = D == 128 ? z : (z >> 1);
+    L.vb = smem_base + TILE_BYTES +
+           (uint32_t)((4 * h + z) * RB + 64 * zz + 16 * w + 8 * (ap & 1));
+  }
+
+  __device__ static void load_q(QFrag &qf, const FwdArgs &a, const elem_t *qbase, int qrow, int h) {
+    const int row = min(qrow, a.Sq - 1);
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks)
+      qf.x[ks] = as_bf16x8(*(const u32x4 *)(qbase + (int64_t)row * a.q_ss + ks * 16 + 8 * h));
+  }
+
+  // Issue the direct loads of the tile starting at key kb into the LDS slot at byte
+  // offset `slot` (from the start of LDS).
+  __device__ static void load_tile(const Lane &L, const FwdArgs &a, const elem_t *kbase,
+                                   const elem_t *vbase, int kb, uint32_t slot, int wave) {
+    const bool tail = kb + BN > a.Skv;
+    const elem_t *kt = kbase + (int64_t)kb * a.k_ss;
+    const elem_t *vt = vbase + (int64_t)kb * a.v_ss;
+#pragma unroll
+    for (int i = 0; i < BPW; ++i) {
+      const uint32_t blk = (uint32_t)__builtin_amdgcn_readfirstlane(wave + kWaves * i);
+      int koff = L.k_goff[i], voff = L.v_goff[i];
+      if (tail) {  // rows past the end read the last row (their scores are masked)
+        const int kr = min(kb + L.k_row[i], a.Skv - 1) - kb;
+        const int vr = min(kb + L.v_row[i], a.Skv - 1) - kb;
+        koff = (int)(kr * a.k_ss * 2) + 16 * L.k_chunk[i];
+        voff = (int)(vr * a.v_ss * 2) + 16 * L.v_chunk[i];
+      }
+#if RA_FWD_DMA_ASM
+      dma_b128(kt, koff, slot + blk * 1024);
+      dma_b128(vt, voff, slot + TILE_BYTES + blk * 1024);
+#else
+      __builtin_amdgcn_global_load_lds((const void *)((const char *)kt + koff),
+                                       (lds_u8 *)(size_t)(slot + blk * 1024), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void *)((const char *)vt + voff),
+                                       (lds_u8 *)(size_t)(slot + TILE_BYTES + blk * 1024), 16, 0,
+                                       0);
+#endif
+    }
+  }
+
+  __device__ static u32x4 k_frag(uint32_t ka, int step) {
+    const int ks = step >> 1, mt = step & 1;
+    const uint32_t addr = (ka ^ (uint32_t)(32 * ks)) + (uint32_t)(mt * 32 * RB);
+    return lds_read_b128(addr);
+  }
+
+  // S^T[32 keys x 32 queries] for the two 32-key halves of the tile.
+  __device__ static void qk(f32x16 (&s)[2], const QFrag &qf, uint32_t ka) {
+    constexpr int NSTEP = 2 * (D / 16);
+    u32x4 kf[kDepth];
+#pragma unroll
+    for (int i = 0; i < kDepth; ++i) kf[i] = k_frag(ka, i);
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) s[mt] = f32x16{};
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int step = 0; step < NSTEP; ++step) {
+      const int ks = step >> 1, mt = step & 1;
+      s[mt] = mfma_bf16(as_bf16x8(kf[step % kDepth]), qf.x[ks], s[mt]);
+      if (step + kDepth < NSTEP) kf[step % kDepth] = k_frag(ka, step + kDepth);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+
+  __device__ static float exp_pack(const f32x16 (&s)[2], float c, float mneg, PFrag &pf) {
+    float acc0 = 0.f, acc1 = 0.f;
+#pragma unroll
+    for (int kstep = 0; kstep < 4; ++kstep) {
+      const int mt = kstep >> 1, s2 = kstep & 1;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const float p0 = fast_exp2(fmaf(s[mt][8 * s2 + 2 * w], c, mneg));
+        const float p1 = fast_exp2(fmaf(s[mt][8 * s2 + 2 * w + 1], c, mneg));
+        const bf16x2 pk = __builtin_convertvector((f32x2){p0, p1}, bf16x2);
+        pf.x[kstep][w] = __builtin_bit_cast(uint32_t, pk);
+        acc0 += p0;
+        acc1 += p1;
+      }
+    }
+    return acc0 + acc1;
+  }
+
+  // V^T operand for PV step (kstep, dt): two transposing 8-byte reads (keys
+  // 16*kstep + 4h + 0..3 and + 8), matching the k order of the P^T registers.
+  __device__ static u32x4 v_frag(uint32_t vb, int step) {
+    const int kstep = step / (D / 32), dt = step % (D / 32);
+    const uint32_t base = (vb ^ (uint32_t)(64 * dt)) + (uint32_t)(16 * kstep * RB);
+    const s16x4 lo = lds_read_tr16_b64(base);
+    const s16x4 hi = lds_read_tr16_b64(base + 8 * RB);
+    u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+    return u32x4{l2[0], l2[1], h2[0], h2[1]};
+  }
+
+  __device__ static void pv(f32x16 (&o)[D / 32], const PFrag &pf, uint32_t vb) {
+    constexpr int NSTEP = 4 * (D / 32);
+    u32x4 vf[kVDepth];
+#pragma unroll
+    for (int i = 0; i < kVDepth; ++i) vf[i] = v_frag(vb, i);
+#pragma unroll
+    for (int step = 0; step < NSTEP; ++step) {
+      const int kstep = step / (D / 32), dt = step % (D / 32);
+      o[dt] = mfma_bf16(as_bf16x8(vf[step % kVDepth]), as_bf16x8(pf.x[kstep]), o[dt]);
+      if (step + kVDepth < NSTEP) vf[step % kVDepth] = v_frag(vb, step + kVDepth);
     }
   }
 };
@@ -613,6 +817,165 @@ attn_fwd_kernel(FwdArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------------
+// Kernel for the bf16 direct path: double-buffered LDS, the next tile's direct loads in
+// flight under the current tile's math.
+// ---------------------------------------------------------------------------------
+template <int D, bool CAUSAL>
+__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+attn_fwd_direct_kernel(FwdArgs a) {
+  using Path = Bf16DirectPath<D>;
+  using elem_t = uint16_t;
+  constexpr int BM = 32 * Path::kWaves;
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * Path::BUF_BYTES];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int r32 = lane & 31;
+  const int h = lane >> 5;
+
+  const int HB = a.Hq * a.B;
+  const int bid = blockIdx.x;
+  const int trank = bid / HB;
+  int j = bid - trank * HB;
+  if ((HB & 7) == 0) j = (j & 7) * (HB >> 3) + (j >> 3);
+  const int hq = j % a.Hq;
+  const int b = j / a.Hq;
+  const int qt = a.num_q_tiles - 1 - trank;
+  const int hk = hq / a.group;
+
+  const int q0 = qt * BM;
+  const int qlast = min(q0 + BM, a.Sq) - 1;
+  const elem_t *qbase = (const elem_t *)a.q + b * a.q_sb + hq * a.q_sh;
+  const elem_t *kbase = (const elem_t *)a.k + b * a.k_sb + hk * a.k_sh;
+  const elem_t *vbase = (const elem_t *)a.v + b * a.v_sb + hk * a.v_sh;
+
+  const int qrow = q0 + 32 * wave + r32;
+  const int64_t qpos = a.q_offset + qrow;
+  const int64_t wpos_first = a.q_offset + q0 + 32 * wave;
+  const int64_t wpos_last = wpos_first + 31;
+  const bool wave_active = (q0 + 32 * wave) < a.Sq;
+  const float c = a.scale_log2;
+
+  typename Path::Lane L;
+  Path::setup(L, a, tid, lds_offset(smem));
+  typename Path::QFrag qf;
+  Path::load_q(qf, a, qbase, qrow, h);
+
+  f32x16 o[D / 32];
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt) o[dt] = f32x16{};
+  float m_run = -INFINITY;
+  float l_run = 0.f;
+
+  const int64_t vis_lim = a.q_offset + qlast - a.kv_offset + 1;
+  int t = -1, kb = 0, kend = 0, cend = 0;
+  ring_next(a, CAUSAL, vis_lim, t, kb, kend, cend);
+  const uint32_t smem0 = lds_offset(smem);
+  if (t < a.num_chunks) Path::load_tile(L, a, kbase, vbase, kb, smem0, wave);
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): Q and the first tile have landed
+  __syncthreads();
+
+  int cur = 0;
+  while (t < a.num_chunks) {
+    const int kb_cur = kb, cend_cur = cend;
+    ring_next(a, CAUSAL, vis_lim, t, kb, kend, cend);
+    const bool has_next = t < a.num_chunks;
+#if !RA_FWD_DMA_LATE
+    if (has_next)
+      Path::load_tile(L, a, kbase, vbase, kb, smem0 + (cur ^ 1) * Path::BUF_BYTES, wave);
+#endif
+
+    const int64_t kpos0 = a.kv_offset + kb_cur;
+    if (wave_active && !(CAUSAL && kpos0 > wpos_last)) {
+      const uint32_t slot = (uint32_t)(cur * Path::BUF_BYTES);
+      f32x16 s[2];
+      Path::qk(s, qf, L.ka + slot);
+      const int kvalid = min(BN, cend_cur - kb_cur);
+      const bool need_mask = (kvalid < BN) || (CAUSAL && kpos0 + kvalid - 1 > wpos_first);
+      if (need_mask) {
+        int lim = kvalid;  // keys kk < lim are visible to this lane's row
+        if (CAUSAL) {
+          const int64_t vis = qpos - kpos0 + 1;
+          lim = vis < (int64_t)lim ? (vis > 0 ? (int)vis : 0) : lim;
+        }
+        lim -= 4 * h;
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int kk = 32 * mt + (i >> 2) * 8 + (i & 3);
+            s[mt][i] = kk < lim ? s[mt][i] : -INFINITY;
+          }
+      }
+      float mx = fmaxf(fmaxf(s[0][0], s[0][1]), s[0][2]);
+#pragma unroll
+      for (int i = 3; i < 15; i += 2) mx = fmaxf(fmaxf(mx, s[0][i]), s[0][i + 1]);
+      mx = fmaxf(mx, s[0][15]);
+#pragma unroll
+      for (int i = 0; i < 16; i += 2) mx = fmaxf(fmaxf(mx, s[1][i]), s[1][i + 1]);
+      mx = halves_max(mx) * c;
+      if (__builtin_amdgcn_ballot_w64(mx > m_run + kLazyRescale) != 0) {
+        const float m_new = fmaxf(m_run, mx);
+        const float alpha = m_new == -INFINITY ? 1.f : fast_exp2(m_run - m_new);
+        l_run *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt) o[dt] *= alpha;
+        m_run = m_new;
+      }
+      const float mneg = m_run == -INFINITY ? 0.f : -m_run;
+      typename Path::PFrag pf;
+      l_run += Path::exp_pack(s, c, mneg, pf);
+      Path::pv(o, pf, L.vb + slot);
+    }
+#if RA_FWD_DMA_LATE
+    if (has_next)
+      Path::load_tile(L, a, kbase, vbase, kb, smem0 + (cur ^ 1) * Path::BUF_BYTES, wave);
+#endif
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the next tile's direct loads landed
+    __syncthreads();
+    cur ^= 1;
+  }
+
+  const float l_tot = halves_sum(l_run);
+  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  if (qrow < a.Sq) {
+    if (h == 0) {
+      const float lse = l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
+      a.lse[b * a.l_sb + hq * a.l_sh + qrow] = lse;
+    }
+    const int64_t orow = b * a.o_sb + hq * a.o_sh + (int64_t)qrow * a.o_ss;
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d = 32 * dt + 8 * g + 4 * h;
+        const float x0 = o[dt][4 * g + 0] * inv, x1 = o[dt][4 * g + 1] * inv;
+        const float x2 = o[dt][4 * g + 2] * inv, x3 = o[dt][4 * g + 3] * inv;
+        if (a.o_is_f32) {
+          *(float4 *)((float *)a.o + orow + d) = float4{x0, x1, x2, x3};
+        } else {
+          const bf16x2 lo = __builtin_convertvector((f32x2){x0, x1}, bf16x2);
+          const bf16x2 hi = __builtin_convertvector((f32x2){x2, x3}, bf16x2);
+          *(u32x2 *)((uint16_t *)a.o + orow + d) =
+              u32x2{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
+        }
+      }
+  }
+}
+
+template <int D, bool CAUSAL>
+int launch_direct(const FwdArgs &args, hipStream_t stream) {
+  FwdArgs a = args;
+  a.num_q_tiles = (a.Sq + 255) / 256;
+  const int64_t blocks = (int64_t)a.num_q_tiles * a.Hq * a.B;
+  if (blocks <= 0) return RA_OK;
+  hipLaunchKernelGGL((attn_fwd_direct_kernel<D, CAUSAL>), dim3((unsigned)blocks), dim3(512), 0,
+                     stream, a);
+  return hipGetLastError() == hipSuccess ? RA_OK : RA_ERR_HIP;
+}
+
 template <class Path, int D, bool CAUSAL>
 int launch_one(const FwdArgs &args, hipStream_t stream) {
   FwdArgs a = args;
@@ -627,6 +990,10 @@ int launch_one(const FwdArgs &args, hipStream_t stream) {
 }  // namespace
 
 int launch_attn_fwd(const FwdArgs &a, int dtype, int D, int causal, hipStream_t stream) {
+  if (dtype == RA_BF16 && RA_FWD_DIRECT) {
+    if (D == 128) return causal ? launch_direct<128, true>(a, stream) : launch_direct<128, false>(a, stream);
+    if (D == 64) return causal ? launch_direct<64, true>(a, stream) : launch_direct<64, false>(a, stream);
+  }
   if (dtype == RA_BF16) {
     if (D == 128) return causal ? launch_one<Bf16Path<128, kBf16Waves>, 128, true>(a, stream)
                                 : launch_one<Bf16Path<128, kBf16Waves>, 128, false>(a, stream);
