@@ -1,14 +1,540 @@
-// attn_bwd -- gradients of exact softmax attention, recomputing P from the saved lse.
+// attn_bwd -- gradients of exact softmax attention, recomputing the attention weights
+// from the forward's saved log-sum-exp instead of storing them.
+//
+// Sources (page title, host):
+//   [P4] "ms-swift集成FlashAttention 2/3，长文本训练更高效" (maplevalley.com.cn), section
+//        "为什么传统注意力这么“吃”显存？": the backward pass needs the attention
+//        intermediates, kept or recomputed; here they are recomputed tile by tile.
+//   [P1] "ms-swift支持Ulysses与Ring-Attention降低长文本显存占用" (bjdmk.com.cn), section
+//        "Ring-Attention：面向大规模部署的工程利器": gradients travel back along the ring.
+// The gradient formulas are the textbook ones (not on the pages), for L = sum(dO * O):
+//   P = exp(scale q.k - lse),  D_i = rowsum(dO * O),  dV = P^T dO,  dP = dO V^T,
+//   dS = P * (dP - D),  dQ = scale dS K,  dK = scale dS^T Q.
+//
+// Three kernels, no atomics (bitwise deterministic):
+//   * bwd_delta  -- D_i = sum_d dO_id O_id (fp32), a streaming pass;
+//   * bwd_dq     -- one workgroup per 256 query rows (8 waves x 32); K/V tiles of 64 keys
+//                   stream through LDS in ring order; per tile: S^T = K Q^T and
+//                   dP^T = V dO^T (Q, dO in registers), P and dS in registers, then
+//                   dQ^T += K^T dS^T with K^T read transposed from the same LDS tile;
+//   * bwd_dkdv   -- one workgroup per 128 keys (4 waves x 32) of one key/value head;
+//                   loops over 64-row query tiles of every query head of the group,
+//                   Q and dO tiles in LDS: S = Q K^T, dP = dO V^T (K^T, V^T in registers),
+//                   dV^T += dO^T P and dK^T += Q^T dS with dO^T, Q^T read transposed.
+// Tiles move global -> LDS with direct loads and a swizzle that keeps both row-wise
+// (ds_read_b128) and transposed (ds_read_b64_tr_b16) operand reads conflict-free.
+#include <math.h>
+
 #include "common.h"
 #include "internal.h"
 
 namespace ra {
+namespace {
+
+constexpr int TN = 64;  // rows per LDS tile (keys in bwd_dq, queries in bwd_dkdv)
+
+// 16-byte-chunk swizzle of a tile row: for 16 consecutive rows at one chunk the physical
+// chunks differ (row-wise reads), and for 4 consecutive rows at 4 consecutive chunks
+// they fall in different 64-byte segments (transposed reads).
+template <int D>
+__device__ __forceinline__ int usw(int r) {
+  if (D == 128) return (r & 15) ^ ((r & 3) << 2);
+  return ((r >> 1) & 7) ^ (((r >> 1) & 1) << 2);
+}
+
+// A TN x D bf16 tile in LDS (dense, swizzled), loaded with direct loads.
+template <int D, int NW>
+struct STile {
+  static constexpr int RB = 2 * D;
+  static constexpr int BYTES = TN * RB;
+  static constexpr int NBLK = BYTES / 1024;
+  static constexpr int BPW = NBLK / NW;  // 1-KiB blocks per wave
+  static_assert(NBLK % NW == 0, "tile must split evenly over the waves");
+
+  struct Lane {
+    int row[BPW], chunk[BPW];
+  };
+  __device__ static void setup(Lane &L, int lane, int wave) {
+#pragma unroll
+    for (int i = 0; i < BPW; ++i) {
+      const int byte = (wave + NW * i) * 1024 + 16 * lane;
+      const int r = byte / RB, p = (byte % RB) / 16;
+      L.row[i] = r;
+      L.chunk[i] = p ^ usw<D>(r);
+    }
+  }
+  // rows row0 .. row0+TN-1 of a [rows, D] matrix with row stride `ss` elements; rows
+  // at or past `nrows` read row nrows-1 instead (callers mask them).
+  __device__ static void load(const Lane &L, const uint16_t *base, int64_t ss, int row0,
+                              int nrows, uint32_t lds, int wave) {
+    const uint16_t *tb = base + (int64_t)row0 * ss;
+#pragma unroll
+    for (int i = 0; i < BPW; ++i) {
+      const int r = min(row0 + L.row[i], nrows - 1) - row0;
+      const int off = (int)(r * ss * 2) + 16 * L.chunk[i];
+      const uint32_t blk = (uint32_t)__builtin_amdgcn_readfirstlane(wave + NW * i);
+      dma_b128(tb, off, lds + blk * 1024);
+    }
+  }
+  // Row-wise MFMA operand: 8 consecutive bf16 (chunk 2*ks + h) of row r.  Returns the
+  // lane part; the read address is (part ^ 32*ks) + tile base (+ 32*RB per 32-row step).
+  __device__ static uint32_t row_part(int r, int h) {
+    return (uint32_t)(r * RB + 16 * (usw<D>(r) ^ h));
+  }
+  __device__ static u32x4 row_read(uint32_t base, uint32_t part, int ks) {
+    return lds_read_b128(base + (part ^ (uint32_t)(32 * ks)));
+  }
+  // Transposed MFMA operand (M = head dim, K = tile rows): for rows r0 + 4h + (0..3)
+  // and r0 + 8 + 4h + (0..3) and head dims 32*dt + (lane & 31).  lane_part(s) is the
+  // per-lane address of sub-read s; the dt selection is an XOR by 64*dt.
+  __device__ static uint32_t tr_part(int lane, int s) {
+    const int h = lane >> 5, g = lane >> 4, ap = lane & 15, z = ap >> 2;
+    const int w = 2 * (g & 1) + ((ap & 3) >> 1);
+    const int r = 8 * s + 4 * h + z;  // row within a 16-row step
+    const int f = usw<D>(r);
+    // physical chunk = (4*dt + w) ^ f ; keep the dt part out (XORed per read)
+    const int chunk_nodt = w ^ f;
+    return (uint32_t)(r * RB + 16 * chunk_nodt + 8 * (ap & 1));
+  }
+  __device__ static u32x4 tr_read(uint32_t base, uint32_t part0, uint32_t part1, int r0, int dt) {
+    const uint32_t x = (uint32_t)(64 * dt);
+    const s16x4 lo = lds_read_tr16_b64(base + (uint32_t)(r0 * RB) + (part0 ^ x));
+    const s16x4 hi = lds_read_tr16_b64(base + (uint32_t)(r0 * RB) + (part1 ^ x));
+    const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+    return u32x4{l2[0], l2[1], h2[0], h2[1]};
+  }
+};
+
+// ---------------------------------------------------------------------------------
+// D_i = sum_d dO_id * O_id  (one 64-lane wave per row group; D <= 128)
+// ---------------------------------------------------------------------------------
+template <int D>
+__global__ void __launch_bounds__(256) bwd_delta_kernel(BwdArgs a) {
+  constexpr int LPR = D / 8;  // lanes per row (8 bf16 each)
+  const int64_t nrows = (int64_t)a.B * a.Hq * a.Sq;
+  const int sub = threadIdx.x % LPR;
+  for (int64_t row = ((int64_t)blockIdx.x * 256 + threadIdx.x) / LPR; row < nrows;
+       row += (int64_t)gridDim.x * (256 / LPR)) {
+    const int s = (int)(row % a.Sq);
+    const int64_t bh = row / a.Sq;
+    const int hh = (int)(bh % a.Hq), b = (int)(bh / a.Hq);
+    const u32x4 x = *(const u32x4 *)((const uint16_t *)a.o + b * a.o_sb + hh * a.o_sh +
+                                       (int64_t)s * a.o_ss + 8 * sub);
+    const u32x4 y = *(const u32x4 *)((const uint16_t *)a.dout + b * a.do_sb + hh * a.do_sh +
+                                       (int64_t)s * a.do_ss + 8 * sub);
+    float acc = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      acc = fmaf(bf16_bits_to_float(x[w] & 0xffffu), bf16_bits_to_float(y[w] & 0xffffu), acc);
+      acc = fmaf(bf16_bits_to_float(x[w] >> 16), bf16_bits_to_float(y[w] >> 16), acc);
+    }
+#pragma unroll
+    for (int off = LPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, LPR);
+    if (sub == 0) a.delta[row] = acc;
+  }
+}
+
+// Next key tile in ring order (as in the forward).  t == P means done.
+__device__ __forceinline__ void ring_next_bwd(const BwdArgs &a, bool causal, int64_t vis_lim,
+                                              int &t, int &kb, int &kend, int &cend) {
+  kb += TN;
+  while (kb >= kend) {
+    ++t;
+    if (t >= a.num_chunks) return;
+    int c = a.start_chunk + t;
+    if (c >= a.num_chunks) c -= a.num_chunks;
+    kb = c * a.chunk_len;
+    cend = kb + a.chunk_len;
+    kend = cend;
+    if (causal && vis_lim < (int64_t)kend) kend = vis_lim > kb ? (int)vis_lim : kb;
+  }
+}
+
+// ---------------------------------------------------------------------------------
+// dQ: 8 waves x 32 query rows.  Per key tile (64 keys, two 32-key halves mt):
+//   S^T_mt = K_mt Q^T, dP^T_mt = V_mt dO^T         (16 + 16 MFMAs over the tile)
+//   P^T = exp2(c S^T - log2e lse), dS^T = P^T (dP^T - D)  -> bf16
+//   dQ^T += K^T_mt dS^T_mt                          (16 MFMAs over the tile)
+// ---------------------------------------------------------------------------------
+template <int D, bool CAUSAL>
+__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+bwd_dq_kernel(BwdArgs a, int num_q_tiles) {
+  constexpr int NW = 8, BM = 32 * NW;
+  using Tile = STile<D, NW>;
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * 2 * Tile::BYTES];
+  const uint32_t smem0 = lds_offset(smem);
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int r32 = lane & 31, h = lane >> 5;
+  const int HB = a.Hq * a.B;
+  const int bid = blockIdx.x;
+  const int trank = bid / HB;
+  int j = bid - trank * HB;
+  if ((HB & 7) == 0) j = (j & 7) * (HB >> 3) + (j >> 3);
+  const int hq = j % a.Hq, b = j / a.Hq, hk = hq / a.group;
+  const int qt = num_q_tiles - 1 - trank;
+  const int q0 = qt * BM;
+  const int qlast = min(q0 + BM, a.Sq) - 1;
+  const int qrow = q0 + 32 * wave + r32;
+  const int qr = min(qrow, a.Sq - 1);
+  const int64_t qpos = a.q_offset + qrow;
+  const int64_t wpos_first = a.q_offset + q0 + 32 * wave;
+  const int64_t wpos_last = wpos_first + 31;
+  const bool wave_active = (q0 + 32 * wave) < a.Sq;
+  const float c = a.scale_log2;
+
+  const uint16_t *qb = (const uint16_t *)a.q + b * a.q_sb + hq * a.q_sh;
+  const uint16_t *dob = (const uint16_t *)a.dout + b * a.do_sb + hq * a.do_sh;
+  const uint16_t *kbase = (const uint16_t *)a.k + b * a.k_sb + hk * a.k_sh;
+  const uint16_t *vbase = (const uint16_t *)a.v + b * a.v_sb + hk * a.v_sh;
+
+  // Q and dO as B operands (k = head dim 16*ks + 8h .. +8), one row per lane.
+  bf16x8 qf[D / 16], df[D / 16];
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) {
+    qf[ks] = as_bf16x8(*(const u32x4 *)(qb + (int64_t)qr * a.q_ss + 16 * ks + 8 * h));
+    df[ks] = as_bf16x8(*(const u32x4 *)(dob + (int64_t)qr * a.do_ss + 16 * ks + 8 * h));
+  }
+  const float lse = a.lse[b * a.l_sb + hq * a.l_sh + qr];
+  // exp2 argument offset; an empty row (lse = -inf) gets +inf so every P is 0
+  const float lse2 = lse == -INFINITY ? INFINITY : lse * kLog2e;
+  const float dlt = a.delta[((int64_t)b * a.Hq + hq) * a.Sq + qr];
+
+  f32x16 dq[D / 32];
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt) dq[dt] = f32x16{};
+
+  typename Tile::Lane TL;
+  Tile::setup(TL, lane, wave);
+  const uint32_t kpart = Tile::row_part(r32, h);  // rows r32 (+32 per mt)
+  const uint32_t tp0 = Tile::tr_part(lane, 0), tp1 = Tile::tr_part(lane, 1);
+
+  const int64_t vis_lim = a.q_offset + qlast - a.kv_offset + 1;
+  int t = -1, kb = 0, kend = 0, cend = 0;
+  ring_next_bwd(a, CAUSAL, vis_lim, t, kb, kend, cend);
+  if (t < a.num_chunks) {
+    Tile::load(TL, kbase, a.k_ss, kb, a.Skv, smem0, wave);
+    Tile::load(TL, vbase, a.v_ss, kb, a.Skv, smem0 + Tile::BYTES, wave);
+  }
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+  __syncthreads();
+
+  int cur = 0;
+  while (t < a.num_chunks) {
+    const int kb_cur = kb, cend_cur = cend;
+    ring_next_bwd(a, CAUSAL, vis_lim, t, kb, kend, cend);
+    if (t < a.num_chunks) {
+      const uint32_t nx = smem0 + (cur ^ 1) * 2 * Tile::BYTES;
+      Tile::load(TL, kbase, a.k_ss, kb, a.Skv, nx, wave);
+      Tile::load(TL, vbase, a.v_ss, kb, a.Skv, nx + Tile::BYTES, wave);
+    }
+    const int64_t kpos0 = a.kv_offset + kb_cur;
+    if (wave_active && !(CAUSAL && kpos0 > wpos_last)) {
+      const uint32_t kt = smem0 + cur * 2 * Tile::BYTES, vt = kt + Tile::BYTES;
+      const int kvalid = min(TN, cend_cur - kb_cur);
+      const bool need_mask = (kvalid < TN) || (CAUSAL && kpos0 + kvalid - 1 > wpos_first);
+      int lim = kvalid;
+      if (CAUSAL) {
+        const int64_t vis = qpos - kpos0 + 1;
+        lim = vis < (int64_t)lim ? (vis > 0 ? (int)vis : 0) : lim;
+      }
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) {
+        f32x16 s = f32x16{}, dp = f32x16{};
+        const uint32_t ko = kt + (uint32_t)(mt * 32 * Tile::RB);
+        const uint32_t vo = vt + (uint32_t)(mt * 32 * Tile::RB);
+#pragma unroll
+        for (int ks = 0; ks < D / 16; ++ks) {
+          s = mfma_bf16(as_bf16x8(Tile::row_read(ko, kpart, ks)), qf[ks], s);
+          dp = mfma_bf16(as_bf16x8(Tile::row_read(vo, kpart, ks)), df[ks], dp);
+        }
+        // P^T and dS^T (lane: one query row, 16 of the 32 keys of this half)
+        u32x4 dsf[2];
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            float d2[2];
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+              const int i = 8 * s2 + 2 * w + e;
+              const int kk = 32 * mt + (i >> 2) * 8 + 4 * h + (i & 3);
+              float p = fast_exp2(fmaf(s[i], c, -lse2));
+              if (need_mask && kk >= lim) p = 0.f;
+              d2[e] = p * (dp[i] - dlt);
+            }
+            const bf16x2 pk = __builtin_convertvector((f32x2){d2[0], d2[1]}, bf16x2);
+            dsf[s2][w] = __builtin_bit_cast(uint32_t, pk);
+          }
+        // dQ^T[D x 32 q] += K^T[D x 32 keys] dS^T[32 keys x 32 q]
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+          for (int dt = 0; dt < D / 32; ++dt) {
+            const u32x4 kf = Tile::tr_read(kt, tp0, tp1, 32 * mt + 16 * s2, dt);
+            dq[dt] = mfma_bf16(as_bf16x8(kf), as_bf16x8(dsf[s2]), dq[dt]);
+          }
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): next tile landed
+    __syncthreads();
+    cur ^= 1;
+  }
+
+  if (qrow < a.Sq) {
+    const int64_t orow = b * a.dq_sb + hq * a.dq_sh + (int64_t)qrow * a.dq_ss;
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d = 32 * dt + 8 * g + 4 * h;
+        const bf16x2 lo = __builtin_convertvector(
+            (f32x2){dq[dt][4 * g] * a.scale, dq[dt][4 * g + 1] * a.scale}, bf16x2);
+        const bf16x2 hi = __builtin_convertvector(
+            (f32x2){dq[dt][4 * g + 2] * a.scale, dq[dt][4 * g + 3] * a.scale}, bf16x2);
+        *(u32x2 *)((uint16_t *)a.dq + orow + d) =
+            u32x2{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------------
+// dK, dV: 4 waves x 32 keys.  Per query tile (64 rows, two 32-row steps qs), for each
+// query head of the group:
+//   S = Q K^T, dP = dO V^T                 (A: Q / dO rows from LDS, B: K^T / V^T regs)
+//   P = exp2(c S - log2e lse), dS = P (dP - D)
+//   dV^T += dO^T P, dK^T += Q^T dS          (A: transposed reads of dO / Q)
+// ---------------------------------------------------------------------------------
+template <int D, bool CAUSAL>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+bwd_dkdv_kernel(BwdArgs a, int num_kv_tiles) {
+  constexpr int NW = 4, BK = 32 * NW;
+  using Tile = STile<D, NW>;
+  // per slot: Q tile, dO tile, lse2[TN], delta[TN]
+  constexpr int SLOT = 2 * Tile::BYTES + 2 * TN * 4;
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * SLOT];
+  const uint32_t smem0 = lds_offset(smem);
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int r32 = lane & 31, h = lane >> 5;
+  const int HB = a.Hkv * a.B;
+  const int bid = blockIdx.x;
+  const int kt_i = bid / HB;  // ascending key tiles: lowest keys see the most queries
+  int j = bid - kt_i * HB;
+  if ((HB & 7) == 0) j = (j & 7) * (HB >> 3) + (j >> 3);
+  const int hk = j % a.Hkv, b = j / a.Hkv;
+  const int k0 = kt_i * BK;
+  const int krow = k0 + 32 * wave + r32;  // this lane's key (column of S)
+  const int kr = min(krow, a.Skv - 1);
+  const int64_t kpos = a.kv_offset + krow;
+  const int64_t wk_first = a.kv_offset + k0 + 32 * wave;
+  const int64_t wk_last = wk_first + 31;
+  const bool wave_active = (k0 + 32 * wave) < a.Skv;
+  const float c = a.scale_log2;
+
+  const uint16_t *kb_ = (const uint16_t *)a.k + b * a.k_sb + hk * a.k_sh;
+  const uint16_t *vb_ = (const uint16_t *)a.v + b * a.v_sb + hk * a.v_sh;
+  // K^T and V^T as B operands: column = key, k = head dim 16*ks + 8h .. +8
+  bf16x8 kf[D / 16], vf[D / 16];
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) {
+    kf[ks] = as_bf16x8(*(const u32x4 *)(kb_ + (int64_t)kr * a.k_ss + 16 * ks + 8 * h));
+    vf[ks] = as_bf16x8(*(const u32x4 *)(vb_ + (int64_t)kr * a.v_ss + 16 * ks + 8 * h));
+  }
+
+  f32x16 dk[D / 32], dv[D / 32];
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt) {
+    dk[dt] = f32x16{};
+    dv[dt] = f32x16{};
+  }
+
+  typename Tile::Lane TL;
+  Tile::setup(TL, lane, wave);
+  const uint32_t qpart = Tile::row_part(r32, h);
+  const uint32_t tp0 = Tile::tr_part(lane, 0), tp1 = Tile::tr_part(lane, 1);
+
+  // First query row that can see this workgroup's first key (causal), as a tile start.
+  int qstart = 0;
+  if (CAUSAL) {
+    const int64_t first = a.kv_offset + k0 - a.q_offset;
+    qstart = first <= 0 ? 0 : (first >= (int64_t)a.Sq ? a.Sq : (int)first);
+    qstart = (qstart / TN) * TN;
+  }
+  const int nqt = qstart >= a.Sq ? 0 : (a.Sq - qstart + TN - 1) / TN;
+  const int total = nqt * a.group;  // (query head, query tile) pairs
+
+  auto issue = [&](int it, uint32_t slot) {
+    const int hq = hk * a.group + it / nqt;
+    const int q0 = qstart + (it % nqt) * TN;
+    const uint16_t *qb = (const uint16_t *)a.q + b * a.q_sb + hq * a.q_sh;
+    const uint16_t *dob = (const uint16_t *)a.dout + b * a.do_sb + hq * a.do_sh;
+    Tile::load(TL, qb, a.q_ss, q0, a.Sq, slot, wave);
+    Tile::load(TL, dob, a.do_ss, q0, a.Sq, slot + Tile::BYTES, wave);
+  };
+  // lse (as exp2 offsets) and delta of the tile's 64 rows: 32 threads of wave 0
+  auto stats = [&](int it, float &val) {
+    const int hq = hk * a.group + it / nqt;
+    const int q0 = qstart + (it % nqt) * TN;
+    const int i = tid & 63;
+    const int q = min(q0 + i, a.Sq - 1);
+    if (tid < 64) {
+      const float l = a.lse[b * a.l_sb + hq * a.l_sh + q];
+      val = l == -INFINITY ? INFINITY : l * kLog2e;
+    } else if (tid < 128) {
+      val = a.delta[((int64_t)b * a.Hq + hq) * a.Sq + q];
+    }
+  };
+  auto stats_store = [&](float val, uint32_t slot) {
+    if (tid < 128) {
+      const uint32_t at = slot + 2 * Tile::BYTES + (uint32_t)(4 * tid);
+      *(__attribute__((address_space(3))) float *)(size_t)at = val;
+    }
+  };
+
+  float sv = 0.f;
+  if (total > 0) {
+    issue(0, smem0);
+    stats(0, sv);
+    stats_store(sv, smem0);
+  }
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+  __syncthreads();
+
+  int cur = 0;
+  for (int it = 0; it < total; ++it) {
+    const uint32_t slot = smem0 + cur * SLOT;
+    const bool has_next = it + 1 < total;
+    if (has_next) {
+      issue(it + 1, smem0 + (cur ^ 1) * SLOT);
+      stats(it + 1, sv);
+    }
+    const int q0 = qstart + (it % nqt) * TN;
+    const int64_t qpos0 = a.q_offset + q0;
+#pragma unroll
+    for (int qs = 0; qs < 2; ++qs) {
+      const int64_t sfirst = qpos0 + 32 * qs, slast = sfirst + 31;  // query positions
+      const int qvalid = min(32, a.Sq - (q0 + 32 * qs));
+      if (!wave_active || qvalid <= 0 || (CAUSAL && wk_first > slast)) continue;
+      const bool need_mask = qvalid < 32 || (CAUSAL && wk_last > sfirst);
+      const uint32_t qo = slot + (uint32_t)(32 * qs * Tile::RB);
+      const uint32_t oo = qo + Tile::BYTES;
+      f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+      for (int ks = 0; ks < D / 16; ++ks) {
+        s = mfma_bf16(as_bf16x8(Tile::row_read(qo, qpart, ks)), kf[ks], s);
+        dp = mfma_bf16(as_bf16x8(Tile::row_read(oo, qpart, ks)), vf[ks], dp);
+      }
+      // lane: key column r32; element i is query row (i/4)*8 + 4h + i%4 of this step
+      const uint32_t st = slot + 2 * Tile::BYTES + (uint32_t)(4 * 32 * qs);
+      u32x4 pf[2], dsf[2];
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const f32x4 l4 = *(const __attribute__((address_space(3))) f32x4 *)(size_t)(
+            st + (uint32_t)(4 * (8 * g + 4 * h)));
+        const f32x4 d4 = *(const __attribute__((address_space(3))) f32x4 *)(size_t)(
+            st + (uint32_t)(4 * TN + 4 * (8 * g + 4 * h)));
+        float pv[4], dv4[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int i = 4 * g + e;
+          const int qi = (i >> 2) * 8 + 4 * h + (i & 3);  // row within the step
+          float p = fast_exp2(fmaf(s[i], c, -l4[e]));
+          if (need_mask && (qi >= qvalid || (CAUSAL && kpos > sfirst + qi))) p = 0.f;
+          pv[e] = p;
+          dv4[e] = p * (dp[i] - d4[e]);
+        }
+        // element i = 4g + e belongs to k-step s2 = g/2, slot w = 2*(g%2) + e/2
+        const int s2 = g >> 1;
+        const bf16x2 p01 = __builtin_convertvector((f32x2){pv[0], pv[1]}, bf16x2);
+        const bf16x2 p23 = __builtin_convertvector((f32x2){pv[2], pv[3]}, bf16x2);
+        const bf16x2 d01 = __builtin_convertvector((f32x2){dv4[0], dv4[1]}, bf16x2);
+        const bf16x2 d23 = __builtin_convertvector((f32x2){dv4[2], dv4[3]}, bf16x2);
+        pf[s2][2 * (g & 1)] = __builtin_bit_cast(uint32_t, p01);
+        pf[s2][2 * (g & 1) + 1] = __builtin_bit_cast(uint32_t, p23);
+        dsf[s2][2 * (g & 1)] = __builtin_bit_cast(uint32_t, d01);
+        dsf[s2][2 * (g & 1) + 1] = __builtin_bit_cast(uint32_t, d23);
+      }
+      // dV^T[D x 32 keys] += dO^T[D x 32 q] P[32 q x 32 keys];  dK^T += Q^T dS
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt) {
+          const u32x4 of = Tile::tr_read(oo, tp0, tp1, 16 * s2, dt);
+          dv[dt] = mfma_bf16(as_bf16x8(of), as_bf16x8(pf[s2]), dv[dt]);
+          const u32x4 qf2 = Tile::tr_read(qo, tp0, tp1, 16 * s2, dt);
+          dk[dt] = mfma_bf16(as_bf16x8(qf2), as_bf16x8(dsf[s2]), dk[dt]);
+        }
+    }
+    if (has_next) stats_store(sv, smem0 + (cur ^ 1) * SLOT);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): next tile landed
+    __syncthreads();
+    cur ^= 1;
+  }
+
+  if (krow < a.Skv) {
+    const int64_t krow_dk = b * a.dk_sb + hk * a.dk_sh + (int64_t)krow * a.dk_ss;
+    const int64_t krow_dv = b * a.dv_sb + hk * a.dv_sh + (int64_t)krow * a.dv_ss;
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d = 32 * dt + 8 * g + 4 * h;
+        const bf16x2 k01 = __builtin_convertvector(
+            (f32x2){dk[dt][4 * g] * a.scale, dk[dt][4 * g + 1] * a.scale}, bf16x2);
+        const bf16x2 k23 = __builtin_convertvector(
+            (f32x2){dk[dt][4 * g + 2] * a.scale, dk[dt][4 * g + 3] * a.scale}, bf16x2);
+        *(u32x2 *)((uint16_t *)a.dk + krow_dk + d) =
+            u32x2{__builtin_bit_cast(uint32_t, k01), __builtin_bit_cast(uint32_t, k23)};
+        const bf16x2 v01 = __builtin_convertvector((f32x2){dv[dt][4 * g], dv[dt][4 * g + 1]}, bf16x2);
+        const bf16x2 v23 =
+            __builtin_convertvector((f32x2){dv[dt][4 * g + 2], dv[dt][4 * g + 3]}, bf16x2);
+        *(u32x2 *)((uint16_t *)a.dv + krow_dv + d) =
+            u32x2{__builtin_bit_cast(uint32_t, v01), __builtin_bit_cast(uint32_t, v23)};
+      }
+  }
+}
+
+template <int D, bool CAUSAL>
+int launch_bwd(const BwdArgs &a, hipStream_t stream) {
+  // 1. D_i
+  {
+    const int64_t nrows = (int64_t)a.B * a.Hq * a.Sq;
+    int64_t blocks = (nrows * (D / 8) + 255) / 256;
+    if (blocks > (1 << 20)) blocks = 1 << 20;
+    if (blocks > 0)
+      hipLaunchKernelGGL((bwd_delta_kernel<D>), dim3((unsigned)blocks), dim3(256), 0, stream, a);
+  }
+  // 2. dK, dV
+  {
+    const int nkt = (a.Skv + 127) / 128;
+    const int64_t blocks = (int64_t)nkt * a.Hkv * a.B;
+    if (blocks > 0)
+      hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3((unsigned)blocks), dim3(256), 0,
+                         stream, a, nkt);
+  }
+  // 3. dQ
+  {
+    const int nqt = (a.Sq + 255) / 256;
+    const int64_t blocks = (int64_t)nqt * a.Hq * a.B;
+    if (blocks > 0)
+      hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3((unsigned)blocks), dim3(512), 0,
+                         stream, a, nqt);
+  }
+  return hipGetLastError() == hipSuccess ? RA_OK : RA_ERR_HIP;
+}
+
+}  // namespace
 
 size_t bwd_workspace_bytes(int64_t B, int64_t Hq, int64_t Sq) {
   const size_t n = (size_t)(B * Hq * Sq) * sizeof(float);
   return (n + 255) / 256 * 256;
 }
 
-int launch_attn_bwd(const BwdArgs &, int, int, hipStream_t) { return RA_ERR_UNSUPPORTED; }
+int launch_attn_bwd(const BwdArgs &a, int D, int causal, hipStream_t stream) {
+  if (D == 128) return causal ? launch_bwd<128, true>(a, stream) : launch_bwd<128, false>(a, stream);
+  if (D == 64) return causal ? launch_bwd<64, true>(a, stream) : launch_bwd<64, false>(a, stream);
+  return RA_ERR_UNSUPPORTED;
+}
 
 }  // namespace ra

@@ -67,7 +67,6 @@ constexpr int kBf16Waves = RA_FWD_BF16_WAVES;  // 8 measured faster than 2 x 4
 #define RA_FWD_PIPELINE 0
 #endif
 
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 // ---------------------------------------------------------------------------------
 // bf16 path: 32x32x16 bf16 MFMA; K row-major in LDS, V transposed + key-permuted in LDS.
@@ -285,37 +284,6 @@ struct Bf16Path {
 // addressed by lanes a, a+4, a+8, a+12.  No staging registers, no transpose ALU work
 // and no LDS store instructions.
 // ---------------------------------------------------------------------------------
-typedef __attribute__((address_space(3))) unsigned char lds_u8;
-typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-// 32-bit LDS offset of a __shared__ object (generic -> local address space).
-__device__ __forceinline__ uint32_t lds_offset(const void *p) {
-  return (uint32_t)(size_t)(const lds_u8 *)p;
-}
-__device__ __forceinline__ u32x4 lds_read_b128(uint32_t addr) {
-  return *(const lds_u32x4 *)(size_t)addr;
-}
-__device__ __forceinline__ s16x4 lds_read_tr16_b64(uint32_t addr) {
-  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(size_t)addr);
-}
-
-// One 16-byte-per-lane direct load from global memory into LDS: lane l's bytes land at
-// LDS offset lds + 16*l.  Issued through inline assembly so the compiler's wait analysis
-// does not see an LDS write in flight (it would otherwise drain every LDS read queue);
-// every consumer of the slot waits explicitly (vmcnt(0) + barrier) instead.  The loop
-// that uses it issues no other vector-memory operation.  M0 needs one wait state
-// before the load reads it.
-__device__ __forceinline__ void dma_b128(const void *tile_base, int lane_off, uint32_t lds) {
-  asm volatile(
-      "s_mov_b32 m0, %2\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %0, %1"
-      :
-      : "v"(lane_off), "s"(tile_base), "s"(lds)
-      : "memory", "m0");
-}
-
 template <int D>
 struct Bf16DirectPath {
   using elem_t = uint16_t;

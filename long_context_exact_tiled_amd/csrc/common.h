@@ -19,8 +19,10 @@ namespace ra {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -66,5 +68,42 @@ __device__ __forceinline__ bf16x8 as_bf16x8(const u32x4 &u) { return __builtin_b
 __device__ __forceinline__ uint32_t perm_b32(uint32_t hi, uint32_t lo, uint32_t sel) {
   return __builtin_amdgcn_perm(hi, lo, sel);
 }
+
+// ---- LDS addressing and direct global->LDS loads -------------------------------
+typedef __attribute__((address_space(3))) unsigned char lds_u8;
+typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+// 32-bit LDS offset of a __shared__ object (generic -> local address space).
+__device__ __forceinline__ uint32_t lds_offset(const void *p) {
+  return (uint32_t)(size_t)(const lds_u8 *)p;
+}
+__device__ __forceinline__ u32x4 lds_read_b128(uint32_t addr) {
+  return *(const lds_u32x4 *)(size_t)addr;
+}
+__device__ __forceinline__ s16x4 lds_read_tr16_b64(uint32_t addr) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(size_t)addr);
+}
+
+// One 16-byte-per-lane direct load from global memory into LDS: lane l's bytes land at
+// LDS offset lds + 16*l (lds must be wave-uniform).  Issued through inline assembly so
+// the compiler's wait analysis does not see an LDS write in flight (it would otherwise
+// drain every LDS read queue).  Consequences the callers honour: every reader of the
+// destination waits explicitly (s_waitcnt vmcnt(0), then a barrier); loads the compiler
+// does track stay correctly waited, because memory loads complete in issue order and
+// uncounted extra loads only make the compiler's vmcnt(N) waits stricter.  M0 needs one
+// wait state before the load reads it.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"  // m0: no compiler-generated code here uses it
+__device__ __forceinline__ void dma_b128(const void *tile_base, int lane_off, uint32_t lds) {
+  asm volatile(
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %0, %1"
+      :
+      : "v"(lane_off), "s"(tile_base), "s"(lds)
+      : "memory", "m0");
+}
+#pragma clang diagnostic pop
 
 }  // namespace ra

@@ -1,0 +1,111 @@
+"""GPU parity of ra_attn_bwd (dq, dk, dv) against the oracle's fp64 gradients.
+
+The GPU forward supplies o and lse to the GPU backward (the product path); the oracle
+recomputes everything from q, k, v, dO on its own.
+
+Tolerance for bf16 gradients (none is stated for gradients, so it is derived from the
+arithmetic): each output is rounded to bf16 once (<= 2^-9 |g|) and P and dS are rounded
+to bf16 before their matrix products (aggregate <= 2^-9 |g| more), so element-wise
+|err| <= 2e-2 + 2^-8 |ref|; besides, mean abs err <= 2e-3 and relative L2 <= 1e-2.  With
+grouped heads dK and dV sum over the group and reach |g| of several units, where the
+output rounding alone exceeds a flat 2e-2.
+"""
+import numpy as np
+import pytest
+import torch
+
+import long_context_exact_tiled_amd as ra
+import oracle
+import seeded_inputs as si
+from _gpu import require_gpu, say, to_dev, to_np64
+
+pytestmark = pytest.mark.gpu
+
+GRAD_TOL = dict(o_max=2e-2, o_mean=2e-3)
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    require_gpu()
+
+
+def check_grad(got, ref, what):
+    assert np.isfinite(got).all(), f"{what}: non-finite"
+    err = np.abs(got - ref)
+    mx, mean = float(err.max(initial=0.0)), float(err.mean()) if err.size else 0.0
+    rel = float(np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-30))
+    print(f"[parity] {what}: max|err|={mx:.3e} mean|err|={mean:.3e} relL2={rel:.3e} "
+          f"max|ref|={float(np.abs(ref).max(initial=0.0)):.3e}", flush=True)
+    excess = float((err - (GRAD_TOL["o_max"] + 2.0 ** -8 * np.abs(ref))).max(initial=-1.0))
+    assert excess <= 0.0, f"{what}: element error over 2e-2 + 2^-8|ref| by {excess}"
+    assert mean <= GRAD_TOL["o_mean"], f"{what}: mean abs err {mean}"
+    assert rel <= 1e-2, f"{what}: relative L2 {rel}"
+
+
+def _run(B, Hq, Hkv, Sq, Skv, D, causal, P=1, start=0, q_off=0, kv_off=0, seed=0):
+    say(f"bwd D={D} causal={causal} B={B} Hq={Hq} Hkv={Hkv} Sq={Sq} Skv={Skv} P={P} "
+        f"start={start} q_off={q_off} kv_off={kv_off}")
+    q, k, v, do = si.draw_qkv(seed, (B, Hq, Sq, D), (B, Hkv, Skv, D), "bf16", with_dout=True)
+    qd, kd, vd, dod = (to_dev(x, "bf16") for x in (q, k, v, do))
+    kw = dict(causal=causal, num_chunks=P, start_chunk=start, q_offset=q_off, kv_offset=kv_off)
+    o, lse = ra.attn_fwd(qd, kd, vd, **kw)
+    dq = torch.full_like(qd, float("nan"))
+    dk = torch.full_like(kd, float("nan"))
+    dv = torch.full_like(vd, float("nan"))
+    ra.attn_bwd(qd, kd, vd, o, dod, lse, dq=dq, dk=dk, dv=dv, **kw)
+    torch.cuda.synchronize()
+    ref = oracle.attention_bwd(*(si.as_f64(x, "bf16") for x in (q, k, v, do)), causal=causal,
+                               q_offset=q_off, kv_offset=kv_off)
+    for got, r, name in zip((dq, dk, dv), ref, ("dq", "dk", "dv")):
+        check_grad(to_np64(got), r, name)
+
+
+CASES = [
+    # B, Hq, Hkv, Sq, Skv, D, causal, P, start, q_off, kv_off
+    (1, 2, 2, 300, 300, 128, True, 1, 0, 0, 0),
+    (2, 4, 2, 200, 300, 64, False, 3, 1, 0, 0),
+    (1, 4, 1, 256, 256, 128, True, 4, 1, 0, 0),
+    (1, 2, 2, 130, 390, 128, True, 3, 2, 260, 0),
+    (1, 2, 2, 200, 200, 128, True, 1, 0, 0, 100),
+    (1, 7, 1, 333, 333, 128, True, 1, 0, 0, 0),
+    (1, 2, 2, 1, 1, 64, True, 1, 0, 0, 0),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: "-".join(map(str, c)))
+def test_small_bwd(case):
+    B, Hq, Hkv, Sq, Skv, D, causal, P, start, q_off, kv_off = case
+    _run(B, Hq, Hkv, Sq, Skv, D, causal, P, start, q_off, kv_off,
+         seed=sum(map(ord, str(case))) % 991)
+
+
+def test_bwd_deterministic():
+    say("bwd determinism")
+    q, k, v, do = (torch.randn(1, 4, 400, 128, device="cuda").bfloat16() for _ in range(4))
+    o, lse = ra.attn_fwd(q, k, v, causal=True)
+    a = ra.attn_bwd(q, k, v, o, do, lse, causal=True)
+    b = ra.attn_bwd(q, k, v, o, do, lse, causal=True)
+    torch.cuda.synchronize()
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+
+
+def test_llama_causal_bwd_16k_workload_sampled_heads():
+    """Full-size backward; every element of three whole heads checked against the oracle."""
+    w = si.WORKLOADS["llama7b_causal_bwd_16k"]
+    say(f"workload {w.name}")
+    q, k, v, do = si.draw_qkv(w.seed, w.q_shape, w.kv_shape, "bf16", with_dout=True)
+    qd, kd, vd, dod = (to_dev(x, "bf16") for x in (q, k, v, do))
+    o, lse = ra.attn_fwd(qd, kd, vd, causal=True)
+    dq, dk, dv = ra.attn_bwd(qd, kd, vd, o, dod, lse, causal=True)
+    torch.cuda.synchronize()
+    for t in (dq, dk, dv):
+        assert torch.isfinite(t).all()
+    heads = [(0, 0), (0, 17), (0, 31)]
+    q64, k64, v64, do64 = (si.as_f64(x, "bf16") for x in (q, k, v, do))
+    ref = oracle.attention_bwd_heads(q64, k64, v64, do64, heads, causal=True, row_block=512)
+    dq_n, dk_n, dv_n = (to_np64(t) for t in (dq, dk, dv))
+    for (b, g), (rq, rk, rv) in ref.items():
+        check_grad(dq_n[b, g:g + 1], rq, f"dq head {g}")
+        check_grad(dk_n[b, g], rk, f"dk head {g}")
+        check_grad(dv_n[b, g], rv, f"dv head {g}")
