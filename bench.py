@@ -58,6 +58,30 @@ def attn_flops(B, Hq, Sq, Skv, D, num_chunks=1, causal=True, q_offset=0, kv_offs
     return 4.0 * B * Hq * D * visible_pairs(Sq, Skv, num_chunks, causal, q_offset, kv_offset)
 
 
+ROOT = os.path.dirname(os.path.abspath(__file__))
+COUNTERS = os.path.join(ROOT, "profiles", "attn_fwd_qwen7b_gqa_32k_counters.md")
+FWD_SOURCES = ("long_context_exact_tiled_amd/csrc/attn_fwd.hip",
+               "long_context_exact_tiled_amd/csrc/common.h")
+
+
+def measured_traffic():
+    """HBM bytes per launch of the headline attention kernel, from the committed counter
+    summary (FETCH_SIZE/WRITE_SIZE scaled by a plain copy of known size) -- or None when
+    the kernel source no longer matches the profiled one."""
+    import hashlib
+    import re
+    try:
+        text = open(COUNTERS).read()
+        h = hashlib.sha1()
+        for f in FWD_SOURCES:
+            h.update(open(os.path.join(ROOT, f), "rb").read())
+        want = re.search(r"source_sha1:\s*([0-9a-f]{40})", text).group(1)
+        val = re.search(r"traffic_bytes_per_launch:\s*(\d+)", text).group(1)
+    except (OSError, AttributeError):
+        return None
+    return int(val) if h.hexdigest() == want else None
+
+
 def blas_threads() -> int:
     try:
         from threadpoolctl import threadpool_info
@@ -88,9 +112,17 @@ def cpu_baseline(w, budget_s: float = 15.0):
     for a in starts:
         qb = si.bf16_bits_to_f32(si.bf16_bits(
             rng.standard_normal((1, 1, blk, D), dtype=np.float32))).astype(np.float64)
-        oracle.full_attention(qb, k64, v64, causal=w.causal, q_offset=w.q_offset + a,
-                              kv_offset=w.kv_offset)
-        done_flops += attn_flops(1, 1, blk, Skv, D, 1, w.causal, w.q_offset + a, w.kv_offset)
+        if w.backward:  # all five products for the block's (query, key) pairs
+            nk = min(Skv, w.q_offset + a + blk - w.kv_offset) if w.causal else Skv
+            oracle.attention_bwd(qb, k64[:, :, :nk], v64[:, :, :nk], qb, causal=w.causal,
+                                 q_offset=w.q_offset + a, kv_offset=w.kv_offset)
+            done_flops += 2.5 * attn_flops(1, 1, blk, Skv, D, 1, w.causal, w.q_offset + a,
+                                           w.kv_offset)
+        else:
+            oracle.full_attention(qb, k64, v64, causal=w.causal, q_offset=w.q_offset + a,
+                                  kv_offset=w.kv_offset)
+            done_flops += attn_flops(1, 1, blk, Skv, D, 1, w.causal, w.q_offset + a,
+                                     w.kv_offset)
         rows += blk
         if time.perf_counter() - t0 > budget_s:
             break
@@ -98,9 +130,9 @@ def cpu_baseline(w, budget_s: float = 15.0):
     return {
         "value": done_flops / dt / 1e12, "unit": "TFLOP/s", "cores": blas_threads(),
         "kind": "oracle",
-        "sample": f"{rows} query rows ({len(starts) and rows // blk} blocks of {blk}, spread "
-                  f"over the sequence) of one head against the full {Skv}-key causal context, "
-                  f"fp64 NumPy, {dt:.1f} s",
+        "sample": f"{rows} query rows ({rows // blk} blocks of {blk}, random positions) of "
+                  f"one head against its {'causal ' if w.causal else ''}{Skv}-key context, "
+                  f"{'backward' if w.backward else 'forward'} oracle, fp64 NumPy, {dt:.1f} s",
     }
 
 
@@ -112,6 +144,8 @@ def main():
     ap.add_argument("--workload", default="qwen7b_ulysses4_rank0_32k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--chunked", action="store_true",
+                    help="ring workloads: one attn_fwd per visible chunk + lse_merge")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: every box here has a single MI355X, and the multi-GPU "
@@ -157,19 +191,44 @@ def main():
 
         def post():
             ra.ulysses_permute(o, P, r, 1, out=o_seq)
-    else:
-        q, k, v = (to_dev(x) for x in si.draw_qkv(w.seed, w.q_shape, w.kv_shape, w.dtype))
-        o = torch.empty_like(q)
-        lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+    elif w.backward:
+        q, k, v, do = (to_dev(x) for x in si.draw_qkv(w.seed, w.q_shape, w.kv_shape, w.dtype,
+                                                      with_dout=True))
+        o, lse = ra.attn_fwd(q, k, v, causal=w.causal)
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        ws = torch.empty(max(ra.attn_bwd_workspace_size(q, k, causal=w.causal), 256),
+                         dtype=torch.uint8, device=dev)
+        flops *= 2.5  # five matrix products per (query, key) pair against the forward's two
         moved = 0
+        extra["kernel"] = "attn_bwd (delta + dkdv + dq)"
 
         def pre():
             pass
 
         def attn():
-            ra.attn_fwd(q, k, v, causal=w.causal, num_chunks=w.num_chunks,
-                        start_chunk=w.start_chunk, q_offset=w.q_offset, kv_offset=w.kv_offset,
-                        out=o, lse=lse)
+            ra.attn_bwd(q, k, v, o, do, lse, causal=w.causal, dq=dq, dk=dk, dv=dv, workspace=ws)
+
+        def post():
+            pass
+    else:
+        q, k, v = (to_dev(x) for x in si.draw_qkv(w.seed, w.q_shape, w.kv_shape, w.dtype))
+        o = torch.empty_like(q)
+        lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+        moved = 0
+        kw = dict(causal=w.causal, num_chunks=w.num_chunks, start_chunk=w.start_chunk,
+                  q_offset=w.q_offset, kv_offset=w.kv_offset)
+
+        def pre():
+            pass
+
+        if args.chunked:
+            extra["kernel"] = "attn_fwd per visible chunk (fp32 partials) + lse_merge"
+
+            def attn():
+                ra.ring_attn_chunked(q, k, v, **kw)
+        else:
+            def attn():
+                ra.attn_fwd(q, k, v, out=o, lse=lse, **kw)
 
         def post():
             pass
@@ -226,10 +285,13 @@ def main():
                    "q_offset": w.q_offset, "ulysses_P": w.ulysses_P,
                    "ulysses_rank": w.ulysses_rank, "parallelism": "1 GPU (one rank's share)"},
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
-                     "frac": achieved / peak, "traffic": None, "kernel": "attn_fwd"},
+                     "frac": achieved / peak, "traffic": None,
+                     "kernel": extra.pop("kernel", "attn_fwd")},
         "cpu_baseline": None,
         **extra,
     }
+    if w.name == "qwen7b_ulysses4_rank0_32k" and not args.chunked:
+        line["roofline"]["traffic"] = measured_traffic()
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)
     print(json.dumps(line), flush=True)

@@ -14,7 +14,7 @@
 //        softmax keeps a running max and normaliser, only the output is written back.
 //
 // Design on gfx950 (CDNA4), from measured rates (MFMA 32x32x16 bf16 ~37 clk/SIMD;
-// v_exp_f32 ~5x a plain VALU op; ds_read_b128 ~190 B/clk/CU vs ~120 for b64):
+// v_exp_f32 ~4-5x a plain VALU op; ds_read_b128 ~190 B/clk/CU vs ~120 for b64):
 //   * one workgroup = 8 wavefronts = 256 query rows (32 per wave) of one (batch, head);
 //     two waves per SIMD, so one wave's softmax (VALU) runs under the other's MFMAs;
 //     all 8 waves share each K/V tile in LDS (one global read of K/V per 256 rows);

@@ -1,0 +1,66 @@
+"""Invariants of the generated gfx950 code, checked from the compiler's assembly on the
+CPU (hipcc cross-compiles; no GPU needed):
+
+* M0 is written only by the direct-load sequences (s_mov_b32 m0 ... global_load_lds):
+  the inline assembly that issues them clobbers M0, which is safe only while no
+  compiler-generated code in these kernels relies on M0;
+* no packed-fp32 VALU instructions (v_pk_fma/mul/add_f32) are generated;
+* the hot kernels keep everything in registers (no scratch spills).
+"""
+import os
+import re
+import shutil
+import subprocess
+
+import pytest
+
+from long_context_exact_tiled_amd import build as B
+
+HOT = ("attn_fwd_direct_kernel", "bwd_dq_kernel", "bwd_dkdv_kernel", "lse_merge_kernel",
+       "permute_kernel")
+
+
+def _asm(src):
+    out = f"/tmp/_inv_{os.getpid()}_{src}.s"
+    cmd = [B.hipcc(), *B.FLAGS, "-I", os.path.join(B.ROOT, "include"), "-S", "--cuda-device-only",
+           os.path.join(B.CSRC, src), "-o", out]
+    subprocess.run(cmd, check=True, stdout=subprocess.DEVNULL, stderr=subprocess.DEVNULL)
+    text = open(out).read()
+    os.remove(out)
+    return text
+
+
+@pytest.fixture(scope="module")
+def asm():
+    if not (shutil.which("hipcc") or os.path.exists("/opt/rocm/bin/hipcc")):
+        pytest.skip("hipcc not available")
+    return {src: _asm(src) for src in ("attn_fwd.hip", "attn_bwd.hip", "lse_merge.hip",
+                                       "ulysses_permute.hip")}
+
+
+def test_m0_only_in_dma_sequences(asm):
+    for src, text in asm.items():
+        lines = [l.strip() for l in text.splitlines()]
+        for i, l in enumerate(lines):
+            if re.search(r"\bm0\b", l) and not l.startswith(";"):
+                assert l.startswith("s_mov_b32 m0, s"), (src, l)
+                nxt = [x for x in lines[i + 1:i + 4] if x and not x.startswith(";")]
+                assert nxt[0].startswith("s_nop") and nxt[1].startswith("global_load_lds_dwordx4"), \
+                    (src, l, nxt)
+
+
+def test_no_packed_fp32(asm):
+    for src, text in asm.items():
+        assert not re.search(r"\bv_pk_(fma|mul|add)_f32\b", text), src
+
+
+def test_hot_kernels_do_not_spill(asm):
+    for src, text in asm.items():
+        for m in re.finditer(r"^(\S+):\s*$", text, re.M):
+            name = m.group(1)
+            if not any(k in name for k in HOT) or name.startswith("."):
+                continue
+            body = text[m.end():text.find(".Lfunc_end", m.end())]
+            scratch = re.search(r";\s*ScratchSize:\s*(\d+)", text[m.end():])
+            assert "scratch_store" not in body and "buffer_store_dword v" not in body, (src, name)
+            assert scratch is None or int(scratch.group(1)) == 0, (src, name, scratch.group(1))
