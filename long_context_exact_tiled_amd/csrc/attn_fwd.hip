@@ -573,6 +573,7 @@ attn_fwd_kernel(FwdArgs a) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);  // wave-uniform copy
   const int r32 = lane & 31;
   const int h = lane >> 5;
 
@@ -597,9 +598,9 @@ attn_fwd_kernel(FwdArgs a) {
   // This lane's query row and the wave's row range (global positions).
   const int qrow = q0 + 32 * wave + r32;
   const int64_t qpos = a.q_offset + qrow;
-  const int64_t wpos_first = a.q_offset + q0 + 32 * wave;
+  const int64_t wpos_first = a.q_offset + q0 + 32 * wave_u;
   const int64_t wpos_last = wpos_first + 31;
-  const bool wave_active = (q0 + 32 * wave) < a.Sq;
+  const bool wave_active = (q0 + 32 * wave_u) < a.Sq;
   const float c = a.scale_log2;
 
   typename Path::QFrag qf;
@@ -800,6 +801,7 @@ attn_fwd_direct_kernel(FwdArgs a) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);  // wave-uniform copy
   const int r32 = lane & 31;
   const int h = lane >> 5;
 
@@ -821,9 +823,9 @@ attn_fwd_direct_kernel(FwdArgs a) {
 
   const int qrow = q0 + 32 * wave + r32;
   const int64_t qpos = a.q_offset + qrow;
-  const int64_t wpos_first = a.q_offset + q0 + 32 * wave;
+  const int64_t wpos_first = a.q_offset + q0 + 32 * wave_u;
   const int64_t wpos_last = wpos_first + 31;
-  const bool wave_active = (q0 + 32 * wave) < a.Sq;
+  const bool wave_active = (q0 + 32 * wave_u) < a.Sq;
   const float c = a.scale_log2;
 
   typename Path::Lane L;
