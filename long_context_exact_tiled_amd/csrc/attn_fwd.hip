@@ -60,6 +60,9 @@ constexpr int kBf16Waves = RA_FWD_BF16_WAVES;  // 8 measured faster than 2 x 4
 #ifndef RA_FWD_DMA_ASM
 #define RA_FWD_DMA_ASM 1
 #endif
+#ifndef RA_FWD_DIRECT_WAVES
+#define RA_FWD_DIRECT_WAVES 8  // waves per workgroup on the bf16 direct path
+#endif
 #ifndef RA_FWD_DMA_LATE
 #define RA_FWD_DMA_LATE 0
 #endif
@@ -284,11 +287,11 @@ struct Bf16Path {
 // addressed by lanes a, a+4, a+8, a+12.  No staging registers, no transpose ALU work
 // and no LDS store instructions.
 // ---------------------------------------------------------------------------------
-template <int D>
+template <int D, int NW = 8>
 struct Bf16DirectPath {
   using elem_t = uint16_t;
-  static constexpr int kWaves = 8;
-  static constexpr int kThreads = 512;
+  static constexpr int kWaves = NW;                // 32 query rows per wave
+  static constexpr int kThreads = 64 * NW;
   static constexpr int RB = 2 * D;                 // row bytes
   static constexpr int TILE_BYTES = BN * RB;       // one of K or V
   static constexpr int BUF_BYTES = 2 * TILE_BYTES; // K then V
@@ -790,10 +793,10 @@ attn_fwd_kernel(FwdArgs a) {
 // Kernel for the bf16 direct path: double-buffered LDS, the next tile's direct loads in
 // flight under the current tile's math.
 // ---------------------------------------------------------------------------------
-template <int D, bool CAUSAL>
-__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+template <int D, bool CAUSAL, int NW>
+__global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 attn_fwd_direct_kernel(FwdArgs a) {
-  using Path = Bf16DirectPath<D>;
+  using Path = Bf16DirectPath<D, NW>;
   using elem_t = uint16_t;
   constexpr int BM = 32 * Path::kWaves;
   __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * Path::BUF_BYTES];
@@ -938,10 +941,11 @@ attn_fwd_direct_kernel(FwdArgs a) {
 template <int D, bool CAUSAL>
 int launch_direct(const FwdArgs &args, hipStream_t stream) {
   FwdArgs a = args;
-  a.num_q_tiles = (a.Sq + 255) / 256;
+  constexpr int NW = RA_FWD_DIRECT_WAVES;
+  a.num_q_tiles = (a.Sq + 32 * NW - 1) / (32 * NW);
   const int64_t blocks = (int64_t)a.num_q_tiles * a.Hq * a.B;
   if (blocks <= 0) return RA_OK;
-  hipLaunchKernelGGL((attn_fwd_direct_kernel<D, CAUSAL>), dim3((unsigned)blocks), dim3(512), 0,
+  hipLaunchKernelGGL((attn_fwd_direct_kernel<D, CAUSAL, NW>), dim3((unsigned)blocks), dim3(64 * NW), 0,
                      stream, a);
   return hipGetLastError() == hipSuccess ? RA_OK : RA_ERR_HIP;
 }
