@@ -27,6 +27,18 @@ FLAGS = [
     "-Wno-unused-result",
 ]
 
+# Per-source extras.  The backward's dK/dV kernel runs one wave per SIMD with more than
+# 256 registers live; by default the compiler then places the score accumulators in
+# AGPRs and copies every element to VGPRs for the softmax VALU work.  The VGPR form of
+# the MFMAs keeps them in VGPRs (measured: 910 -> 313 AGPR copies per tile, 4 % faster).
+EXTRA = {
+    "attn_bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
+
+
+def flags_for(src: str) -> list:
+    return [*FLAGS, *EXTRA.get(src, [])]
+
 
 def hipcc() -> str:
     for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
@@ -44,7 +56,7 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
         objs, procs = [], []
         for src in SOURCES:
             obj = os.path.join(tmp, src + ".o")
-            cmd = [cc, *FLAGS, *inc, "-c", os.path.join(CSRC, src), "-o", obj]
+            cmd = [cc, *flags_for(src), *inc, "-c", os.path.join(CSRC, src), "-o", obj]
             if verbose:
                 print(" ".join(cmd), flush=True)
             procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE,

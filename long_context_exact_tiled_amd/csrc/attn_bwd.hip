@@ -32,6 +32,9 @@ namespace ra {
 namespace {
 
 constexpr int TN = 64;  // rows per LDS tile (keys in bwd_dq, queries in bwd_dkdv)
+#ifndef RA_BWD_DKDV_PIPE
+#define RA_BWD_DKDV_PIPE 1  // software-pipelined dK/dV tile
+#endif
 
 // 16-byte-chunk swizzle of a tile row: for 16 consecutive rows at one chunk the physical
 // chunks differ (row-wise reads), and for 4 consecutive rows at 4 consecutive chunks
@@ -411,6 +414,112 @@ bwd_dkdv_kernel(BwdArgs a, int num_kv_tiles) {
     }
     const int q0 = qstart + (it % nqt) * TN;
     const int64_t qpos0 = a.q_offset + q0;
+#if RA_BWD_DKDV_PIPE
+    // The two 32-query steps of the tile as one stream of 4*NST MFMAs, operands read
+    // kDep MFMAs ahead:  [S,dP of step 0] [S,dP of step 1 | P,dS of step 0]
+    // [dV,dK of step 0 | P,dS of step 1] [dV,dK of step 1].  A step with no visible
+    // (query, key) pair for this wave is computed and masked to zero (diagonal only).
+    const int qv0 = min(32, a.Sq - q0), qv1 = min(32, a.Sq - (q0 + 32));
+    const bool vis0 = !(CAUSAL && wk_first > qpos0 + 31);
+    const bool vis1 = qv1 > 0 && !(CAUSAL && wk_first > qpos0 + 63);
+    if (wave_active && (vis0 || vis1)) {
+      constexpr int NST = D / 8;  // MFMAs per stage
+      constexpr int kDep = 4;
+      const bool nm0 = qv0 < 32 || (CAUSAL && wk_last > qpos0);
+      const bool nm1 = qv1 < 32 || (CAUSAL && wk_last > qpos0 + 32);
+      f32x16 s0 = f32x16{}, dp0 = f32x16{}, s1 = f32x16{}, dp1 = f32x16{};
+      u32x4 pf0[2], dsf0[2], pf1[2], dsf1[2];
+      f32x4 l4[4], d4[4];
+      auto operand = [&](int i) -> u32x4 {
+        const int stage = i / NST, j = i % NST;
+        const int qs = stage & 1;
+        const uint32_t qo = slot + (uint32_t)(32 * qs * Tile::RB);
+        if (stage < 2) return Tile::row_read((j & 1) ? qo + Tile::BYTES : qo, qpart, j >> 1);
+        const int pj = j >> 1, s2 = pj / (D / 32), dt = pj % (D / 32);
+        return Tile::tr_read((j & 1) ? qo : qo + Tile::BYTES, tp0, tp1, 16 * s2, dt);
+      };
+      auto stats_read = [&](int qs) {
+        const uint32_t st = slot + 2 * Tile::BYTES + (uint32_t)(4 * 32 * qs);
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          l4[g] = *(const __attribute__((address_space(3))) f32x4 *)(size_t)(
+              st + (uint32_t)(4 * (8 * g + 4 * h)));
+          d4[g] = *(const __attribute__((address_space(3))) f32x4 *)(size_t)(
+              st + (uint32_t)(4 * TN + 4 * (8 * g + 4 * h)));
+        }
+      };
+      // P and dS of 4 elements (element group g) of one step
+      auto pds = [&](const f32x16 &sv_, const f32x16 &dpv, bool nm, int qv, int64_t sfirst,
+                     int g, u32x4 (&pf)[2], u32x4 (&dsf)[2]) {
+        float pv[4], dv4[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int i = 4 * g + e;
+          const int qi = (i >> 2) * 8 + 4 * h + (i & 3);
+          float p = fast_exp2(fmaf(sv_[i], c, -l4[g][e]));
+          if (nm && (qi >= qv || (CAUSAL && kpos > sfirst + qi))) p = 0.f;
+          pv[e] = p;
+          dv4[e] = p * (dpv[i] - d4[g][e]);
+        }
+        const int s2 = g >> 1;
+        const bf16x2 p01 = __builtin_convertvector((f32x2){pv[0], pv[1]}, bf16x2);
+        const bf16x2 p23 = __builtin_convertvector((f32x2){pv[2], pv[3]}, bf16x2);
+        const bf16x2 d01 = __builtin_convertvector((f32x2){dv4[0], dv4[1]}, bf16x2);
+        const bf16x2 d23 = __builtin_convertvector((f32x2){dv4[2], dv4[3]}, bf16x2);
+        pf[s2][2 * (g & 1)] = __builtin_bit_cast(uint32_t, p01);
+        pf[s2][2 * (g & 1) + 1] = __builtin_bit_cast(uint32_t, p23);
+        dsf[s2][2 * (g & 1)] = __builtin_bit_cast(uint32_t, d01);
+        dsf[s2][2 * (g & 1) + 1] = __builtin_bit_cast(uint32_t, d23);
+      };
+      u32x4 op[kDep];
+#pragma unroll
+      for (int i = 0; i < kDep; ++i) op[i] = operand(i);
+      __builtin_amdgcn_sched_barrier(0);
+      // stage 0: S, dP of step 0
+#pragma unroll
+      for (int i = 0; i < NST; ++i) {
+        const bf16x8 A = as_bf16x8(op[i % kDep]);
+        if (i & 1) dp0 = mfma_bf16(A, vf[i >> 1], dp0); else s0 = mfma_bf16(A, kf[i >> 1], s0);
+        op[i % kDep] = operand(i + kDep);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      stats_read(0);
+      // stage 1: S, dP of step 1 | P, dS of step 0
+#pragma unroll
+      for (int j = 0; j < NST; ++j) {
+        const int i = NST + j;
+        const bf16x8 A = as_bf16x8(op[i % kDep]);
+        if (j & 1) dp1 = mfma_bf16(A, vf[j >> 1], dp1); else s1 = mfma_bf16(A, kf[j >> 1], s1);
+        op[i % kDep] = operand(i + kDep);
+        if (j % (NST / 4) == 1) pds(s0, dp0, nm0, qv0, qpos0, j / (NST / 4), pf0, dsf0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      stats_read(1);
+      // stage 2: dV, dK of step 0 | P, dS of step 1
+#pragma unroll
+      for (int j = 0; j < NST; ++j) {
+        const int i = 2 * NST + j;
+        const bf16x8 A = as_bf16x8(op[i % kDep]);
+        const int pj = j >> 1, s2 = pj / (D / 32), dt = pj % (D / 32);
+        if (j & 1) dk[dt] = mfma_bf16(A, as_bf16x8(dsf0[s2]), dk[dt]);
+        else dv[dt] = mfma_bf16(A, as_bf16x8(pf0[s2]), dv[dt]);
+        op[i % kDep] = operand(i + kDep);
+        if (j % (NST / 4) == 1) pds(s1, dp1, nm1, qv1, qpos0 + 32, j / (NST / 4), pf1, dsf1);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      // stage 3: dV, dK of step 1
+#pragma unroll
+      for (int j = 0; j < NST; ++j) {
+        const int i = 3 * NST + j;
+        const bf16x8 A = as_bf16x8(op[i % kDep]);
+        const int pj = j >> 1, s2 = pj / (D / 32), dt = pj % (D / 32);
+        if (j & 1) dk[dt] = mfma_bf16(A, as_bf16x8(dsf1[s2]), dk[dt]);
+        else dv[dt] = mfma_bf16(A, as_bf16x8(pf1[s2]), dv[dt]);
+        if (i + kDep < 4 * NST) op[i % kDep] = operand(i + kDep);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+#else
 #pragma unroll
     for (int qs = 0; qs < 2; ++qs) {
       const int64_t sfirst = qpos0 + 32 * qs, slast = sfirst + 31;  // query positions
@@ -466,6 +575,7 @@ bwd_dkdv_kernel(BwdArgs a, int num_kv_tiles) {
           dk[dt] = mfma_bf16(as_bf16x8(qf2), as_bf16x8(dsf[s2]), dk[dt]);
         }
     }
+#endif
     if (has_next) stats_store(sv, smem0 + (cur ^ 1) * SLOT);
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): next tile landed
     __syncthreads();

@@ -22,7 +22,7 @@ HOT = ("attn_fwd_direct_kernel", "bwd_dq_kernel", "bwd_dkdv_kernel", "lse_merge_
 
 def _asm(src):
     out = f"/tmp/_inv_{os.getpid()}_{src}.s"
-    cmd = [B.hipcc(), *B.FLAGS, "-I", os.path.join(B.ROOT, "include"), "-S", "--cuda-device-only",
+    cmd = [B.hipcc(), *B.flags_for(src), "-I", os.path.join(B.ROOT, "include"), "-S", "--cuda-device-only",
            os.path.join(B.CSRC, src), "-o", out]
     subprocess.run(cmd, check=True, stdout=subprocess.DEVNULL, stderr=subprocess.DEVNULL)
     text = open(out).read()
