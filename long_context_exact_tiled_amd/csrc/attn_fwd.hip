@@ -60,6 +60,9 @@ constexpr int kBf16Waves = RA_FWD_BF16_WAVES;  // 8 measured faster than 2 x 4
 #ifndef RA_FWD_DMA_ASM
 #define RA_FWD_DMA_ASM 1
 #endif
+#ifndef RA_FWD_KN
+#define RA_FWD_KN 128  // keys per tile on the bf16 direct path (measured: 3.6 % faster than 64)
+#endif
 #ifndef RA_FWD_DIRECT_WAVES
 #define RA_FWD_DIRECT_WAVES 8  // waves per workgroup on the bf16 direct path
 #endif
@@ -287,16 +290,20 @@ struct Bf16Path {
 // addressed by lanes a, a+4, a+8, a+12.  No staging registers, no transpose ALU work
 // and no LDS store instructions.
 // ---------------------------------------------------------------------------------
-template <int D, int NW = 8>
+template <int D, int NW = 8, int KN = BN>
 struct Bf16DirectPath {
+  static constexpr int NMT = KN / 32;              // 32-key S^T tiles per key tile
   using elem_t = uint16_t;
   static constexpr int kWaves = NW;                // 32 query rows per wave
   static constexpr int kThreads = 64 * NW;
   static constexpr int RB = 2 * D;                 // row bytes
-  static constexpr int TILE_BYTES = BN * RB;       // one of K or V
+  static constexpr int TILE_BYTES = KN * RB;       // one of K or V
   static constexpr int BUF_BYTES = 2 * TILE_BYTES; // K then V
   static constexpr int NBLK = TILE_BYTES / 1024;   // 1-KiB load blocks per tensor
   static constexpr int BPW = NBLK / kWaves;        // blocks per wave per tensor
+  static constexpr int RSTEP = kWaves * 1024 / RB;  // rows between a lane's pieces
+  static_assert((kWaves * 1024) % RB == 0 && RSTEP % 16 == 0,
+                "a lane's pieces share the in-row chunk (swizzles repeat every 16 rows)");
   static constexpr int kDepth = 4;                 // K operand reads in flight
   static constexpr int kVDepth = 2;                // V operand MFMAs in flight
   static_assert(NBLK % kWaves == 0, "tile must split evenly over the waves");
@@ -306,11 +313,11 @@ struct Bf16DirectPath {
   __device__ static int vsw(int r) { return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1); }
 
   struct QFrag { bf16x8 x[D / 16]; };
-  struct PFrag { u32x4 x[4]; };
+  struct PFrag { u32x4 x[KN / 16]; };
   struct Lane {
     int k_goff[BPW], v_goff[BPW];  // byte offsets of this lane's 16 B in the tile (row 0 = kb)
-    int k_row[BPW], v_row[BPW];    // tile rows this lane loads (for the clamped tail)
-    int k_chunk[BPW], v_chunk[BPW];
+    int row0;                      // tile row of piece 0; piece i is RSTEP*i rows further
+    int k_chunk, v_chunk;          // the 16-byte chunk within the row (the same for every i)
     uint32_t ka;                   // K operand read address (before the ks XOR), slot 0
     uint32_t vb;                   // V operand read address (before the dt XOR), slot 0
   };
@@ -322,12 +329,13 @@ struct Bf16DirectPath {
       const int blk = wave + kWaves * i;
       const int byte = blk * 1024 + 16 * lane;
       const int r = byte / RB, p = (byte % RB) / 16;
-      L.k_row[i] = r;
-      L.k_chunk[i] = p ^ ksw(r);
-      L.k_goff[i] = (int)(r * a.k_ss * 2) + 16 * L.k_chunk[i];
-      L.v_row[i] = r;
-      L.v_chunk[i] = p ^ vsw(r);
-      L.v_goff[i] = (int)(r * a.v_ss * 2) + 16 * L.v_chunk[i];
+      if (i == 0) {
+        L.row0 = r;
+        L.k_chunk = p ^ ksw(r);
+        L.v_chunk = p ^ vsw(r);
+      }
+      L.k_goff[i] = (int)(r * a.k_ss * 2) + 16 * L.k_chunk;
+      L.v_goff[i] = (int)(r * a.v_ss * 2) + 16 * L.v_chunk;
     }
     const int r = lane & 31, h = lane >> 5;
     L.ka = smem_base + (uint32_t)(r * RB + 16 * (ksw(r) ^ h));
@@ -349,7 +357,7 @@ struct Bf16DirectPath {
   // offset `slot` (from the start of LDS).
   __device__ static void load_tile(const Lane &L, const FwdArgs &a, const elem_t *kbase,
                                    const elem_t *vbase, int kb, uint32_t slot, int wave) {
-    const bool tail = kb + BN > a.Skv;
+    const bool tail = kb + KN > a.Skv;
     const elem_t *kt = kbase + (int64_t)kb * a.k_ss;
     const elem_t *vt = vbase + (int64_t)kb * a.v_ss;
 #pragma unroll
@@ -357,10 +365,9 @@ struct Bf16DirectPath {
       const uint32_t blk = (uint32_t)__builtin_amdgcn_readfirstlane(wave + kWaves * i);
       int koff = L.k_goff[i], voff = L.v_goff[i];
       if (tail) {  // rows past the end read the last row (their scores are masked)
-        const int kr = min(kb + L.k_row[i], a.Skv - 1) - kb;
-        const int vr = min(kb + L.v_row[i], a.Skv - 1) - kb;
-        koff = (int)(kr * a.k_ss * 2) + 16 * L.k_chunk[i];
-        voff = (int)(vr * a.v_ss * 2) + 16 * L.v_chunk[i];
+        const int r = min(kb + L.row0 + RSTEP * i, a.Skv - 1) - kb;
+        koff = (int)(r * a.k_ss * 2) + 16 * L.k_chunk;
+        voff = (int)(r * a.v_ss * 2) + 16 * L.v_chunk;
       }
 #if RA_FWD_DMA_ASM
       dma_b128(kt, koff, slot + blk * 1024);
@@ -376,33 +383,33 @@ struct Bf16DirectPath {
   }
 
   __device__ static u32x4 k_frag(uint32_t ka, int step) {
-    const int ks = step >> 1, mt = step & 1;
+    const int ks = step / NMT, mt = step % NMT;
     const uint32_t addr = (ka ^ (uint32_t)(32 * ks)) + (uint32_t)(mt * 32 * RB);
     return lds_read_b128(addr);
   }
 
   // S^T[32 keys x 32 queries] for the two 32-key halves of the tile.
-  __device__ static void qk(f32x16 (&s)[2], const QFrag &qf, uint32_t ka) {
-    constexpr int NSTEP = 2 * (D / 16);
+  __device__ static void qk(f32x16 (&s)[NMT], const QFrag &qf, uint32_t ka) {
+    constexpr int NSTEP = NMT * (D / 16);
     u32x4 kf[kDepth];
 #pragma unroll
     for (int i = 0; i < kDepth; ++i) kf[i] = k_frag(ka, i);
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt) s[mt] = f32x16{};
+    for (int mt = 0; mt < NMT; ++mt) s[mt] = f32x16{};
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int step = 0; step < NSTEP; ++step) {
-      const int ks = step >> 1, mt = step & 1;
+      const int ks = step / NMT, mt = step % NMT;
       s[mt] = mfma_bf16(as_bf16x8(kf[step % kDepth]), qf.x[ks], s[mt]);
       if (step + kDepth < NSTEP) kf[step % kDepth] = k_frag(ka, step + kDepth);
       __builtin_amdgcn_sched_barrier(0);
     }
   }
 
-  __device__ static float exp_pack(const f32x16 (&s)[2], float c, float mneg, PFrag &pf) {
+  __device__ static float exp_pack(const f32x16 (&s)[NMT], float c, float mneg, PFrag &pf) {
     float acc0 = 0.f, acc1 = 0.f;
 #pragma unroll
-    for (int kstep = 0; kstep < 4; ++kstep) {
+    for (int kstep = 0; kstep < KN / 16; ++kstep) {
       const int mt = kstep >> 1, s2 = kstep & 1;
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
@@ -429,7 +436,7 @@ struct Bf16DirectPath {
   }
 
   __device__ static void pv(f32x16 (&o)[D / 32], const PFrag &pf, uint32_t vb) {
-    constexpr int NSTEP = 4 * (D / 32);
+    constexpr int NSTEP = (KN / 16) * (D / 32);
     u32x4 vf[kVDepth];
 #pragma unroll
     for (int i = 0; i < kVDepth; ++i) vf[i] = v_frag(vb, i);
@@ -547,9 +554,10 @@ struct F32Path {
 // Next tile of the ring walk: tiles of BN keys, chunk by chunk in the order
 // (start + t) mod P; inside a chunk, tiles stop at the last key visible to the
 // block's last query row (vis_lim).  t == P means done.
+template <int KN = BN>
 __device__ __forceinline__ void ring_next(const FwdArgs &a, bool causal, int64_t vis_lim,
                                           int &t, int &kb, int &kend, int &cend) {
-  kb += BN;
+  kb += KN;
   while (kb >= kend) {
     ++t;
     if (t >= a.num_chunks) return;
@@ -793,10 +801,11 @@ attn_fwd_kernel(FwdArgs a) {
 // Kernel for the bf16 direct path: double-buffered LDS, the next tile's direct loads in
 // flight under the current tile's math.
 // ---------------------------------------------------------------------------------
-template <int D, bool CAUSAL, int NW>
+template <int D, bool CAUSAL, int NW, int KN>
 __global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 attn_fwd_direct_kernel(FwdArgs a) {
-  using Path = Bf16DirectPath<D, NW>;
+  using Path = Bf16DirectPath<D, NW, KN>;
+  constexpr int NMT = KN / 32;
   using elem_t = uint16_t;
   constexpr int BM = 32 * Path::kWaves;
   __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * Path::BUF_BYTES];
@@ -844,7 +853,7 @@ attn_fwd_direct_kernel(FwdArgs a) {
 
   const int64_t vis_lim = a.q_offset + qlast - a.kv_offset + 1;
   int t = -1, kb = 0, kend = 0, cend = 0;
-  ring_next(a, CAUSAL, vis_lim, t, kb, kend, cend);
+  ring_next<KN>(a, CAUSAL, vis_lim, t, kb, kend, cend);
   const uint32_t smem0 = lds_offset(smem);
   if (t < a.num_chunks) Path::load_tile(L, a, kbase, vbase, kb, smem0, wave);
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): Q and the first tile have landed
@@ -853,7 +862,7 @@ attn_fwd_direct_kernel(FwdArgs a) {
   int cur = 0;
   while (t < a.num_chunks) {
     const int kb_cur = kb, cend_cur = cend;
-    ring_next(a, CAUSAL, vis_lim, t, kb, kend, cend);
+    ring_next<KN>(a, CAUSAL, vis_lim, t, kb, kend, cend);
     const bool has_next = t < a.num_chunks;
 #if !RA_FWD_DMA_LATE
     if (has_next)
@@ -863,10 +872,10 @@ attn_fwd_direct_kernel(FwdArgs a) {
     const int64_t kpos0 = a.kv_offset + kb_cur;
     if (wave_active && !(CAUSAL && kpos0 > wpos_last)) {
       const uint32_t slot = (uint32_t)(cur * Path::BUF_BYTES);
-      f32x16 s[2];
+      f32x16 s[NMT];
       Path::qk(s, qf, L.ka + slot);
-      const int kvalid = min(BN, cend_cur - kb_cur);
-      const bool need_mask = (kvalid < BN) || (CAUSAL && kpos0 + kvalid - 1 > wpos_first);
+      const int kvalid = min(KN, cend_cur - kb_cur);
+      const bool need_mask = (kvalid < KN) || (CAUSAL && kpos0 + kvalid - 1 > wpos_first);
       if (need_mask) {
         int lim = kvalid;  // keys kk < lim are visible to this lane's row
         if (CAUSAL) {
@@ -875,7 +884,7 @@ attn_fwd_direct_kernel(FwdArgs a) {
         }
         lim -= 4 * h;
 #pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
+        for (int mt = 0; mt < NMT; ++mt)
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
             const int kk = 32 * mt + (i >> 2) * 8 + (i & 3);
@@ -887,7 +896,9 @@ attn_fwd_direct_kernel(FwdArgs a) {
       for (int i = 3; i < 15; i += 2) mx = fmaxf(fmaxf(mx, s[0][i]), s[0][i + 1]);
       mx = fmaxf(mx, s[0][15]);
 #pragma unroll
-      for (int i = 0; i < 16; i += 2) mx = fmaxf(fmaxf(mx, s[1][i]), s[1][i + 1]);
+      for (int mt = 1; mt < NMT; ++mt)
+#pragma unroll
+        for (int i = 0; i < 16; i += 2) mx = fmaxf(fmaxf(mx, s[mt][i]), s[mt][i + 1]);
       mx = halves_max(mx) * c;
       if (__builtin_amdgcn_ballot_w64(mx > m_run + kLazyRescale) != 0) {
         const float m_new = fmaxf(m_run, mx);
@@ -945,8 +956,9 @@ int launch_direct(const FwdArgs &args, hipStream_t stream) {
   a.num_q_tiles = (a.Sq + 32 * NW - 1) / (32 * NW);
   const int64_t blocks = (int64_t)a.num_q_tiles * a.Hq * a.B;
   if (blocks <= 0) return RA_OK;
-  hipLaunchKernelGGL((attn_fwd_direct_kernel<D, CAUSAL, NW>), dim3((unsigned)blocks), dim3(64 * NW), 0,
-                     stream, a);
+  constexpr int KN = RA_FWD_KN;
+  hipLaunchKernelGGL((attn_fwd_direct_kernel<D, CAUSAL, NW, KN>), dim3((unsigned)blocks),
+                     dim3(64 * NW), 0, stream, a);
   return hipGetLastError() == hipSuccess ? RA_OK : RA_ERR_HIP;
 }
 
