@@ -31,7 +31,13 @@
 namespace ra {
 namespace {
 
-constexpr int TN = 64;  // rows per LDS tile (keys in bwd_dq, queries in bwd_dkdv)
+constexpr int TN = 64;  // rows per LDS tile of queries in bwd_dkdv
+#ifndef RA_BWD_DQ_UNROLL
+#define RA_BWD_DQ_UNROLL 2  // 32-key halves of a dQ tile unrolled together
+#endif
+#ifndef RA_BWD_DQ_KT
+#define RA_BWD_DQ_KT 64  // keys per LDS tile in bwd_dq (128 measured equal)
+#endif
 #ifndef RA_BWD_DKDV_PIPE
 #define RA_BWD_DKDV_PIPE 1  // software-pipelined dK/dV tile
 #endif
@@ -46,10 +52,10 @@ __device__ __forceinline__ int usw(int r) {
 }
 
 // A TN x D bf16 tile in LDS (dense, swizzled), loaded with direct loads.
-template <int D, int NW>
+template <int D, int NW, int ROWS = TN>
 struct STile {
   static constexpr int RB = 2 * D;
-  static constexpr int BYTES = TN * RB;
+  static constexpr int BYTES = ROWS * RB;
   static constexpr int NBLK = BYTES / 1024;
   static constexpr int BPW = NBLK / NW;  // 1-KiB blocks per wave
   static_assert(NBLK % NW == 0, "tile must split evenly over the waves");
@@ -138,9 +144,10 @@ __global__ void __launch_bounds__(256) bwd_delta_kernel(BwdArgs a) {
 }
 
 // Next key tile in ring order (as in the forward).  t == P means done.
+template <int STEP>
 __device__ __forceinline__ void ring_next_bwd(const BwdArgs &a, bool causal, int64_t vis_lim,
                                               int &t, int &kb, int &kend, int &cend) {
-  kb += TN;
+  kb += STEP;
   while (kb >= kend) {
     ++t;
     if (t >= a.num_chunks) return;
@@ -154,7 +161,7 @@ __device__ __forceinline__ void ring_next_bwd(const BwdArgs &a, bool causal, int
 }
 
 // ---------------------------------------------------------------------------------
-// dQ: 8 waves x 32 query rows.  Per key tile (64 keys, two 32-key halves mt):
+// dQ: 8 waves x 32 query rows.  Per key tile (KT keys, 32-key blocks mt):
 //   S^T_mt = K_mt Q^T, dP^T_mt = V_mt dO^T         (16 + 16 MFMAs over the tile)
 //   P^T = exp2(c S^T - log2e lse), dS^T = P^T (dP^T - D)  -> bf16
 //   dQ^T += K^T_mt dS^T_mt                          (16 MFMAs over the tile)
@@ -163,7 +170,8 @@ template <int D, bool CAUSAL>
 __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 bwd_dq_kernel(BwdArgs a, int num_q_tiles) {
   constexpr int NW = 8, BM = 32 * NW;
-  using Tile = STile<D, NW>;
+  constexpr int KT = RA_BWD_DQ_KT;  // keys per LDS tile
+  using Tile = STile<D, NW, KT>;
   __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * 2 * Tile::BYTES];
   const uint32_t smem0 = lds_offset(smem);
 
@@ -214,7 +222,7 @@ bwd_dq_kernel(BwdArgs a, int num_q_tiles) {
 
   const int64_t vis_lim = a.q_offset + qlast - a.kv_offset + 1;
   int t = -1, kb = 0, kend = 0, cend = 0;
-  ring_next_bwd(a, CAUSAL, vis_lim, t, kb, kend, cend);
+  ring_next_bwd<KT>(a, CAUSAL, vis_lim, t, kb, kend, cend);
   if (t < a.num_chunks) {
     Tile::load(TL, kbase, a.k_ss, kb, a.Skv, smem0, wave);
     Tile::load(TL, vbase, a.v_ss, kb, a.Skv, smem0 + Tile::BYTES, wave);
@@ -225,7 +233,7 @@ bwd_dq_kernel(BwdArgs a, int num_q_tiles) {
   int cur = 0;
   while (t < a.num_chunks) {
     const int kb_cur = kb, cend_cur = cend;
-    ring_next_bwd(a, CAUSAL, vis_lim, t, kb, kend, cend);
+    ring_next_bwd<KT>(a, CAUSAL, vis_lim, t, kb, kend, cend);
     if (t < a.num_chunks) {
       const uint32_t nx = smem0 + (cur ^ 1) * 2 * Tile::BYTES;
       Tile::load(TL, kbase, a.k_ss, kb, a.Skv, nx, wave);
@@ -234,15 +242,15 @@ bwd_dq_kernel(BwdArgs a, int num_q_tiles) {
     const int64_t kpos0 = a.kv_offset + kb_cur;
     if (wave_active && !(CAUSAL && kpos0 > wpos_last)) {
       const uint32_t kt = smem0 + cur * 2 * Tile::BYTES, vt = kt + Tile::BYTES;
-      const int kvalid = min(TN, cend_cur - kb_cur);
-      const bool need_mask = (kvalid < TN) || (CAUSAL && kpos0 + kvalid - 1 > wpos_first);
+      const int kvalid = min(KT, cend_cur - kb_cur);
+      const bool need_mask = (kvalid < KT) || (CAUSAL && kpos0 + kvalid - 1 > wpos_first);
       int lim = kvalid;
       if (CAUSAL) {
         const int64_t vis = qpos - kpos0 + 1;
         lim = vis < (int64_t)lim ? (vis > 0 ? (int)vis : 0) : lim;
       }
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
+#pragma unroll RA_BWD_DQ_UNROLL
+      for (int mt = 0; mt < KT / 32; ++mt) {
         f32x16 s = f32x16{}, dp = f32x16{};
         const uint32_t ko = kt + (uint32_t)(mt * 32 * Tile::RB);
         const uint32_t vo = vt + (uint32_t)(mt * 32 * Tile::RB);

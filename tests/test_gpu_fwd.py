@@ -54,6 +54,8 @@ CASES = [
     ("bf16", 128, True, 1, 2, 2, 200, 200, 1, 0, 0, 100),        # rows with no visible key
     ("bf16", 128, True, 1, 2, 2, 1, 1, 1, 0, 0, 0),
     ("bf16", 128, True, 1, 2, 1, 130, 64, 1, 0, 70, 0),
+    ("bf16", 128, True, 1, 2, 1, 300, 800, 8, 5, 500, 0),        # 100-key chunks (< one tile)
+    ("bf16", 64, True, 2, 2, 2, 260, 520, 4, 3, 130, 0),         # D=64 causal ring share
     ("f32", 128, True, 1, 2, 2, 200, 200, 2, 1, 0, 0),
     ("f32", 64, False, 2, 2, 1, 150, 260, 4, 3, 0, 0),
     ("f32", 64, True, 1, 3, 3, 190, 380, 2, 1, 190, 0),
