@@ -263,6 +263,25 @@ def main():
     if moved:
         extra["permute_ms_per_step"] = float(np.mean(perm_ms))
         extra["permute_GBps"] = moved / (np.mean(perm_ms) * 1e-3) / 1e9
+        # cold-cache rate: a 1 GiB write evicts the 256 MB Infinity Cache before each pass
+        scratch = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        cold = []
+        for _ in range(5):
+            scratch.zero_()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            pre()
+            e1.record(stream)
+            scratch.zero_()
+            e2, e3 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e2.record(stream)
+            post()
+            e3.record(stream)
+            torch.cuda.synchronize()
+            cold.append(e0.elapsed_time(e1) + e2.elapsed_time(e3))
+        del scratch
+        extra["permute_cold_ms_per_step"] = float(np.median(cold))
+        extra["permute_cold_GBps"] = moved / (np.median(cold) * 1e-3) / 1e9
     extra["attn_fwd_ms"] = attn_avg
     extra["attn_fwd_ms_min"] = float(np.min(attn_ms))
     extra["attn_flops"] = flops

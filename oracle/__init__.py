@@ -23,12 +23,16 @@ give, in the order they give them.  Sources (page title, then the section):
   sections "FlashAttention 如何破局？不只是融合内核" (tiling with an online
   running max and normaliser; result identical to full attention) and
   "Ulysses：强互联下的高速通路" (sequence shards [B, S_local] x N, an
-  all-to-all before attention and one after that restores the order).
+  all-to-all before attention and one after that restores the order), and
+  "工程实践中的真实收益" (packing mixed sequences into one).
+* [P3] "ms-swift长文本训练秘诀：Ulysses并行技术解析" (bxzpzcl.cn), section
+  "5. 实战案例" -- short samples packed into a single 32K sequence.
 
 Module map:
 
 * ``attention``  -- full softmax attention (the definition), per-chunk
-  partials, the pairwise ring fold and the n-way LSE merge.
+  partials, the pairwise ring fold, the n-way LSE merge, and attention over
+  packed documents (each document its own problem).
 * ``permute``    -- the Ulysses sequence-shard <-> head-shard layout step.
 * ``backward``   -- the textbook softmax-attention gradient (the pages only
   say the backward recomputes from saved statistics; the formulas are not on
@@ -46,6 +50,7 @@ from .attention import (  # noqa: F401
     ring_attention,
     fold_pair,
     lse_merge,
+    varlen_attention,
 )
 from .permute import seq_to_head, head_to_seq  # noqa: F401
 from .backward import attention_bwd, attention_bwd_heads  # noqa: F401

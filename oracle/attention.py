@@ -250,3 +250,33 @@ def lse_merge(o_parts: Sequence[np.ndarray], lse_parts: Sequence[np.ndarray]):
     w = np.where(fin[None], np.exp(L - ref[None]), 0.0)
     o = (w[..., None] * O).sum(axis=0)
     return o, lse
+
+
+def varlen_attention(q, k, v, cu_seqlens: Sequence[int], *, causal: bool = False,
+                     scale: Optional[float] = None):
+    """Attention over packed documents -> (o, lse), fp64.
+
+    [P3] "ms-swift长文本训练秘诀：Ulysses并行技术解析", section "5. 实战案例": several short
+    samples are packed into one 32K sequence; [P4] section "工程实践中的真实收益" packs
+    mixed sequences the same way.  The pages do not state the mask; the reading taken
+    here is that every packed sample is its own attention problem: q, k, v are
+    [B, H, T, D] token streams, document d holds tokens cu_seqlens[d] .. cu_seqlens[d+1]-1,
+    and a query sees exactly the keys of its own document (the ones at or before it when
+    ``causal``).  Each document is therefore ``full_attention`` of its own slice, with
+    positions counted from the document's first token.  Tokens past the last document see
+    no key: o = 0, lse = -inf.
+    """
+    q, k, v = _as64(q), _as64(k), _as64(v)
+    B, Hq, T, D, Hkv, Tk = _shapes(q, k, v)
+    if Tk != T:
+        raise ValueError("packed q and k/v must hold the same tokens")
+    cu = [int(x) for x in cu_seqlens]
+    if not cu or cu[0] != 0 or any(b < a for a, b in zip(cu, cu[1:])) or cu[-1] > T:
+        raise ValueError("cu_seqlens must start at 0, not decrease and stay within T")
+    o = np.zeros((B, Hq, T, D))
+    lse = np.full((B, Hq, T), NEG_INF)
+    for a, b in zip(cu, cu[1:]):
+        if b > a:
+            o[:, :, a:b], lse[:, :, a:b] = full_attention(
+                q[:, :, a:b], k[:, :, a:b], v[:, :, a:b], causal=causal, scale=scale)
+    return o, lse

@@ -103,9 +103,24 @@ class Workload:
     ulysses_P: int = 0
     ulysses_rank: int = 0
     backward: bool = False
+    # packed documents (cu_seqlens drawn by draw_doc_offsets from this workload's seed)
+    packed_docs: bool = False
 
 
-# The five workloads.  Seeds are 1000 + workload number.
+def draw_doc_offsets(seed: int, total: int, median: int = 2048, sigma: float = 1.0,
+                     lo: int = 64, hi: int = 16384) -> list:
+    """Document boundaries of a packed token stream: lengths log-normal around `median`
+    (clipped to [lo, hi]) drawn until `total` tokens are covered, the last one cut to
+    fit.  Returns cu_seqlens = [0, end_0, end_1, ..., total]."""
+    rng = np.random.default_rng(np.random.PCG64(seed))
+    cu = [0]
+    while cu[-1] < total:
+        n = int(np.clip(round(float(rng.lognormal(np.log(median), sigma))), lo, hi))
+        cu.append(min(total, cu[-1] + n))
+    return cu
+
+
+# The workloads.  Seeds are 1000 + workload number.
 WORKLOADS: Dict[str, Workload] = {
     "ring_tiny_f32": Workload(
         name="ring_tiny_f32", dtype="f32",
@@ -123,6 +138,10 @@ WORKLOADS: Dict[str, Workload] = {
         name="qwen7b_ulysses4_rank0_32k", dtype="bf16",
         q_shape=(1, 7, 32768, 128), kv_shape=(1, 1, 32768, 128),
         causal=True, seed=1004, ulysses_P=4, ulysses_rank=0),
+    "qwen7b_packed_32k": Workload(
+        name="qwen7b_packed_32k", dtype="bf16",
+        q_shape=(1, 28, 32768, 128), kv_shape=(1, 4, 32768, 128),
+        causal=True, seed=1006, packed_docs=True),
     "llama7b_causal_bwd_16k": Workload(
         name="llama7b_causal_bwd_16k", dtype="bf16",
         q_shape=(1, 32, 16384, 128), kv_shape=(1, 32, 16384, 128),
