@@ -109,10 +109,18 @@ def cpu_baseline(w, budget_s: float = 15.0):
     starts = list(range(0, Sq, blk))
     rng.shuffle(starts)
     done_flops, rows, t0 = 0.0, 0, time.perf_counter()
+    cu = si.draw_doc_offsets(w.seed, Sq) if w.packed_docs else None
     for a in starts:
         qb = si.bf16_bits_to_f32(si.bf16_bits(
             rng.standard_normal((1, 1, blk, D), dtype=np.float32))).astype(np.float64)
-        if w.backward:  # all five products for the block's (query, key) pairs
+        if cu is not None:  # rows of one document against that document's keys
+            d = max(i for i in range(len(cu) - 1) if cu[i] <= a)
+            lo, hi = cu[d], cu[d + 1]
+            n = min(blk, hi - a)
+            kk, vv = k64[:, :, lo:hi], v64[:, :, lo:hi]
+            oracle.full_attention(qb[:, :, :n], kk, vv, causal=w.causal, q_offset=a - lo)
+            done_flops += attn_flops(1, 1, n, hi - lo, D, 1, w.causal, a - lo, 0)
+        elif w.backward:  # all five products for the block's (query, key) pairs
             nk = min(Skv, w.q_offset + a + blk - w.kv_offset) if w.causal else Skv
             oracle.attention_bwd(qb, k64[:, :, :nk], v64[:, :, :nk], qb, causal=w.causal,
                                  q_offset=w.q_offset + a, kv_offset=w.kv_offset)
@@ -131,7 +139,8 @@ def cpu_baseline(w, budget_s: float = 15.0):
         "value": done_flops / dt / 1e12, "unit": "TFLOP/s", "cores": blas_threads(),
         "kind": "oracle",
         "sample": f"{rows} query rows ({rows // blk} blocks of {blk}, random positions) of "
-                  f"one head against its {'causal ' if w.causal else ''}{Skv}-key context, "
+                  f"one head against its {'causal ' if w.causal else ''}"
+                  f"{'own document' if cu is not None else str(Skv) + '-key context'}, "
                   f"{'backward' if w.backward else 'forward'} oracle, fp64 NumPy, {dt:.1f} s",
     }
 
@@ -191,6 +200,25 @@ def main():
 
         def post():
             ra.ulysses_permute(o, P, r, 1, out=o_seq)
+    elif w.packed_docs:
+        q, k, v = (to_dev(x) for x in si.draw_qkv(w.seed, w.q_shape, w.kv_shape, w.dtype))
+        cu = si.draw_doc_offsets(w.seed, Sq)
+        cud = torch.tensor(cu, dtype=torch.int32, device=dev)
+        o = torch.empty_like(q)
+        lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+        flops = sum(attn_flops(B, Hq, b - a, b - a, D, 1, w.causal) for a, b in zip(cu, cu[1:]))
+        moved = 0
+        extra["kernel"] = "attn_fwd_varlen"
+        extra["documents"] = len(cu) - 1
+
+        def pre():
+            pass
+
+        def attn():
+            ra.attn_fwd_varlen(q, k, v, cud, causal=w.causal, out=o, lse=lse)
+
+        def post():
+            pass
     elif w.backward:
         q, k, v, do = (to_dev(x) for x in si.draw_qkv(w.seed, w.q_shape, w.kv_shape, w.dtype,
                                                       with_dout=True))

@@ -4,6 +4,7 @@
  * Sources (page title, host), cited by section below:
  *   [P1] "ms-swift支持Ulysses与Ring-Attention降低长文本显存占用" (bjdmk.com.cn)
  *   [P2] "Ulysses与Ring-Attention序列并行技术详解" (cnvsn.com)
+ *   [P3] "ms-swift长文本训练秘诀：Ulysses并行技术解析" (bxzpzcl.cn)
  *   [P4] "ms-swift集成FlashAttention 2/3，长文本训练更高效" (maplevalley.com.cn)
  *
  * General rules for every entry point
@@ -36,6 +37,7 @@ extern "C" {
 
 #define RA_VERSION 100 /* 0.1.0 */
 #define RA_MAX_MERGE_PARTS 64
+#define RA_MAX_DOCS (1 << 24)
 
 typedef enum {
   RA_OK = 0,
@@ -103,6 +105,34 @@ int ra_attn_fwd(const ra_tensor *q, const ra_tensor *k, const ra_tensor *v,
                 const ra_attn_params *p, ra_tensor *o, ra_tensor *lse, ra_stream stream);
 int ra_attn_fwd_validate(const ra_tensor *q, const ra_tensor *k, const ra_tensor *v,
                          const ra_attn_params *p, const ra_tensor *o, const ra_tensor *lse);
+
+/*
+ * ra_attn_fwd_varlen -- ra_attn_fwd over packed documents: several sequences laid end
+ * to end in one token stream, each its own attention problem.
+ *
+ * [P3] "ms-swift长文本训练秘诀：Ulysses并行技术解析", section "5. 实战案例" (short samples
+ * packed into one 32K sequence) and [P4] section "工程实践中的真实收益" (mixed sequences
+ * packed the same way).  The pages do not state the mask; here a query sees exactly the
+ * keys of its own document (with p->causal, those at or before it).
+ *
+ * q   [B, Hq, T, D]  RA_BF16; k, v [B, Hkv, T, D] (the same T tokens); D 64 or 128
+ * cu_seqlens  DEVICE pointer to n_docs + 1 int32 (4-byte aligned), read by the kernel:
+ *             document d holds tokens cu_seqlens[d] .. cu_seqlens[d+1] - 1; the same
+ *             packing for every batch entry.  Must start at 0, not decrease and not
+ *             exceed T; tokens at or past cu_seqlens[n_docs] see no key (o = 0,
+ *             lse = -inf).  Values breaking these rules give unspecified results but
+ *             no access outside q, k, v, o, lse and the n_docs + 1 entries.
+ * 1 <= n_docs <= RA_MAX_DOCS.  p: causal and scale apply; num_chunks must be 1 and
+ * start_chunk, q_offset, kv_offset 0 (else RA_ERR_RANGE).  o: bf16 or RA_F32; lse fp32.
+ * The caller owns every buffer; nothing is allocated; work is enqueued on `stream`.
+ */
+int ra_attn_fwd_varlen(const ra_tensor *q, const ra_tensor *k, const ra_tensor *v,
+                       const int32_t *cu_seqlens, int32_t n_docs, const ra_attn_params *p,
+                       ra_tensor *o, ra_tensor *lse, ra_stream stream);
+int ra_attn_fwd_varlen_validate(const ra_tensor *q, const ra_tensor *k, const ra_tensor *v,
+                                const int32_t *cu_seqlens, int32_t n_docs,
+                                const ra_attn_params *p, const ra_tensor *o,
+                                const ra_tensor *lse);
 
 /*
  * ra_lse_merge -- combine n partial results (o_i, lse_i) of the same queries over

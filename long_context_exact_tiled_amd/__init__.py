@@ -26,6 +26,7 @@ __all__ = [
     "attn_fwd", "lse_merge", "ulysses_permute", "attn_bwd", "attn_bwd_workspace_size",
     "attn_fwd_validate", "lse_merge_validate", "ulysses_permute_validate", "attn_bwd_validate",
     "status_string", "version", "lib", "LIB_PATH", "RaError", "STATUS",
+    "attn_fwd_varlen", "attn_fwd_varlen_validate",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libra.so")
@@ -77,6 +78,8 @@ def lib() -> ctypes.CDLL:
         sigs = {
             "ra_attn_fwd": [T, T, T, PP, T, T, vp],
             "ra_attn_fwd_validate": [T, T, T, PP, T, T],
+            "ra_attn_fwd_varlen": [T, T, T, vp, i32, PP, T, T, vp],
+            "ra_attn_fwd_varlen_validate": [T, T, T, vp, i32, PP, T, T],
             "ra_lse_merge": [i32, T, T, T, T, vp],
             "ra_lse_merge_validate": [i32, T, T, T, T],
             "ra_ulysses_permute": [T, T, i32, i32, i32, vp],
@@ -173,6 +176,40 @@ def attn_fwd_validate(q, k, v, out, lse, *, causal=False, num_chunks=1, start_ch
     p = _params(causal, num_chunks, start_chunk, q_offset, kv_offset, scale)
     return int(lib().ra_attn_fwd_validate(desc(q), desc(k), desc(v), ctypes.byref(p),
                                           desc(out), desc(lse)))
+
+
+def _cu_arg(cu_seqlens: torch.Tensor):
+    if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1 or not cu_seqlens.is_contiguous():
+        raise RaError(-2, "RA_ERR_DTYPE: cu_seqlens must be a contiguous 1-D int32 tensor")
+    if cu_seqlens.numel() < 2:
+        raise RaError(-6, "RA_ERR_RANGE: cu_seqlens needs at least two entries")
+    return ctypes.c_void_p(cu_seqlens.data_ptr()), int(cu_seqlens.numel() - 1)
+
+
+def attn_fwd_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens: torch.Tensor,
+                    *, causal: bool = False, scale: Optional[float] = None,
+                    out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                    out_dtype: Optional[torch.dtype] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Attention over packed documents: q [B,Hq,T,D], k, v [B,Hkv,T,D]; document d holds
+    tokens cu_seqlens[d] .. cu_seqlens[d+1]-1 (a device int32 tensor) and each query sees
+    only its own document's keys.  Returns (o, lse)."""
+    if out is None:
+        out = torch.empty(q.shape, dtype=out_dtype or q.dtype, device=q.device)
+    if lse is None:
+        lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+    cu, n = _cu_arg(cu_seqlens)
+    p = _params(causal, 1, 0, 0, 0, scale)
+    _check(lib().ra_attn_fwd_varlen(desc(q), desc(k), desc(v), cu, n, ctypes.byref(p),
+                                    desc(out), desc(lse), _stream(q)))
+    return out, lse
+
+
+def attn_fwd_varlen_validate(q, k, v, cu_seqlens, out, lse, *, causal=False, scale=None) -> int:
+    """Host-side argument check of attn_fwd_varlen (no device access); returns the status."""
+    cu, n = _cu_arg(cu_seqlens)
+    p = _params(causal, 1, 0, 0, 0, scale)
+    return int(lib().ra_attn_fwd_varlen_validate(desc(q), desc(k), desc(v), cu, n,
+                                                 ctypes.byref(p), desc(out), desc(lse)))
 
 
 def _parts_arrays(o_parts, lse_parts):

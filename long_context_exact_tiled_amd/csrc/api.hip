@@ -259,6 +259,54 @@ int ra_attn_fwd(const ra_tensor *q, const ra_tensor *k, const ra_tensor *v,
   return launch_attn_fwd(a, q->dtype, (int)q->shape[3], p->causal, (hipStream_t)stream);
 }
 
+namespace {
+// Packed documents: q and k/v hold the same T tokens; one chunk, no offsets; bf16.
+int varlen_validate(const ra_tensor *q, const ra_tensor *k, const ra_tensor *v,
+                    const int32_t *cu_seqlens, int32_t n_docs, const ra_attn_params *p,
+                    const ra_tensor *o, const ra_tensor *lse) {
+  RA_TRY(fwd_validate(q, k, v, p, o, lse));
+  if (q->shape[2] != k->shape[2]) return RA_ERR_SHAPE;
+  if (p->num_chunks != 1 || p->start_chunk != 0 || p->q_offset != 0 || p->kv_offset != 0)
+    return RA_ERR_RANGE;
+  if (n_docs < 1 || n_docs > RA_MAX_DOCS) return RA_ERR_RANGE;
+  if (!cu_seqlens) return RA_ERR_NULL;
+  if (((uintptr_t)cu_seqlens) % 4) return RA_ERR_ALIGN;
+  if (q->dtype != RA_BF16) return RA_ERR_UNSUPPORTED;
+  return RA_OK;
+}
+}  // namespace
+
+int ra_attn_fwd_varlen_validate(const ra_tensor *q, const ra_tensor *k, const ra_tensor *v,
+                                const int32_t *cu_seqlens, int32_t n_docs,
+                                const ra_attn_params *p, const ra_tensor *o,
+                                const ra_tensor *lse) {
+  return varlen_validate(q, k, v, cu_seqlens, n_docs, p, o, lse);
+}
+
+int ra_attn_fwd_varlen(const ra_tensor *q, const ra_tensor *k, const ra_tensor *v,
+                       const int32_t *cu_seqlens, int32_t n_docs, const ra_attn_params *p,
+                       ra_tensor *o, ra_tensor *lse, ra_stream stream) {
+  RA_TRY(varlen_validate(q, k, v, cu_seqlens, n_docs, p, o, lse));
+  if (numel(q) == 0) return RA_OK;
+  FwdArgs a{};
+  a.q = q->data; a.k = k->data; a.v = v->data; a.o = o->data; a.lse = (float *)lse->data;
+  a.q_sb = q->stride[0]; a.q_sh = q->stride[1]; a.q_ss = q->stride[2];
+  a.k_sb = k->stride[0]; a.k_sh = k->stride[1]; a.k_ss = k->stride[2];
+  a.v_sb = v->stride[0]; a.v_sh = v->stride[1]; a.v_ss = v->stride[2];
+  a.o_sb = o->stride[0]; a.o_sh = o->stride[1]; a.o_ss = o->stride[2];
+  a.l_sb = lse->stride[0]; a.l_sh = lse->stride[1];
+  a.B = (int32_t)q->shape[0]; a.Hq = (int32_t)q->shape[1]; a.Sq = (int32_t)q->shape[2];
+  a.Hkv = (int32_t)k->shape[1]; a.Skv = (int32_t)k->shape[2];
+  a.group = a.Hq / a.Hkv;
+  a.num_chunks = 1; a.start_chunk = 0; a.chunk_len = a.Skv;
+  a.q_offset = 0; a.kv_offset = 0;
+  a.scale_log2 = effective_scale(p, q->shape[3]) * kLog2eHost;
+  a.o_is_f32 = o->dtype == RA_F32;
+  a.cu = cu_seqlens;
+  a.n_docs = n_docs;
+  return launch_attn_fwd_varlen(a, (int)q->shape[3], p->causal, (hipStream_t)stream);
+}
+
 int ra_lse_merge_validate(int32_t n, const ra_tensor *o_parts, const ra_tensor *lse_parts,
                           const ra_tensor *o, const ra_tensor *lse) {
   return merge_validate(n, o_parts, lse_parts, o, lse);

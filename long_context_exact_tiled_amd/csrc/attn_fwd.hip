@@ -570,6 +570,25 @@ __device__ __forceinline__ void ring_next(const FwdArgs &a, bool causal, int64_t
   }
 }
 
+// Document of token t in a packed stream: [ds, de) with cu[d] <= t < cu[d+1] (the last
+// such d; cu[0] is 0).  A token past the last document, or offsets that break the rules,
+// give the empty range [t+1, t+1).  At most ceil(log2(n+1)) probes, all inside cu[0..n].
+__device__ __forceinline__ void doc_bounds(const int32_t *cu, int n, int t, int T, int &ds,
+                                           int &de) {
+  int lo = 0, hi = n;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (cu[mid] <= t) lo = mid; else hi = mid - 1;
+  }
+  ds = de = t + 1;
+  if (lo >= n) return;
+  const int a0 = min(max(cu[lo], 0), T), a1 = min(max(cu[lo + 1], a0), T);
+  if (a0 <= t && t < a1) {
+    ds = a0;
+    de = a1;
+  }
+}
+
 // ---------------------------------------------------------------------------------
 // The kernel.
 // ---------------------------------------------------------------------------------
@@ -801,7 +820,7 @@ attn_fwd_kernel(FwdArgs a) {
 // Kernel for the bf16 direct path: double-buffered LDS, the next tile's direct loads in
 // flight under the current tile's math.
 // ---------------------------------------------------------------------------------
-template <int D, bool CAUSAL, int NW, int KN>
+template <int D, bool CAUSAL, int NW, int KN, bool VARLEN>
 __global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 attn_fwd_direct_kernel(FwdArgs a) {
   using Path = Bf16DirectPath<D, NW, KN>;
@@ -854,6 +873,24 @@ attn_fwd_direct_kernel(FwdArgs a) {
   const int64_t vis_lim = a.q_offset + qlast - a.kv_offset + 1;
   int t = -1, kb = 0, kend = 0, cend = 0;
   ring_next<KN>(a, CAUSAL, vis_lim, t, kb, kend, cend);
+  // Packed documents: this lane's row sees keys [ds, de) (causal: [ds, row]); the wave's
+  // first and last rows bound the wave's keys; the block walks from the tile holding its
+  // first row's document start.
+  int ds = 0, de = 0, w_ds_first = 0, w_ds_last = 0, w_de_first = 0, w_de_last = 0;
+  if (VARLEN) {
+    doc_bounds(a.cu, a.n_docs, min(qrow, a.Sq - 1), a.Skv, ds, de);
+    w_ds_first = __builtin_amdgcn_readlane(ds, 0);
+    w_ds_last = __builtin_amdgcn_readlane(ds, 31);
+    w_de_first = __builtin_amdgcn_readlane(de, 0);
+    w_de_last = __builtin_amdgcn_readlane(de, 31);
+    int b_ds, b_de, l_ds, l_de;
+    doc_bounds(a.cu, a.n_docs, q0, a.Skv, b_ds, b_de);
+    doc_bounds(a.cu, a.n_docs, qlast, a.Skv, l_ds, l_de);
+    b_ds = __builtin_amdgcn_readfirstlane(min(b_ds, qlast));
+    kb = (b_ds / KN) * KN;
+    if (!CAUSAL) kend = __builtin_amdgcn_readfirstlane(max(l_de, l_ds));
+    if (kb >= kend) t = a.num_chunks;
+  }
   const uint32_t smem0 = lds_offset(smem);
   if (t < a.num_chunks) Path::load_tile(L, a, kbase, vbase, kb, smem0, wave);
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): Q and the first tile have landed
@@ -870,25 +907,35 @@ attn_fwd_direct_kernel(FwdArgs a) {
 #endif
 
     const int64_t kpos0 = a.kv_offset + kb_cur;
-    if (wave_active && !(CAUSAL && kpos0 > wpos_last)) {
+    const bool doc_skip =
+        VARLEN && (kb_cur + KN <= w_ds_first || (!CAUSAL && kb_cur >= w_de_last));
+    if (wave_active && !(CAUSAL && kpos0 > wpos_last) && !doc_skip) {
       const uint32_t slot = (uint32_t)(cur * Path::BUF_BYTES);
       f32x16 s[NMT];
       Path::qk(s, qf, L.ka + slot);
       const int kvalid = min(KN, cend_cur - kb_cur);
-      const bool need_mask = (kvalid < KN) || (CAUSAL && kpos0 + kvalid - 1 > wpos_first);
+      const bool need_mask =
+          (kvalid < KN) || (CAUSAL && kpos0 + kvalid - 1 > wpos_first) ||
+          (VARLEN && (kb_cur < w_ds_last || (!CAUSAL && kb_cur + kvalid > w_de_first)));
       if (need_mask) {
-        int lim = kvalid;  // keys kk < lim are visible to this lane's row
+        int lim = kvalid;  // keys lo <= kk < lim are visible to this lane's row
         if (CAUSAL) {
           const int64_t vis = qpos - kpos0 + 1;
           lim = vis < (int64_t)lim ? (vis > 0 ? (int)vis : 0) : lim;
         }
+        int lo = 0;
+        if (VARLEN) {
+          if (!CAUSAL) lim = min(lim, de - kb_cur);
+          lo = ds - kb_cur;
+        }
         lim -= 4 * h;
+        lo -= 4 * h;
 #pragma unroll
         for (int mt = 0; mt < NMT; ++mt)
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
             const int kk = 32 * mt + (i >> 2) * 8 + (i & 3);
-            s[mt][i] = kk < lim ? s[mt][i] : -INFINITY;
+            s[mt][i] = (kk < lim && (!VARLEN || kk >= lo)) ? s[mt][i] : -INFINITY;
           }
       }
       float mx = fmaxf(fmaxf(s[0][0], s[0][1]), s[0][2]);
@@ -949,7 +996,7 @@ attn_fwd_direct_kernel(FwdArgs a) {
   }
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool VARLEN = false>
 int launch_direct(const FwdArgs &args, hipStream_t stream) {
   FwdArgs a = args;
   constexpr int NW = RA_FWD_DIRECT_WAVES;
@@ -957,7 +1004,7 @@ int launch_direct(const FwdArgs &args, hipStream_t stream) {
   const int64_t blocks = (int64_t)a.num_q_tiles * a.Hq * a.B;
   if (blocks <= 0) return RA_OK;
   constexpr int KN = RA_FWD_KN;
-  hipLaunchKernelGGL((attn_fwd_direct_kernel<D, CAUSAL, NW, KN>), dim3((unsigned)blocks),
+  hipLaunchKernelGGL((attn_fwd_direct_kernel<D, CAUSAL, NW, KN, VARLEN>), dim3((unsigned)blocks),
                      dim3(64 * NW), 0, stream, a);
   return hipGetLastError() == hipSuccess ? RA_OK : RA_ERR_HIP;
 }
@@ -991,6 +1038,14 @@ int launch_attn_fwd(const FwdArgs &a, int dtype, int D, int causal, hipStream_t 
     if (D == 64) return causal ? launch_one<F32Path<64>, 64, true>(a, stream)
                                : launch_one<F32Path<64>, 64, false>(a, stream);
   }
+  return RA_ERR_UNSUPPORTED;
+}
+
+int launch_attn_fwd_varlen(const FwdArgs &a, int D, int causal, hipStream_t stream) {
+  if (D == 128)
+    return causal ? launch_direct<128, true, true>(a, stream) : launch_direct<128, false, true>(a, stream);
+  if (D == 64)
+    return causal ? launch_direct<64, true, true>(a, stream) : launch_direct<64, false, true>(a, stream);
   return RA_ERR_UNSUPPORTED;
 }
 

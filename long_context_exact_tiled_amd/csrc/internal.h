@@ -32,9 +32,13 @@ struct FwdArgs {
   int64_t q_offset, kv_offset;
   float scale_log2;     // scale * log2(e)
   int32_t o_is_f32;     // output dtype: 1 = fp32, 0 = same as inputs (bf16 path)
+  // packed documents (attn_fwd_varlen only): document d holds tokens cu[d] .. cu[d+1]-1
+  const int32_t *cu;
+  int32_t n_docs;
 };
 
 int launch_attn_fwd(const FwdArgs &a, int dtype, int D, int causal, hipStream_t stream);
+int launch_attn_fwd_varlen(const FwdArgs &a, int D, int causal, hipStream_t stream);
 
 struct MergeArgs {
   const void *o_parts[RA_MAX_MERGE_PARTS];

@@ -89,6 +89,26 @@ def test_fwd_validation(ra):
     assert _fwd(ra, q, _t((1, 2, 0, 128)), _t((1, 2, 0, 128))) == "RA_OK"
 
 
+def test_varlen_validation(ra):
+    q, k, v = _t((1, 4, 64, 128)), _t((1, 2, 64, 128)), _t((1, 2, 64, 128))
+    cu = torch.tensor([0, 10, 64], dtype=torch.int32)
+
+    def f(q=q, k=k, v=v, cu=cu, o=None, lse=None, **kw):
+        o = torch.zeros(q.shape, dtype=q.dtype) if o is None else o
+        lse = torch.zeros(q.shape[:3], dtype=torch.float32) if lse is None else lse
+        return ra.STATUS[ra.attn_fwd_varlen_validate(q, k, v, cu, o, lse, **kw)]
+
+    assert f() == "RA_OK"
+    assert f(causal=True) == "RA_OK"
+    assert f(o=torch.zeros(q.shape)) == "RA_OK"  # fp32 output
+    assert f(k=_t((1, 2, 32, 128)), v=_t((1, 2, 32, 128))) == "RA_ERR_SHAPE"  # T differs
+    assert f(q=q.float(), k=k.float(), v=v.float()) == "RA_ERR_UNSUPPORTED"  # bf16 only
+    with pytest.raises(ra.RaError):
+        f(cu=torch.tensor([0], dtype=torch.int32))
+    with pytest.raises(ra.RaError):
+        f(cu=torch.tensor([0, 64], dtype=torch.int64))
+
+
 def test_fwd_rejects_before_launch(ra):
     """A failing call returns its code without touching the device (CPU tensors here)."""
     q, k = _t((1, 4, 64, 128)), _t((1, 3, 64, 128))

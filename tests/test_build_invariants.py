@@ -43,7 +43,8 @@ def test_m0_only_in_dma_sequences(asm):
         lines = [l.strip() for l in text.splitlines()]
         for i, l in enumerate(lines):
             if re.search(r"\bm0\b", l) and not l.startswith(";"):
-                assert l.startswith("s_mov_b32 m0, s"), (src, l)
+                # the DMA sequence's scalar operand: any SGPR, vcc_lo/vcc_hi included
+                assert re.match(r"s_mov_b32 m0, (s\d+|vcc_lo|vcc_hi)$", l), (src, l)
                 nxt = [x for x in lines[i + 1:i + 4] if x and not x.startswith(";")]
                 assert nxt[0].startswith("s_nop") and nxt[1].startswith("global_load_lds_dwordx4"), \
                     (src, l, nxt)
