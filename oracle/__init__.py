@@ -53,4 +53,4 @@ from .attention import (  # noqa: F401
     varlen_attention,
 )
 from .permute import seq_to_head, head_to_seq  # noqa: F401
-from .backward import attention_bwd, attention_bwd_heads  # noqa: F401
+from .backward import attention_bwd, attention_bwd_heads, varlen_attention_bwd  # noqa: F401

@@ -25,7 +25,7 @@ invariants (sum_j dS_ij = 0, sum_j dK_j = 0, sum_j dV_j = sum_i dO_i).
 from __future__ import annotations
 
 import math
-from typing import Iterable, Optional, Tuple
+from typing import Iterable, Optional, Sequence, Tuple
 
 import numpy as np
 
@@ -99,3 +99,27 @@ def attention_bwd_heads(q, k, v, do, kv_heads: Iterable[Tuple[int, int]], *,
                                           causal, row_block)
         out[(b, g)] = (np.stack([dq_heads[h] for h in sorted(dq_heads)]), dk_g, dv_g)
     return out
+
+
+def varlen_attention_bwd(q, k, v, do, cu_seqlens: Sequence[int], *, causal: bool = False,
+                         scale: Optional[float] = None):
+    """(dq, dk, dv) of L = sum(dO * varlen_attention(q, k, v, cu_seqlens)), fp64.
+
+    Each packed document is its own attention problem (the reading of the pages'
+    packing taken in ``attention.varlen_attention``), so its gradients are
+    ``attention_bwd`` of its own slice; tokens in no document get zero gradients.
+    """
+    q, k, v, do = _as64(q), _as64(k), _as64(v), _as64(do)
+    B, Hq, T, D, Hkv, Tk = _shapes(q, k, v)
+    if Tk != T or do.shape != q.shape:
+        raise ValueError("packed q, k, v, dO must hold the same tokens")
+    cu = [int(x) for x in cu_seqlens]
+    if not cu or cu[0] != 0 or any(b < a for a, b in zip(cu, cu[1:])) or cu[-1] > T:
+        raise ValueError("cu_seqlens must start at 0, not decrease and stay within T")
+    dq, dk, dv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+    for a, b in zip(cu, cu[1:]):
+        if b > a:
+            dq[:, :, a:b], dk[:, :, a:b], dv[:, :, a:b] = attention_bwd(
+                q[:, :, a:b], k[:, :, a:b], v[:, :, a:b], do[:, :, a:b], causal=causal,
+                scale=scale)
+    return dq, dk, dv

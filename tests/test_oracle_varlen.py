@@ -103,3 +103,44 @@ def test_bad_offsets_rejected():
     for cu in ([1, 8], [0, 5, 3], [0, 9], []):
         with pytest.raises(ValueError):
             oracle.varlen_attention(q, q, q, cu)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_finite_differences(causal):
+    """Gradients of L = sum(dO * o) against central differences of the packed forward
+    (itself pinned by the brute force above); cu has an empty document and tokens past
+    the last one (their gradients must be 0)."""
+    cu = [0, 3, 3, 7, 8]
+    T = 10
+    q, k, v = _rand((1, 2, T, 3), 71), _rand((1, 1, T, 3), 72), _rand((1, 1, T, 3), 73)
+    do = _rand((1, 2, T, 3), 74)
+    dq, dk, dv = oracle.varlen_attention_bwd(q, k, v, do, cu, causal=causal, scale=0.6)
+
+    def loss(qq, kk, vv):
+        o, _ = oracle.varlen_attention(qq, kk, vv, cu, causal=causal, scale=0.6)
+        return float((do * o).sum())
+
+    h = 1e-6
+    for name, x, g in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+        fd = np.zeros_like(x)
+        for idx in np.ndindex(x.shape):
+            args = {"q": q, "k": k, "v": v}
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += h
+            xm[idx] -= h
+            args[name] = xp
+            lp = loss(args["q"], args["k"], args["v"])
+            args[name] = xm
+            lm = loss(args["q"], args["k"], args["v"])
+            fd[idx] = (lp - lm) / (2 * h)
+        err = np.linalg.norm(fd - g) / max(np.linalg.norm(g), 1e-30)
+        assert err <= 1e-6, (name, err)
+        assert np.all(g[:, :, 8:] == 0.0), name  # tokens in no document
+
+
+def test_backward_one_document_is_attention_bwd():
+    q, k, v, do = (_rand((1, 2, 30, 4), s) for s in (81, 82, 83, 84))
+    a = oracle.varlen_attention_bwd(q, k, v, do, [0, 30], causal=True)
+    b = oracle.attention_bwd(q, k, v, do, causal=True)
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y)
