@@ -118,8 +118,14 @@ def cpu_baseline(w, budget_s: float = 15.0):
             lo, hi = cu[d], cu[d + 1]
             n = min(blk, hi - a)
             kk, vv = k64[:, :, lo:hi], v64[:, :, lo:hi]
-            oracle.full_attention(qb[:, :, :n], kk, vv, causal=w.causal, q_offset=a - lo)
-            done_flops += attn_flops(1, 1, n, hi - lo, D, 1, w.causal, a - lo, 0)
+            if w.backward:
+                nk = min(hi - lo, a - lo + n) if w.causal else hi - lo
+                oracle.attention_bwd(qb[:, :, :n], kk[:, :, :nk], vv[:, :, :nk], qb[:, :, :n],
+                                     causal=w.causal, q_offset=a - lo)
+                done_flops += 2.5 * attn_flops(1, 1, n, hi - lo, D, 1, w.causal, a - lo, 0)
+            else:
+                oracle.full_attention(qb[:, :, :n], kk, vv, causal=w.causal, q_offset=a - lo)
+                done_flops += attn_flops(1, 1, n, hi - lo, D, 1, w.causal, a - lo, 0)
         elif w.backward:  # all five products for the block's (query, key) pairs
             nk = min(Skv, w.q_offset + a + blk - w.kv_offset) if w.causal else Skv
             oracle.attention_bwd(qb, k64[:, :, :nk], v64[:, :, :nk], qb, causal=w.causal,
@@ -208,14 +214,27 @@ def main():
         lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
         flops = sum(attn_flops(B, Hq, b - a, b - a, D, 1, w.causal) for a, b in zip(cu, cu[1:]))
         moved = 0
-        extra["kernel"] = "attn_fwd_varlen"
         extra["documents"] = len(cu) - 1
+        if w.backward:
+            ra.attn_fwd_varlen(q, k, v, cud, causal=w.causal, out=o, lse=lse)
+            do = to_dev(si.draw_qkv(w.seed, w.q_shape, w.kv_shape, w.dtype, with_dout=True)[3])
+            dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+            ws = torch.empty(max(ra.attn_bwd_workspace_size(q, k, causal=w.causal), 256),
+                             dtype=torch.uint8, device=dev)
+            flops *= 2.5
+            extra["kernel"] = "attn_bwd_varlen (delta + dkdv + dq)"
+
+            def attn():
+                ra.attn_bwd_varlen(q, k, v, o, do, lse, cud, causal=w.causal, dq=dq, dk=dk,
+                                   dv=dv, workspace=ws)
+        else:
+            extra["kernel"] = "attn_fwd_varlen"
+
+            def attn():
+                ra.attn_fwd_varlen(q, k, v, cud, causal=w.causal, out=o, lse=lse)
 
         def pre():
             pass
-
-        def attn():
-            ra.attn_fwd_varlen(q, k, v, cud, causal=w.causal, out=o, lse=lse)
 
         def post():
             pass

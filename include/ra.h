@@ -208,6 +208,30 @@ int ra_attn_bwd_validate(const ra_tensor *q, const ra_tensor *k, const ra_tensor
 /* Bytes of workspace ra_attn_bwd needs for these shapes (0 if the shapes are invalid). */
 size_t ra_attn_bwd_workspace_size(const ra_tensor *q, const ra_tensor *k, const ra_attn_params *p);
 
+/*
+ * ra_attn_bwd_varlen -- ra_attn_bwd over packed documents (the gradients of
+ * ra_attn_fwd_varlen): each document's queries, keys and values get the gradients of
+ * that document's own attention problem; tokens in no document get zero gradients.
+ *
+ * Same sources and reading as ra_attn_fwd_varlen ([P3] section "5. 实战案例", [P4]
+ * section "工程实践中的真实收益"; the backward formulas are the textbook softmax
+ * gradient, recomputing P from lse).  Tensors, dtypes, workspace and errors as for
+ * ra_attn_bwd (bf16, D 64 or 128, workspace from ra_attn_bwd_workspace_size with
+ * num_chunks = 1); q, k, v, o, dout hold the same T tokens; cu_seqlens, n_docs and the
+ * params restrictions as for ra_attn_fwd_varlen; o and lse must come from
+ * ra_attn_fwd_varlen with the same cu_seqlens.
+ */
+int ra_attn_bwd_varlen(const ra_tensor *q, const ra_tensor *k, const ra_tensor *v,
+                       const ra_tensor *o, const ra_tensor *dout, const ra_tensor *lse,
+                       const int32_t *cu_seqlens, int32_t n_docs, const ra_attn_params *p,
+                       ra_tensor *dq, ra_tensor *dk, ra_tensor *dv, void *workspace,
+                       size_t workspace_bytes, ra_stream stream);
+int ra_attn_bwd_varlen_validate(const ra_tensor *q, const ra_tensor *k, const ra_tensor *v,
+                                const ra_tensor *o, const ra_tensor *dout, const ra_tensor *lse,
+                                const int32_t *cu_seqlens, int32_t n_docs,
+                                const ra_attn_params *p, const ra_tensor *dq, const ra_tensor *dk,
+                                const ra_tensor *dv);
+
 /* Static message for a status code (never NULL). */
 const char *ra_status_string(int status);
 /* RA_VERSION of the loaded library. */

@@ -26,7 +26,7 @@ __all__ = [
     "attn_fwd", "lse_merge", "ulysses_permute", "attn_bwd", "attn_bwd_workspace_size",
     "attn_fwd_validate", "lse_merge_validate", "ulysses_permute_validate", "attn_bwd_validate",
     "status_string", "version", "lib", "LIB_PATH", "RaError", "STATUS",
-    "attn_fwd_varlen", "attn_fwd_varlen_validate",
+    "attn_fwd_varlen", "attn_fwd_varlen_validate", "attn_bwd_varlen", "attn_bwd_varlen_validate",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libra.so")
@@ -86,6 +86,8 @@ def lib() -> ctypes.CDLL:
             "ra_ulysses_permute_validate": [T, T, i32, i32, i32],
             "ra_attn_bwd": [T, T, T, T, T, T, PP, T, T, T, vp, sz, vp],
             "ra_attn_bwd_validate": [T, T, T, T, T, T, PP, T, T, T],
+            "ra_attn_bwd_varlen": [T, T, T, T, T, T, vp, i32, PP, T, T, T, vp, sz, vp],
+            "ra_attn_bwd_varlen_validate": [T, T, T, T, T, T, vp, i32, PP, T, T, T],
             "ra_attn_bwd_workspace_size": [T, T, PP],
             "ra_status_string": [ctypes.c_int],
             "ra_version": [],
@@ -285,6 +287,33 @@ def attn_bwd(q, k, v, o, dout, lse, *, causal=False, num_chunks=1, start_chunk=0
                              ctypes.byref(p), desc(dq), desc(dk), desc(dv),
                              workspace.data_ptr(), workspace.numel(), _stream(q)))
     return dq, dk, dv
+
+
+def attn_bwd_varlen(q, k, v, o, dout, lse, cu_seqlens, *, causal=False, scale=None, dq=None,
+                    dk=None, dv=None, workspace: Optional[torch.Tensor] = None):
+    """Gradients of attn_fwd_varlen (packed documents, cu_seqlens a device int32 tensor)."""
+    p = _params(causal, 1, 0, 0, 0, scale)
+    cu, n = _cu_arg(cu_seqlens)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    need = int(lib().ra_attn_bwd_workspace_size(desc(q), desc(k), ctypes.byref(p)))
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    _check(lib().ra_attn_bwd_varlen(desc(q), desc(k), desc(v), desc(o), desc(dout), desc(lse),
+                                    cu, n, ctypes.byref(p), desc(dq), desc(dk), desc(dv),
+                                    workspace.data_ptr(), workspace.numel(), _stream(q)))
+    return dq, dk, dv
+
+
+def attn_bwd_varlen_validate(q, k, v, o, dout, lse, cu_seqlens, dq, dk, dv, *, causal=False,
+                             scale=None) -> int:
+    """Host-side argument check of attn_bwd_varlen (no device access); returns the status."""
+    p = _params(causal, 1, 0, 0, 0, scale)
+    cu, n = _cu_arg(cu_seqlens)
+    return int(lib().ra_attn_bwd_varlen_validate(desc(q), desc(k), desc(v), desc(o), desc(dout),
+                                                 desc(lse), cu, n, ctypes.byref(p), desc(dq),
+                                                 desc(dk), desc(dv)))
 
 
 def attn_bwd_validate(q, k, v, o, dout, lse, dq, dk, dv, *, causal=False, num_chunks=1,

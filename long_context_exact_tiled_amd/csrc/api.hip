@@ -207,6 +207,49 @@ int bwd_validate(const ra_tensor *q, const ra_tensor *k, const ra_tensor *v, con
   return RA_OK;
 }
 
+// Backward over packed documents: the ra_attn_bwd checks plus those of the packed forward.
+int bwd_varlen_validate(const ra_tensor *q, const ra_tensor *k, const ra_tensor *v,
+                        const ra_tensor *o, const ra_tensor *dout, const ra_tensor *lse,
+                        const int32_t *cu_seqlens, int32_t n_docs, const ra_attn_params *p,
+                        const ra_tensor *dq, const ra_tensor *dk, const ra_tensor *dv) {
+  RA_TRY(bwd_validate(q, k, v, o, dout, lse, p, dq, dk, dv));
+  if (q->shape[2] != k->shape[2]) return RA_ERR_SHAPE;
+  if (p->num_chunks != 1 || p->start_chunk != 0 || p->q_offset != 0 || p->kv_offset != 0)
+    return RA_ERR_RANGE;
+  if (n_docs < 1 || n_docs > RA_MAX_DOCS) return RA_ERR_RANGE;
+  if (!cu_seqlens) return RA_ERR_NULL;
+  if (((uintptr_t)cu_seqlens) % 4) return RA_ERR_ALIGN;
+  return RA_OK;
+}
+
+BwdArgs bwd_args(const ra_tensor *q, const ra_tensor *k, const ra_tensor *v, const ra_tensor *o,
+                 const ra_tensor *dout, const ra_tensor *lse, const ra_attn_params *p,
+                 ra_tensor *dq, ra_tensor *dk, ra_tensor *dv, void *workspace) {
+  BwdArgs a{};
+  a.q = q->data; a.k = k->data; a.v = v->data; a.o = o->data; a.dout = dout->data;
+  a.lse = (const float *)lse->data;
+  a.dq = dq->data; a.dk = dk->data; a.dv = dv->data;
+  a.delta = (float *)workspace;
+  a.q_sb = q->stride[0]; a.q_sh = q->stride[1]; a.q_ss = q->stride[2];
+  a.k_sb = k->stride[0]; a.k_sh = k->stride[1]; a.k_ss = k->stride[2];
+  a.v_sb = v->stride[0]; a.v_sh = v->stride[1]; a.v_ss = v->stride[2];
+  a.o_sb = o->stride[0]; a.o_sh = o->stride[1]; a.o_ss = o->stride[2];
+  a.do_sb = dout->stride[0]; a.do_sh = dout->stride[1]; a.do_ss = dout->stride[2];
+  a.l_sb = lse->stride[0]; a.l_sh = lse->stride[1];
+  a.dq_sb = dq->stride[0]; a.dq_sh = dq->stride[1]; a.dq_ss = dq->stride[2];
+  a.dk_sb = dk->stride[0]; a.dk_sh = dk->stride[1]; a.dk_ss = dk->stride[2];
+  a.dv_sb = dv->stride[0]; a.dv_sh = dv->stride[1]; a.dv_ss = dv->stride[2];
+  a.B = (int32_t)q->shape[0]; a.Hq = (int32_t)q->shape[1]; a.Sq = (int32_t)q->shape[2];
+  a.Hkv = (int32_t)k->shape[1]; a.Skv = (int32_t)k->shape[2];
+  a.group = a.Hkv ? a.Hq / a.Hkv : 1;
+  a.num_chunks = p->num_chunks; a.start_chunk = p->start_chunk;
+  a.chunk_len = a.Skv / a.num_chunks;
+  a.q_offset = p->q_offset; a.kv_offset = p->kv_offset;
+  a.scale = effective_scale(p, q->shape[3]);
+  a.scale_log2 = a.scale * kLog2eHost;
+  return a;
+}
+
 }  // namespace
 }  // namespace ra
 
@@ -381,29 +424,32 @@ int ra_attn_bwd(const ra_tensor *q, const ra_tensor *k, const ra_tensor *v, cons
   if (need > 0 && (!workspace || workspace_bytes < need || ((uintptr_t)workspace) % 256))
     return RA_ERR_WORKSPACE;
   if (numel(q) == 0 && numel(k) == 0) return RA_OK;
-  BwdArgs a{};
-  a.q = q->data; a.k = k->data; a.v = v->data; a.o = o->data; a.dout = dout->data;
-  a.lse = (const float *)lse->data;
-  a.dq = dq->data; a.dk = dk->data; a.dv = dv->data;
-  a.delta = (float *)workspace;
-  a.q_sb = q->stride[0]; a.q_sh = q->stride[1]; a.q_ss = q->stride[2];
-  a.k_sb = k->stride[0]; a.k_sh = k->stride[1]; a.k_ss = k->stride[2];
-  a.v_sb = v->stride[0]; a.v_sh = v->stride[1]; a.v_ss = v->stride[2];
-  a.o_sb = o->stride[0]; a.o_sh = o->stride[1]; a.o_ss = o->stride[2];
-  a.do_sb = dout->stride[0]; a.do_sh = dout->stride[1]; a.do_ss = dout->stride[2];
-  a.l_sb = lse->stride[0]; a.l_sh = lse->stride[1];
-  a.dq_sb = dq->stride[0]; a.dq_sh = dq->stride[1]; a.dq_ss = dq->stride[2];
-  a.dk_sb = dk->stride[0]; a.dk_sh = dk->stride[1]; a.dk_ss = dk->stride[2];
-  a.dv_sb = dv->stride[0]; a.dv_sh = dv->stride[1]; a.dv_ss = dv->stride[2];
-  a.B = (int32_t)q->shape[0]; a.Hq = (int32_t)q->shape[1]; a.Sq = (int32_t)q->shape[2];
-  a.Hkv = (int32_t)k->shape[1]; a.Skv = (int32_t)k->shape[2];
-  a.group = a.Hkv ? a.Hq / a.Hkv : 1;
-  a.num_chunks = p->num_chunks; a.start_chunk = p->start_chunk;
-  a.chunk_len = a.Skv / a.num_chunks;
-  a.q_offset = p->q_offset; a.kv_offset = p->kv_offset;
-  a.scale = effective_scale(p, q->shape[3]);
-  a.scale_log2 = a.scale * kLog2eHost;
+  BwdArgs a = bwd_args(q, k, v, o, dout, lse, p, dq, dk, dv, workspace);
   return launch_attn_bwd(a, (int)q->shape[3], p->causal, (hipStream_t)stream);
+}
+
+int ra_attn_bwd_varlen_validate(const ra_tensor *q, const ra_tensor *k, const ra_tensor *v,
+                                const ra_tensor *o, const ra_tensor *dout, const ra_tensor *lse,
+                                const int32_t *cu_seqlens, int32_t n_docs,
+                                const ra_attn_params *p, const ra_tensor *dq, const ra_tensor *dk,
+                                const ra_tensor *dv) {
+  return bwd_varlen_validate(q, k, v, o, dout, lse, cu_seqlens, n_docs, p, dq, dk, dv);
+}
+
+int ra_attn_bwd_varlen(const ra_tensor *q, const ra_tensor *k, const ra_tensor *v,
+                       const ra_tensor *o, const ra_tensor *dout, const ra_tensor *lse,
+                       const int32_t *cu_seqlens, int32_t n_docs, const ra_attn_params *p,
+                       ra_tensor *dq, ra_tensor *dk, ra_tensor *dv, void *workspace,
+                       size_t workspace_bytes, ra_stream stream) {
+  RA_TRY(bwd_varlen_validate(q, k, v, o, dout, lse, cu_seqlens, n_docs, p, dq, dk, dv));
+  const size_t need = bwd_workspace_bytes(q->shape[0], q->shape[1], q->shape[2]);
+  if (need > 0 && (!workspace || workspace_bytes < need || ((uintptr_t)workspace) % 256))
+    return RA_ERR_WORKSPACE;
+  if (numel(q) == 0 && numel(k) == 0) return RA_OK;
+  BwdArgs a = bwd_args(q, k, v, o, dout, lse, p, dq, dk, dv, workspace);
+  a.cu = cu_seqlens;
+  a.n_docs = n_docs;
+  return launch_attn_bwd_varlen(a, (int)q->shape[3], p->causal, (hipStream_t)stream);
 }
 
 }  // extern "C"

@@ -166,7 +166,7 @@ __device__ __forceinline__ void ring_next_bwd(const BwdArgs &a, bool causal, int
 //   P^T = exp2(c S^T - log2e lse), dS^T = P^T (dP^T - D)  -> bf16
 //   dQ^T += K^T_mt dS^T_mt                          (16 MFMAs over the tile)
 // ---------------------------------------------------------------------------------
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool VARLEN>
 __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 bwd_dq_kernel(BwdArgs a, int num_q_tiles) {
   constexpr int NW = 8, BM = 32 * NW;
@@ -223,6 +223,23 @@ bwd_dq_kernel(BwdArgs a, int num_q_tiles) {
   const int64_t vis_lim = a.q_offset + qlast - a.kv_offset + 1;
   int t = -1, kb = 0, kend = 0, cend = 0;
   ring_next_bwd<KT>(a, CAUSAL, vis_lim, t, kb, kend, cend);
+  // Packed documents: this lane's row sees keys [ds, de) (causal: [ds, row]); the block
+  // walks from the tile holding its first row's document start.
+  int ds = 0, de = 0, w_ds_first = 0, w_ds_last = 0, w_de_first = 0, w_de_last = 0;
+  if (VARLEN) {
+    doc_bounds(a.cu, a.n_docs, qr, a.Skv, ds, de);
+    w_ds_first = __builtin_amdgcn_readlane(ds, 0);
+    w_ds_last = __builtin_amdgcn_readlane(ds, 31);
+    w_de_first = __builtin_amdgcn_readlane(de, 0);
+    w_de_last = __builtin_amdgcn_readlane(de, 31);
+    int b_ds, b_de, l_ds, l_de;
+    doc_bounds(a.cu, a.n_docs, q0, a.Skv, b_ds, b_de);
+    doc_bounds(a.cu, a.n_docs, qlast, a.Skv, l_ds, l_de);
+    b_ds = __builtin_amdgcn_readfirstlane(min(b_ds, qlast));
+    kb = (b_ds / KT) * KT;
+    if (!CAUSAL) kend = __builtin_amdgcn_readfirstlane(max(l_de, l_ds));
+    if (kb >= kend) t = a.num_chunks;
+  }
   if (t < a.num_chunks) {
     Tile::load(TL, kbase, a.k_ss, kb, a.Skv, smem0, wave);
     Tile::load(TL, vbase, a.v_ss, kb, a.Skv, smem0 + Tile::BYTES, wave);
@@ -240,11 +257,17 @@ bwd_dq_kernel(BwdArgs a, int num_q_tiles) {
       Tile::load(TL, vbase, a.v_ss, kb, a.Skv, nx + Tile::BYTES, wave);
     }
     const int64_t kpos0 = a.kv_offset + kb_cur;
-    if (wave_active && !(CAUSAL && kpos0 > wpos_last)) {
+    const bool doc_skip =
+        VARLEN && (kb_cur + KT <= w_ds_first || (!CAUSAL && kb_cur >= w_de_last));
+    if (wave_active && !(CAUSAL && kpos0 > wpos_last) && !doc_skip) {
       const uint32_t kt = smem0 + cur * 2 * Tile::BYTES, vt = kt + Tile::BYTES;
       const int kvalid = min(KT, cend_cur - kb_cur);
-      const bool need_mask = (kvalid < KT) || (CAUSAL && kpos0 + kvalid - 1 > wpos_first);
+      const bool need_mask =
+          (kvalid < KT) || (CAUSAL && kpos0 + kvalid - 1 > wpos_first) ||
+          (VARLEN && (kb_cur < w_ds_last || (!CAUSAL && kb_cur + kvalid > w_de_first)));
       int lim = kvalid;
+      const int lo = VARLEN ? ds - kb_cur : 0;  // keys lo <= kk < lim are visible
+      if (VARLEN && !CAUSAL) lim = min(lim, de - kb_cur);
       if (CAUSAL) {
         const int64_t vis = qpos - kpos0 + 1;
         lim = vis < (int64_t)lim ? (vis > 0 ? (int)vis : 0) : lim;
@@ -271,7 +294,7 @@ bwd_dq_kernel(BwdArgs a, int num_q_tiles) {
               const int i = 8 * s2 + 2 * w + e;
               const int kk = 32 * mt + (i >> 2) * 8 + 4 * h + (i & 3);
               float p = fast_exp2(fmaf(s[i], c, -lse2));
-              if (need_mask && kk >= lim) p = 0.f;
+              if (need_mask && (kk >= lim || (VARLEN && kk < lo))) p = 0.f;
               d2[e] = p * (dp[i] - dlt);
             }
             const bf16x2 pk = __builtin_convertvector((f32x2){d2[0], d2[1]}, bf16x2);
@@ -316,7 +339,7 @@ bwd_dq_kernel(BwdArgs a, int num_q_tiles) {
 //   P = exp2(c S - log2e lse), dS = P (dP - D)
 //   dV^T += dO^T P, dK^T += Q^T dS          (A: transposed reads of dO / Q)
 // ---------------------------------------------------------------------------------
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool VARLEN>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 bwd_dkdv_kernel(BwdArgs a, int num_kv_tiles) {
   constexpr int NW = 4, BK = 32 * NW;
@@ -372,7 +395,26 @@ bwd_dkdv_kernel(BwdArgs a, int num_kv_tiles) {
     qstart = first <= 0 ? 0 : (first >= (int64_t)a.Sq ? a.Sq : (int)first);
     qstart = (qstart / TN) * TN;
   }
-  const int nqt = qstart >= a.Sq ? 0 : (a.Sq - qstart + TN - 1) / TN;
+  int qend = a.Sq;
+  // Packed documents: this lane's key is seen by the queries of its document [ds, de)
+  // (causal: [key, de)); the block's queries run from its first key's document start
+  // to its last key's document end.
+  int ds = 0, de = 0, w_ds_first = 0, w_ds_last = 0, w_de_first = 0, w_de_last = 0;
+  if (VARLEN) {
+    static_assert(!VARLEN || RA_BWD_DKDV_PIPE, "packed documents use the pipelined tile");
+    doc_bounds(a.cu, a.n_docs, kr, a.Sq, ds, de);
+    w_ds_first = __builtin_amdgcn_readlane(ds, 0);
+    w_ds_last = __builtin_amdgcn_readlane(ds, 31);
+    w_de_first = __builtin_amdgcn_readlane(de, 0);
+    w_de_last = __builtin_amdgcn_readlane(de, 31);
+    const int klast = min(k0 + BK, a.Skv) - 1;
+    int f_ds, f_de, l_ds, l_de;
+    doc_bounds(a.cu, a.n_docs, min(k0, a.Skv - 1), a.Sq, f_ds, f_de);
+    doc_bounds(a.cu, a.n_docs, klast, a.Sq, l_ds, l_de);
+    if (!CAUSAL) qstart = (__builtin_amdgcn_readfirstlane(min(f_ds, k0)) / TN) * TN;
+    qend = __builtin_amdgcn_readfirstlane(min(max(l_de, l_ds), a.Sq));
+  }
+  const int nqt = qstart >= qend ? 0 : (qend - qstart + TN - 1) / TN;
   const int total = nqt * a.group;  // (query head, query tile) pairs
 
   auto issue = [&](int it, uint32_t slot) {
@@ -428,13 +470,20 @@ bwd_dkdv_kernel(BwdArgs a, int num_kv_tiles) {
     // [dV,dK of step 0 | P,dS of step 1] [dV,dK of step 1].  A step with no visible
     // (query, key) pair for this wave is computed and masked to zero (diagonal only).
     const int qv0 = min(32, a.Sq - q0), qv1 = min(32, a.Sq - (q0 + 32));
-    const bool vis0 = !(CAUSAL && wk_first > qpos0 + 31);
-    const bool vis1 = qv1 > 0 && !(CAUSAL && wk_first > qpos0 + 63);
+    // packed documents: a step wholly outside every document of this wave's keys
+    auto doc_out = [&](int sq) {
+      return VARLEN && (sq >= w_de_last || (!CAUSAL && sq + 32 <= w_ds_first));
+    };
+    const bool vis0 = !(CAUSAL && wk_first > qpos0 + 31) && !doc_out(q0);
+    const bool vis1 = qv1 > 0 && !(CAUSAL && wk_first > qpos0 + 63) && !doc_out(q0 + 32);
     if (wave_active && (vis0 || vis1)) {
       constexpr int NST = D / 8;  // MFMAs per stage
       constexpr int kDep = 4;
-      const bool nm0 = qv0 < 32 || (CAUSAL && wk_last > qpos0);
-      const bool nm1 = qv1 < 32 || (CAUSAL && wk_last > qpos0 + 32);
+      auto doc_cross = [&](int sq) {
+        return VARLEN && (sq + 32 > w_de_first || (!CAUSAL && sq < w_ds_last));
+      };
+      const bool nm0 = qv0 < 32 || (CAUSAL && wk_last > qpos0) || doc_cross(q0);
+      const bool nm1 = qv1 < 32 || (CAUSAL && wk_last > qpos0 + 32) || doc_cross(q0 + 32);
       f32x16 s0 = f32x16{}, dp0 = f32x16{}, s1 = f32x16{}, dp1 = f32x16{};
       u32x4 pf0[2], dsf0[2], pf1[2], dsf1[2];
       f32x4 l4[4], d4[4];
@@ -466,6 +515,10 @@ bwd_dkdv_kernel(BwdArgs a, int num_kv_tiles) {
           const int qi = (i >> 2) * 8 + 4 * h + (i & 3);
           float p = fast_exp2(fmaf(sv_[i], c, -l4[g][e]));
           if (nm && (qi >= qv || (CAUSAL && kpos > sfirst + qi))) p = 0.f;
+          if (VARLEN && nm) {  // packed documents (offsets are 0): the key's document only
+            const int64_t qabs = sfirst + qi;
+            if (qabs >= de || (!CAUSAL && qabs < ds)) p = 0.f;
+          }
           pv[e] = p;
           dv4[e] = p * (dpv[i] - d4[g][e]);
         }
@@ -613,7 +666,7 @@ bwd_dkdv_kernel(BwdArgs a, int num_kv_tiles) {
   }
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool VARLEN = false>
 int launch_bwd(const BwdArgs &a, hipStream_t stream) {
   // 1. D_i
   {
@@ -628,7 +681,7 @@ int launch_bwd(const BwdArgs &a, hipStream_t stream) {
     const int nkt = (a.Skv + 127) / 128;
     const int64_t blocks = (int64_t)nkt * a.Hkv * a.B;
     if (blocks > 0)
-      hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3((unsigned)blocks), dim3(256), 0,
+      hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, VARLEN>), dim3((unsigned)blocks), dim3(256), 0,
                          stream, a, nkt);
   }
   // 3. dQ
@@ -636,7 +689,7 @@ int launch_bwd(const BwdArgs &a, hipStream_t stream) {
     const int nqt = (a.Sq + 255) / 256;
     const int64_t blocks = (int64_t)nqt * a.Hq * a.B;
     if (blocks > 0)
-      hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3((unsigned)blocks), dim3(512), 0,
+      hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, VARLEN>), dim3((unsigned)blocks), dim3(512), 0,
                          stream, a, nqt);
   }
   return hipGetLastError() == hipSuccess ? RA_OK : RA_ERR_HIP;
@@ -647,6 +700,14 @@ int launch_bwd(const BwdArgs &a, hipStream_t stream) {
 size_t bwd_workspace_bytes(int64_t B, int64_t Hq, int64_t Sq) {
   const size_t n = (size_t)(B * Hq * Sq) * sizeof(float);
   return (n + 255) / 256 * 256;
+}
+
+int launch_attn_bwd_varlen(const BwdArgs &a, int D, int causal, hipStream_t stream) {
+  if (D == 128)
+    return causal ? launch_bwd<128, true, true>(a, stream) : launch_bwd<128, false, true>(a, stream);
+  if (D == 64)
+    return causal ? launch_bwd<64, true, true>(a, stream) : launch_bwd<64, false, true>(a, stream);
+  return RA_ERR_UNSUPPORTED;
 }
 
 int launch_attn_bwd(const BwdArgs &a, int D, int causal, hipStream_t stream) {

@@ -106,4 +106,23 @@ __device__ __forceinline__ void dma_b128(const void *tile_base, int lane_off, ui
 }
 #pragma clang diagnostic pop
 
+// Document of token t in a packed stream: [ds, de) with cu[d] <= t < cu[d+1] (the last
+// such d; cu[0] is 0).  A token past the last document, or offsets that break the rules,
+// give the empty range [t+1, t+1).  At most ceil(log2(n+1)) probes, all inside cu[0..n].
+__device__ __forceinline__ void doc_bounds(const int32_t *cu, int n, int t, int T, int &ds,
+                                           int &de) {
+  int lo = 0, hi = n;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (cu[mid] <= t) lo = mid; else hi = mid - 1;
+  }
+  ds = de = t + 1;
+  if (lo >= n) return;
+  const int a0 = min(max(cu[lo], 0), T), a1 = min(max(cu[lo + 1], a0), T);
+  if (a0 <= t && t < a1) {
+    ds = a0;
+    de = a1;
+  }
+}
+
 }  // namespace ra

@@ -86,9 +86,13 @@ struct BwdArgs {
   int32_t num_chunks, start_chunk, chunk_len;
   int64_t q_offset, kv_offset;
   float scale, scale_log2;
+  // packed documents (attn_bwd_varlen only): document d holds tokens cu[d] .. cu[d+1]-1
+  const int32_t *cu;
+  int32_t n_docs;
 };
 
 size_t bwd_workspace_bytes(int64_t B, int64_t Hq, int64_t Sq);
 int launch_attn_bwd(const BwdArgs &a, int D, int causal, hipStream_t stream);
+int launch_attn_bwd_varlen(const BwdArgs &a, int D, int causal, hipStream_t stream);
 
 }  // namespace ra

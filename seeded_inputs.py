@@ -142,6 +142,10 @@ WORKLOADS: Dict[str, Workload] = {
         name="qwen7b_packed_32k", dtype="bf16",
         q_shape=(1, 28, 32768, 128), kv_shape=(1, 4, 32768, 128),
         causal=True, seed=1006, packed_docs=True),
+    "qwen7b_packed_bwd_32k": Workload(
+        name="qwen7b_packed_bwd_32k", dtype="bf16",
+        q_shape=(1, 28, 32768, 128), kv_shape=(1, 4, 32768, 128),
+        causal=True, seed=1006, packed_docs=True, backward=True),
     "llama7b_causal_bwd_16k": Workload(
         name="llama7b_causal_bwd_16k", dtype="bf16",
         q_shape=(1, 32, 16384, 128), kv_shape=(1, 32, 16384, 128),

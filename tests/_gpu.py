@@ -78,3 +78,21 @@ def gather_rows(t: np.ndarray, idx):
 
 def gather_lse(t: np.ndarray, idx):
     return np.array([t[b, h, i] for (b, h, i) in idx])
+
+
+# Gradient tolerance (derived in test_gpu_bwd.py's header): element-wise
+# 2e-2 + 2^-8 |ref|, mean abs 2e-3, relative L2 1e-2.
+GRAD_TOL = dict(o_max=2e-2, o_mean=2e-3)
+
+
+def check_grad(got, ref, what):
+    assert np.isfinite(got).all(), f"{what}: non-finite"
+    err = np.abs(got - ref)
+    mx, mean = float(err.max(initial=0.0)), float(err.mean()) if err.size else 0.0
+    rel = float(np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-30))
+    print(f"[parity] {what}: max|err|={mx:.3e} mean|err|={mean:.3e} relL2={rel:.3e} "
+          f"max|ref|={float(np.abs(ref).max(initial=0.0)):.3e}", flush=True)
+    excess = float((err - (GRAD_TOL["o_max"] + 2.0 ** -8 * np.abs(ref))).max(initial=-1.0))
+    assert excess <= 0.0, f"{what}: element error over 2e-2 + 2^-8|ref| by {excess}"
+    assert mean <= GRAD_TOL["o_mean"], f"{what}: mean abs err {mean}"
+    assert rel <= 1e-2, f"{what}: relative L2 {rel}"

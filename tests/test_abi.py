@@ -109,6 +109,19 @@ def test_varlen_validation(ra):
         f(cu=torch.tensor([0, 64], dtype=torch.int64))
 
 
+def test_bwd_varlen_validation(ra):
+    q, k, v = _t((1, 4, 64, 128)), _t((1, 2, 64, 128)), _t((1, 2, 64, 128))
+    o, do, lse = _t(q.shape), _t(q.shape), torch.zeros(1, 4, 64)
+    cu = torch.tensor([0, 10, 64], dtype=torch.int32)
+
+    def f(q=q, k=k, v=v, **kw):
+        return ra.STATUS[ra.attn_bwd_varlen_validate(q, k, v, o, do, lse, cu, _t(q.shape),
+                                                     _t(k.shape), _t(v.shape), **kw)]
+
+    assert f() == "RA_OK" and f(causal=True) == "RA_OK"
+    assert f(k=_t((1, 2, 32, 128)), v=_t((1, 2, 32, 128))) == "RA_ERR_SHAPE"
+
+
 def test_fwd_rejects_before_launch(ra):
     """A failing call returns its code without touching the device (CPU tensors here)."""
     q, k = _t((1, 4, 64, 128)), _t((1, 3, 64, 128))
