@@ -36,7 +36,8 @@ Module map:
 * ``permute``    -- the Ulysses sequence-shard <-> head-shard layout step.
 * ``backward``   -- the textbook softmax-attention gradient (the pages only
   say the backward recomputes from saved statistics; the formulas are not on
-  them).  Pinned by finite differences in ``tests/``.
+  them), whole or chunk by chunk in ring order for one device's query block,
+  and over packed documents.  Pinned by finite differences in ``tests/``.
 
 Parity status: every function here is pinned by ``-m "not gpu"`` tests
 (brute force, closed forms, invariants, a library routine, finite
@@ -53,4 +54,9 @@ from .attention import (  # noqa: F401
     varlen_attention,
 )
 from .permute import seq_to_head, head_to_seq  # noqa: F401
-from .backward import attention_bwd, attention_bwd_heads, varlen_attention_bwd  # noqa: F401
+from .backward import (  # noqa: F401
+    attention_bwd,
+    attention_bwd_heads,
+    ring_attention_bwd,
+    varlen_attention_bwd,
+)

@@ -29,7 +29,8 @@ from typing import Iterable, Optional, Sequence, Tuple
 
 import numpy as np
 
-from .attention import _as64, _masked_scores, _row_softmax, _shapes
+from .attention import (_as64, _default_scale, _masked_scores, _row_softmax, _shapes,
+                        chunk_bounds, ring_attention, ring_order)
 
 
 def _bwd_group(q, k, v, do, b, g, group, scale, qpos, kpos, causal, row_block):
@@ -122,4 +123,57 @@ def varlen_attention_bwd(q, k, v, do, cu_seqlens: Sequence[int], *, causal: bool
             dq[:, :, a:b], dk[:, :, a:b], dv[:, :, a:b] = attention_bwd(
                 q[:, :, a:b], k[:, :, a:b], v[:, :, a:b], do[:, :, a:b], causal=causal,
                 scale=scale)
+    return dq, dk, dv
+
+
+def ring_attention_bwd(q, k, v, do, *, num_chunks: int, start_chunk: int = 0,
+                       causal: bool = False, scale: Optional[float] = None,
+                       q_offset: int = 0, kv_offset: int = 0):
+    """One device's ring backward, chunk by chunk; returns (dq, dk, dv), fp64.
+
+    The device holds the query block q (and dO) and sees the key/value sequence as
+    ``num_chunks`` equal chunks, visited in the forward's ring order
+    (start_chunk + t) mod P ([P2] ``ring_attention_forward`` listing; [P1]
+    "Ring-Attention：面向大规模部署的工程利器": gradients travel back along the
+    ring).  The forward's merged (o, lse) over every chunk come first (the
+    oracle's own ``ring_attention``); then, per visited chunk c,
+
+        P_c = exp(s_c - lse)  (0 where masked),  D = rowsum(dO * o)
+        dV_c = P_c^T dO,  dS_c = P_c o (dO V_c^T - D)
+        dQ  += scale dS_c K_c,  dK_c = scale dS_c^T q
+
+    so dQ is a sum over chunks and dK/dV of chunk c hold this device's share only
+    (the sum over every device's query block is the full gradient).  A causal chunk
+    whose first key lies after the block's last query is skipped (it adds 0).
+    """
+    q, k, v, do = _as64(q), _as64(k), _as64(v), _as64(do)
+    B, Hq, Sq, D, Hkv, Skv = _shapes(q, k, v)
+    if do.shape != q.shape:
+        raise ValueError("dO must be shaped like q")
+    scale = _default_scale(scale, D)
+    group = Hq // Hkv
+    o, lse = ring_attention(q, k, v, num_chunks=num_chunks, start_chunk=start_chunk,
+                            causal=causal, scale=scale, q_offset=q_offset,
+                            kv_offset=kv_offset)
+    delta = (do * o).sum(axis=3)
+    qpos = q_offset + np.arange(Sq)
+    dq, dk, dv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+    for c in ring_order(num_chunks, start_chunk):
+        lo, hi = chunk_bounds(Skv, num_chunks, c)
+        if hi == lo or (causal and kv_offset + lo > q_offset + Sq - 1):
+            continue
+        kpos = kv_offset + np.arange(lo, hi)
+        for b in range(B):
+            for h in range(Hq):
+                g = h // group
+                kc, vc = k[b, g, lo:hi], v[b, g, lo:hi]
+                s = _masked_scores(q[b, h], kc, scale, qpos, kpos, causal)
+                with np.errstate(invalid="ignore"):
+                    p = np.exp(s - lse[b, h][:, None])
+                p[~np.isfinite(s)] = 0.0
+                dO = do[b, h]
+                dv[b, g, lo:hi] += p.T @ dO
+                ds = p * (dO @ vc.T - delta[b, h][:, None])
+                dq[b, h] += scale * (ds @ kc)
+                dk[b, g, lo:hi] += scale * (ds.T @ q[b, h])
     return dq, dk, dv
