@@ -160,7 +160,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--chunked", action="store_true",
-                    help="ring workloads: one attn_fwd per visible chunk + lse_merge")
+                    help="ring workloads: one attn_fwd per visible chunk + lse_merge "
+                         "(backward: one attn_bwd_accum per visible chunk)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: every box here has a single MI355X, and the multi-GPU "
@@ -241,19 +242,38 @@ def main():
     elif w.backward:
         q, k, v, do = (to_dev(x) for x in si.draw_qkv(w.seed, w.q_shape, w.kv_shape, w.dtype,
                                                       with_dout=True))
-        o, lse = ra.attn_fwd(q, k, v, causal=w.causal)
-        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-        ws = torch.empty(max(ra.attn_bwd_workspace_size(q, k, causal=w.causal), 256),
+        kw = dict(causal=w.causal, num_chunks=w.num_chunks, start_chunk=w.start_chunk,
+                  q_offset=w.q_offset, kv_offset=w.kv_offset)
+        o, lse = ra.attn_fwd(q, k, v, **kw)
+        ws = torch.empty(max(ra.attn_bwd_workspace_size(q, k, **kw), 256),
                          dtype=torch.uint8, device=dev)
         flops *= 2.5  # five matrix products per (query, key) pair against the forward's two
         moved = 0
-        extra["kernel"] = "attn_bwd (delta + dkdv + dq)"
+        if args.chunked:
+            # one ring rank's backward as the ring delivers the chunks: one accumulating
+            # step per visible chunk into fp32 accumulators (zeroed before each pass)
+            dq = torch.zeros(q.shape, dtype=torch.float32, device=dev)
+            dk = torch.zeros(k.shape, dtype=torch.float32, device=dev)
+            dv = torch.zeros(v.shape, dtype=torch.float32, device=dev)
+            extra["kernel"] = "attn_bwd_accum per visible chunk (delta + dkdv + dq each)"
 
-        def pre():
-            pass
+            def pre():
+                dq.zero_()
+                dk.zero_()
+                dv.zero_()
 
-        def attn():
-            ra.attn_bwd(q, k, v, o, do, lse, causal=w.causal, dq=dq, dk=dk, dv=dv, workspace=ws)
+            def attn():
+                ra.ring_attn_bwd_chunked(q, k, v, o, do, lse, dq_acc=dq, dk_acc=dk, dv_acc=dv,
+                                         workspace=ws, **kw)
+        else:
+            dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+            extra["kernel"] = "attn_bwd (delta + dkdv + dq)"
+
+            def pre():
+                pass
+
+            def attn():
+                ra.attn_bwd(q, k, v, o, do, lse, dq=dq, dk=dk, dv=dv, workspace=ws, **kw)
 
         def post():
             pass

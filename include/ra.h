@@ -232,6 +232,40 @@ int ra_attn_bwd_varlen_validate(const ra_tensor *q, const ra_tensor *k, const ra
                                 const ra_attn_params *p, const ra_tensor *dq, const ra_tensor *dk,
                                 const ra_tensor *dv);
 
+/*
+ * ra_attn_bwd_accum -- one device's step of the ring backward: the gradient
+ * contributions of its query block against one key/value chunk, ADDED to fp32
+ * accumulators.
+ *
+ * [P1] section "Ring-Attention：面向大规模部署的工程利器": gradients travel back
+ * along the ring the way the blocks came.  Reading taken: at every step the device
+ * recomputes P = exp(scale q k_c^T - lse) against the chunk it holds, with lse (and o)
+ * the forward's result merged over every chunk; its dq accumulator stays with it and
+ * sums over the chunks; the chunk's dk/dv accumulators travel with the chunk and sum
+ * over the devices.  Formulas as for ra_attn_bwd, restricted to the chunk.
+ *
+ * q, o, dout [B, Hq, Sq, D] RA_BF16; k, v [B, Hkv, Skv, D] RA_BF16, the chunk only;
+ * lse [B, Hq, Sq] RA_F32, the merged forward lse of this block; D 64 or 128.
+ * dq_acc [B, Hq, Sq, D], dk_acc and dv_acc [B, Hkv, Skv, D]: RA_F32, read and
+ * updated in place (acc += contribution); the caller zeroes them before the first
+ * step.  p: causal, scale and the global positions q_offset (first query) and
+ * kv_offset (first key of the chunk); num_chunks must be 1 and start_chunk 0
+ * (RA_ERR_RANGE otherwise).  A causal chunk whose first key follows the block's last
+ * query adds nothing and returns RA_OK with no work enqueued.  workspace as for
+ * ra_attn_bwd (D_i is recomputed on every call).  Accumulators must not overlap each
+ * other or the inputs; steps on one stream accumulate in stream order
+ * (deterministic, no atomics).
+ */
+int ra_attn_bwd_accum(const ra_tensor *q, const ra_tensor *k, const ra_tensor *v,
+                      const ra_tensor *o, const ra_tensor *dout, const ra_tensor *lse,
+                      const ra_attn_params *p, ra_tensor *dq_acc, ra_tensor *dk_acc,
+                      ra_tensor *dv_acc, void *workspace, size_t workspace_bytes,
+                      ra_stream stream);
+int ra_attn_bwd_accum_validate(const ra_tensor *q, const ra_tensor *k, const ra_tensor *v,
+                               const ra_tensor *o, const ra_tensor *dout, const ra_tensor *lse,
+                               const ra_attn_params *p, const ra_tensor *dq_acc,
+                               const ra_tensor *dk_acc, const ra_tensor *dv_acc);
+
 /* Static message for a status code (never NULL). */
 const char *ra_status_string(int status);
 /* RA_VERSION of the loaded library. */

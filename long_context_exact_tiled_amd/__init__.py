@@ -27,6 +27,7 @@ __all__ = [
     "attn_fwd_validate", "lse_merge_validate", "ulysses_permute_validate", "attn_bwd_validate",
     "status_string", "version", "lib", "LIB_PATH", "RaError", "STATUS",
     "attn_fwd_varlen", "attn_fwd_varlen_validate", "attn_bwd_varlen", "attn_bwd_varlen_validate",
+    "attn_bwd_accum", "attn_bwd_accum_validate", "ring_attn_bwd_chunked",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libra.so")
@@ -89,6 +90,8 @@ def lib() -> ctypes.CDLL:
             "ra_attn_bwd_varlen": [T, T, T, T, T, T, vp, i32, PP, T, T, T, vp, sz, vp],
             "ra_attn_bwd_varlen_validate": [T, T, T, T, T, T, vp, i32, PP, T, T, T],
             "ra_attn_bwd_workspace_size": [T, T, PP],
+            "ra_attn_bwd_accum": [T, T, T, T, T, T, PP, T, T, T, vp, sz, vp],
+            "ra_attn_bwd_accum_validate": [T, T, T, T, T, T, PP, T, T, T],
             "ra_status_string": [ctypes.c_int],
             "ra_version": [],
         }
@@ -316,6 +319,30 @@ def attn_bwd_varlen_validate(q, k, v, o, dout, lse, cu_seqlens, dq, dk, dv, *, c
                                                  desc(dk), desc(dv)))
 
 
+def attn_bwd_accum(q, k, v, o, dout, lse, dq_acc, dk_acc, dv_acc, *, causal=False, q_offset=0,
+                   kv_offset=0, scale=None, workspace: Optional[torch.Tensor] = None):
+    """One ring-backward step: adds this block's gradients against the key/value chunk
+    (k, v at global position kv_offset) to the fp32 accumulators, in place."""
+    p = _params(causal, 1, 0, q_offset, kv_offset, scale)
+    need = int(lib().ra_attn_bwd_workspace_size(desc(q), desc(k), ctypes.byref(p)))
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    _check(lib().ra_attn_bwd_accum(desc(q), desc(k), desc(v), desc(o), desc(dout), desc(lse),
+                                   ctypes.byref(p), desc(dq_acc), desc(dk_acc), desc(dv_acc),
+                                   workspace.data_ptr(), workspace.numel(), _stream(q)))
+    return dq_acc, dk_acc, dv_acc
+
+
+def attn_bwd_accum_validate(q, k, v, o, dout, lse, dq_acc, dk_acc, dv_acc, *, causal=False,
+                            num_chunks=1, start_chunk=0, q_offset=0, kv_offset=0,
+                            scale=None) -> int:
+    """Host-side argument check of attn_bwd_accum (no device access); returns the status."""
+    p = _params(causal, num_chunks, start_chunk, q_offset, kv_offset, scale)
+    return int(lib().ra_attn_bwd_accum_validate(desc(q), desc(k), desc(v), desc(o), desc(dout),
+                                                desc(lse), ctypes.byref(p), desc(dq_acc),
+                                                desc(dk_acc), desc(dv_acc)))
+
+
 def attn_bwd_validate(q, k, v, o, dout, lse, dq, dk, dv, *, causal=False, num_chunks=1,
                       start_chunk=0, q_offset=0, kv_offset=0, scale=None) -> int:
     p = _params(causal, num_chunks, start_chunk, q_offset, kv_offset, scale)
@@ -356,3 +383,32 @@ def ring_attn_chunked(q, k, v, *, num_chunks: int, start_chunk: int = 0, causal:
         o_parts.append(o_c)
         lse_parts.append(l_c)
     return lse_merge(o_parts, lse_parts, out_dtype=out_dtype or q.dtype)
+
+
+def ring_attn_bwd_chunked(q, k, v, o, dout, lse, *, num_chunks: int, start_chunk: int = 0,
+                          causal: bool = False, q_offset: int = 0, kv_offset: int = 0,
+                          scale: Optional[float] = None, dq_acc=None, dk_acc=None, dv_acc=None,
+                          workspace: Optional[torch.Tensor] = None):
+    """One ring rank's backward chunk by chunk: one attn_bwd_accum per visible chunk in
+    ring order into fp32 accumulators (zeroed here when not given).  o and lse are the
+    rank's merged forward result; dk_acc/dv_acc cover every chunk [B, Hkv, Skv, D]."""
+    Skv = k.shape[2]
+    L = Skv // num_chunks
+    if dq_acc is None:
+        dq_acc = torch.zeros(q.shape, dtype=torch.float32, device=q.device)
+    if dk_acc is None:
+        dk_acc = torch.zeros(k.shape, dtype=torch.float32, device=k.device)
+    if dv_acc is None:
+        dv_acc = torch.zeros(v.shape, dtype=torch.float32, device=v.device)
+    if workspace is None:
+        p = _params(causal, 1, 0, q_offset, kv_offset, scale)
+        need = int(lib().ra_attn_bwd_workspace_size(desc(q), desc(k), ctypes.byref(p)))
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    for c in ring_visible_chunks(q.shape[2], Skv, num_chunks=num_chunks,
+                                 start_chunk=start_chunk, causal=causal, q_offset=q_offset,
+                                 kv_offset=kv_offset):
+        sl = slice(c * L, (c + 1) * L)
+        attn_bwd_accum(q, k[:, :, sl], v[:, :, sl], o, dout, lse, dq_acc, dk_acc[:, :, sl],
+                       dv_acc[:, :, sl], causal=causal, q_offset=q_offset,
+                       kv_offset=kv_offset + c * L, scale=scale, workspace=workspace)
+    return dq_acc, dk_acc, dv_acc

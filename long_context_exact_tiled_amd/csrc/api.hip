@@ -183,9 +183,11 @@ int permute_validate(const ra_tensor *src, const ra_tensor *dst, int32_t P, int3
   return RA_OK;
 }
 
+// grad_f32: dq, dk, dv are fp32 accumulators (the ring step) rather than q's dtype.
 int bwd_validate(const ra_tensor *q, const ra_tensor *k, const ra_tensor *v, const ra_tensor *o,
                  const ra_tensor *dout, const ra_tensor *lse, const ra_attn_params *p,
-                 const ra_tensor *dq, const ra_tensor *dk, const ra_tensor *dv) {
+                 const ra_tensor *dq, const ra_tensor *dk, const ra_tensor *dv,
+                 bool grad_f32 = false) {
   if (!o || !dout || !lse || !p || !dq || !dk || !dv) return RA_ERR_NULL;
   RA_TRY(check_qkv(q, k, v));
   RA_TRY(check_params(p, k->shape[2]));
@@ -194,8 +196,10 @@ int bwd_validate(const ra_tensor *q, const ra_tensor *k, const ra_tensor *v, con
   RA_TRY(check_tensor(dq, 4, 16, true));
   RA_TRY(check_tensor(dk, 4, 16, true));
   RA_TRY(check_tensor(dv, 4, 16, true));
-  for (const ra_tensor *t : {o, dout, dq, dk, dv})
+  for (const ra_tensor *t : {o, dout})
     if (t->dtype != q->dtype) return RA_ERR_DTYPE;
+  for (const ra_tensor *t : {dq, dk, dv})
+    if (t->dtype != (grad_f32 ? RA_F32 : q->dtype)) return RA_ERR_DTYPE;
   if (!same_shape(o, q) || !same_shape(dout, q) || !same_shape(dq, q)) return RA_ERR_SHAPE;
   if (!same_shape(dk, k) || !same_shape(dv, k)) return RA_ERR_SHAPE;
   RA_TRY(check_lse(lse, q, false));
@@ -219,6 +223,17 @@ int bwd_varlen_validate(const ra_tensor *q, const ra_tensor *k, const ra_tensor 
   if (n_docs < 1 || n_docs > RA_MAX_DOCS) return RA_ERR_RANGE;
   if (!cu_seqlens) return RA_ERR_NULL;
   if (((uintptr_t)cu_seqlens) % 4) return RA_ERR_ALIGN;
+  return RA_OK;
+}
+
+// One device's ring-backward step: the ra_attn_bwd checks with fp32 accumulators, and
+// the key/value block is a single chunk.
+int bwd_accum_validate(const ra_tensor *q, const ra_tensor *k, const ra_tensor *v,
+                       const ra_tensor *o, const ra_tensor *dout, const ra_tensor *lse,
+                       const ra_attn_params *p, const ra_tensor *dq, const ra_tensor *dk,
+                       const ra_tensor *dv) {
+  RA_TRY(bwd_validate(q, k, v, o, dout, lse, p, dq, dk, dv, true));
+  if (p->num_chunks != 1 || p->start_chunk != 0) return RA_ERR_RANGE;
   return RA_OK;
 }
 
@@ -450,6 +465,29 @@ int ra_attn_bwd_varlen(const ra_tensor *q, const ra_tensor *k, const ra_tensor *
   a.cu = cu_seqlens;
   a.n_docs = n_docs;
   return launch_attn_bwd_varlen(a, (int)q->shape[3], p->causal, (hipStream_t)stream);
+}
+
+int ra_attn_bwd_accum_validate(const ra_tensor *q, const ra_tensor *k, const ra_tensor *v,
+                               const ra_tensor *o, const ra_tensor *dout, const ra_tensor *lse,
+                               const ra_attn_params *p, const ra_tensor *dq_acc,
+                               const ra_tensor *dk_acc, const ra_tensor *dv_acc) {
+  return bwd_accum_validate(q, k, v, o, dout, lse, p, dq_acc, dk_acc, dv_acc);
+}
+
+int ra_attn_bwd_accum(const ra_tensor *q, const ra_tensor *k, const ra_tensor *v,
+                      const ra_tensor *o, const ra_tensor *dout, const ra_tensor *lse,
+                      const ra_attn_params *p, ra_tensor *dq_acc, ra_tensor *dk_acc,
+                      ra_tensor *dv_acc, void *workspace, size_t workspace_bytes,
+                      ra_stream stream) {
+  RA_TRY(bwd_accum_validate(q, k, v, o, dout, lse, p, dq_acc, dk_acc, dv_acc));
+  const size_t need = bwd_workspace_bytes(q->shape[0], q->shape[1], q->shape[2]);
+  if (need > 0 && (!workspace || workspace_bytes < need || ((uintptr_t)workspace) % 256))
+    return RA_ERR_WORKSPACE;
+  if (numel(q) == 0 || numel(k) == 0) return RA_OK;  // nothing to add
+  // causal chunk skip: a chunk after the block's last query adds nothing
+  if (p->causal && p->kv_offset > p->q_offset + q->shape[2] - 1) return RA_OK;
+  BwdArgs a = bwd_args(q, k, v, o, dout, lse, p, dq_acc, dk_acc, dv_acc, workspace);
+  return launch_attn_bwd_accum(a, (int)q->shape[3], p->causal, (hipStream_t)stream);
 }
 
 }  // extern "C"

@@ -23,6 +23,10 @@
 //                   dV^T += dO^T P and dK^T += Q^T dS with dO^T, Q^T read transposed.
 // Tiles move global -> LDS with direct loads and a swizzle that keeps both row-wise
 // (ds_read_b128) and transposed (ds_read_b64_tr_b16) operand reads conflict-free.
+// The accumulating form (ACC) is one device's step of the ring backward: the key/value
+// block is one chunk, and the epilogues add the step's dQ, dK, dV into fp32
+// accumulators (dQ stays with the device, dK/dV travel with the chunk) instead of
+// storing bf16 results.
 #include <math.h>
 
 #include "common.h"
@@ -166,7 +170,7 @@ __device__ __forceinline__ void ring_next_bwd(const BwdArgs &a, bool causal, int
 //   P^T = exp2(c S^T - log2e lse), dS^T = P^T (dP^T - D)  -> bf16
 //   dQ^T += K^T_mt dS^T_mt                          (16 MFMAs over the tile)
 // ---------------------------------------------------------------------------------
-template <int D, bool CAUSAL, bool VARLEN>
+template <int D, bool CAUSAL, bool VARLEN, bool ACC>
 __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 bwd_dq_kernel(BwdArgs a, int num_q_tiles) {
   constexpr int NW = 8, BM = 32 * NW;
@@ -322,6 +326,13 @@ bwd_dq_kernel(BwdArgs a, int num_q_tiles) {
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int d = 32 * dt + 8 * g + 4 * h;
+        if (ACC) {
+          f32x4 *acc = (f32x4 *)((float *)a.dq + orow + d);
+          const f32x4 prev = *acc;
+          *acc = f32x4{prev[0] + dq[dt][4 * g] * a.scale, prev[1] + dq[dt][4 * g + 1] * a.scale,
+                       prev[2] + dq[dt][4 * g + 2] * a.scale, prev[3] + dq[dt][4 * g + 3] * a.scale};
+          continue;
+        }
         const bf16x2 lo = __builtin_convertvector(
             (f32x2){dq[dt][4 * g] * a.scale, dq[dt][4 * g + 1] * a.scale}, bf16x2);
         const bf16x2 hi = __builtin_convertvector(
@@ -339,7 +350,7 @@ bwd_dq_kernel(BwdArgs a, int num_q_tiles) {
 //   P = exp2(c S - log2e lse), dS = P (dP - D)
 //   dV^T += dO^T P, dK^T += Q^T dS          (A: transposed reads of dO / Q)
 // ---------------------------------------------------------------------------------
-template <int D, bool CAUSAL, bool VARLEN>
+template <int D, bool CAUSAL, bool VARLEN, bool ACC>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 bwd_dkdv_kernel(BwdArgs a, int num_kv_tiles) {
   constexpr int NW = 4, BK = 32 * NW;
@@ -651,6 +662,16 @@ bwd_dkdv_kernel(BwdArgs a, int num_kv_tiles) {
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int d = 32 * dt + 8 * g + 4 * h;
+        if (ACC) {
+          f32x4 *ak = (f32x4 *)((float *)a.dk + krow_dk + d);
+          f32x4 *av = (f32x4 *)((float *)a.dv + krow_dv + d);
+          const f32x4 pk = *ak, pv = *av;
+          *ak = f32x4{pk[0] + dk[dt][4 * g] * a.scale, pk[1] + dk[dt][4 * g + 1] * a.scale,
+                      pk[2] + dk[dt][4 * g + 2] * a.scale, pk[3] + dk[dt][4 * g + 3] * a.scale};
+          *av = f32x4{pv[0] + dv[dt][4 * g], pv[1] + dv[dt][4 * g + 1], pv[2] + dv[dt][4 * g + 2],
+                      pv[3] + dv[dt][4 * g + 3]};
+          continue;
+        }
         const bf16x2 k01 = __builtin_convertvector(
             (f32x2){dk[dt][4 * g] * a.scale, dk[dt][4 * g + 1] * a.scale}, bf16x2);
         const bf16x2 k23 = __builtin_convertvector(
@@ -666,7 +687,7 @@ bwd_dkdv_kernel(BwdArgs a, int num_kv_tiles) {
   }
 }
 
-template <int D, bool CAUSAL, bool VARLEN = false>
+template <int D, bool CAUSAL, bool VARLEN = false, bool ACC = false>
 int launch_bwd(const BwdArgs &a, hipStream_t stream) {
   // 1. D_i
   {
@@ -681,7 +702,7 @@ int launch_bwd(const BwdArgs &a, hipStream_t stream) {
     const int nkt = (a.Skv + 127) / 128;
     const int64_t blocks = (int64_t)nkt * a.Hkv * a.B;
     if (blocks > 0)
-      hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, VARLEN>), dim3((unsigned)blocks), dim3(256), 0,
+      hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, VARLEN, ACC>), dim3((unsigned)blocks), dim3(256), 0,
                          stream, a, nkt);
   }
   // 3. dQ
@@ -689,7 +710,7 @@ int launch_bwd(const BwdArgs &a, hipStream_t stream) {
     const int nqt = (a.Sq + 255) / 256;
     const int64_t blocks = (int64_t)nqt * a.Hq * a.B;
     if (blocks > 0)
-      hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, VARLEN>), dim3((unsigned)blocks), dim3(512), 0,
+      hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, VARLEN, ACC>), dim3((unsigned)blocks), dim3(512), 0,
                          stream, a, nqt);
   }
   return hipGetLastError() == hipSuccess ? RA_OK : RA_ERR_HIP;
@@ -707,6 +728,16 @@ int launch_attn_bwd_varlen(const BwdArgs &a, int D, int causal, hipStream_t stre
     return causal ? launch_bwd<128, true, true>(a, stream) : launch_bwd<128, false, true>(a, stream);
   if (D == 64)
     return causal ? launch_bwd<64, true, true>(a, stream) : launch_bwd<64, false, true>(a, stream);
+  return RA_ERR_UNSUPPORTED;
+}
+
+int launch_attn_bwd_accum(const BwdArgs &a, int D, int causal, hipStream_t stream) {
+  if (D == 128)
+    return causal ? launch_bwd<128, true, false, true>(a, stream)
+                  : launch_bwd<128, false, false, true>(a, stream);
+  if (D == 64)
+    return causal ? launch_bwd<64, true, false, true>(a, stream)
+                  : launch_bwd<64, false, false, true>(a, stream);
   return RA_ERR_UNSUPPORTED;
 }
 

@@ -94,5 +94,7 @@ struct BwdArgs {
 size_t bwd_workspace_bytes(int64_t B, int64_t Hq, int64_t Sq);
 int launch_attn_bwd(const BwdArgs &a, int D, int causal, hipStream_t stream);
 int launch_attn_bwd_varlen(const BwdArgs &a, int D, int causal, hipStream_t stream);
+// One ring step: dq, dk, dv point at fp32 accumulators that receive += contributions.
+int launch_attn_bwd_accum(const BwdArgs &a, int D, int causal, hipStream_t stream);
 
 }  // namespace ra

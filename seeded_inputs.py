@@ -146,6 +146,10 @@ WORKLOADS: Dict[str, Workload] = {
         name="qwen7b_packed_bwd_32k", dtype="bf16",
         q_shape=(1, 28, 32768, 128), kv_shape=(1, 4, 32768, 128),
         causal=True, seed=1006, packed_docs=True, backward=True),
+    "ring8_rank3_bwd_32k": Workload(
+        name="ring8_rank3_bwd_32k", dtype="bf16",
+        q_shape=(1, 32, 4096, 128), kv_shape=(1, 32, 32768, 128),
+        causal=True, num_chunks=8, start_chunk=3, q_offset=3 * 4096, seed=1007, backward=True),
     "llama7b_causal_bwd_16k": Workload(
         name="llama7b_causal_bwd_16k", dtype="bf16",
         q_shape=(1, 32, 16384, 128), kv_shape=(1, 32, 16384, 128),

@@ -181,3 +181,22 @@ def test_bwd_validation(ra):
     assert val(f(q), f(k), f(v), f(o), f(do), lse, f(dq), f(dk), f(dv)) == "RA_ERR_UNSUPPORTED"
     assert ra.attn_bwd_workspace_size(q, k) >= 4 * 64 * 4
     assert ra.attn_bwd_workspace_size(q, _t((1, 3, 64, 128))) == 0
+
+
+def test_bwd_accum_validation(ra):
+    """The ring-backward step takes fp32 accumulators and one chunk (num_chunks = 1)."""
+    q, k, v = _t((1, 4, 64, 128)), _t((1, 2, 32, 128)), _t((1, 2, 32, 128))
+    o, do, lse = _t(q.shape), _t(q.shape), torch.zeros(1, 4, 64)
+    f32 = lambda shape: torch.zeros(shape)
+    dq, dk, dv = f32(q.shape), f32(k.shape), f32(k.shape)
+    val = lambda *a, **kw: ra.STATUS[ra.attn_bwd_accum_validate(*a, **kw)]
+    assert val(q, k, v, o, do, lse, dq, dk, dv, causal=True, q_offset=32, kv_offset=64) == "RA_OK"
+    assert val(q, k, v, o, do, lse, dq.bfloat16(), dk, dv) == "RA_ERR_DTYPE"
+    assert val(q, k, v, o, do, lse, dq, dk, dv.bfloat16()) == "RA_ERR_DTYPE"
+    assert val(q, k, v, o.float(), do, lse, dq, dk, dv) == "RA_ERR_DTYPE"
+    assert val(q, k, v, o, do, lse, dq, f32((1, 2, 33, 128)), dv) == "RA_ERR_SHAPE"
+    assert val(q, k, v, o, do, lse, dq, dk, dv, num_chunks=2) == "RA_ERR_RANGE"
+    assert val(q, k, v, o, do, lse, dq, dk, dv, q_offset=-1) == "RA_ERR_RANGE"
+    # a transposed (overlapping-free but non-unit last stride) accumulator is refused
+    assert val(q, k, v, o, do, lse, dq, dk, f32((1, 2, 128, 32)).transpose(2, 3)) == \
+        "RA_ERR_STRIDE"
