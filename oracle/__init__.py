@@ -38,6 +38,10 @@ Module map:
   say the backward recomputes from saved statistics; the formulas are not on
   them), whole or chunk by chunk in ring order for one device's query block,
   and over packed documents.  Pinned by finite differences in ``tests/``.
+* ``fp8``        -- the e4m3 code (OCP definition), the per-head scaling rule,
+  attention over dequantized fp8 inputs, and the derived bound on the error of
+  rounding the attention weights to e4m3.  Pinned against torch's float8_e4m3fn
+  conversion, the format's defining values and a simulation of the rounding.
 
 Parity status: every function here is pinned by ``-m "not gpu"`` tests
 (brute force, closed forms, invariants, a library routine, finite
@@ -60,3 +64,4 @@ from .backward import (  # noqa: F401
     ring_attention_bwd,
     varlen_attention_bwd,
 )
+from . import fp8  # noqa: F401,E402
