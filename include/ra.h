@@ -52,7 +52,7 @@ typedef enum {
   RA_ERR_WORKSPACE = -9    /* workspace missing or smaller than required */
 } ra_status;
 
-typedef enum { RA_F32 = 0, RA_BF16 = 1 } ra_dtype;
+typedef enum { RA_F32 = 0, RA_BF16 = 1, RA_FP8_E4M3 = 2 /* OCP e4m3, 1 byte */ } ra_dtype;
 
 typedef struct {
   void *data;        /* device pointer, 16-byte aligned */
@@ -265,6 +265,60 @@ int ra_attn_bwd_accum_validate(const ra_tensor *q, const ra_tensor *k, const ra_
                                const ra_tensor *o, const ra_tensor *dout, const ra_tensor *lse,
                                const ra_attn_params *p, const ra_tensor *dq_acc,
                                const ra_tensor *dk_acc, const ra_tensor *dv_acc);
+
+/*
+ * ra_fp8_quantize -- bf16 -> e4m3 codes with one fp32 scale per (batch, head), the
+ * input of ra_attn_fwd_fp8.
+ *
+ * [P4] section "FlashAttention 如何破局？不只是融合内核": FlashAttention-3 supports the
+ * FP8 data type, halving key/value traffic.  The scaling rule is a reading (the pages
+ * give none): with a = max |x| over the head, code = e4m3(clamp(x * (448 / a), -448,
+ * 448)), an fp32 multiply and a round-to-nearest-even conversion to OCP e4m3;
+ * descale = a / 448 (fp32); an all-zero head gets descale 1 and zero codes.  The value
+ * of a code is decode(code) * descale.
+ *
+ * src     [B, H, S, D] RA_BF16, D a multiple of 16 and at most 256
+ * dst     RA_FP8_E4M3: [B, H, S, D] (transpose = 0), or [B, H, D, S_pad] with
+ *         S_pad = S rounded up to 16 (transpose = 1: tokens contiguous, the layout of
+ *         ra_attn_fwd_fp8's vt; tokens S .. S_pad-1 get code 0)
+ * descale [B, H] RA_F32, written
+ * workspace: device memory of at least ra_fp8_quantize_workspace_size bytes, 256-byte
+ * aligned, overwritten.  Non-finite inputs give unspecified codes.  Deterministic.
+ */
+int ra_fp8_quantize(const ra_tensor *src, ra_tensor *dst, ra_tensor *descale, int32_t transpose,
+                    void *workspace, size_t workspace_bytes, ra_stream stream);
+int ra_fp8_quantize_validate(const ra_tensor *src, const ra_tensor *dst,
+                             const ra_tensor *descale, int32_t transpose);
+/* Bytes of workspace ra_fp8_quantize needs for src (0 if src is invalid). */
+size_t ra_fp8_quantize_workspace_size(const ra_tensor *src);
+
+/*
+ * ra_attn_fwd_fp8 -- ra_attn_fwd over e4m3 inputs: exact softmax attention of the
+ * dequantized q, k, v (value = decode(code) * descale of its (batch, head)), the same
+ * ring walk, causal mask and outputs.
+ *
+ * [P4] section "FlashAttention 如何破局？不只是融合内核" (FlashAttention-3's FP8 support;
+ * tiling and the online softmax); ring and merge sources as ra_attn_fwd.  The attention
+ * weights are rounded to e4m3 for the P V product (after scaling by 2^6); the row sums
+ * and lse use the unrounded fp32 weights.
+ *
+ * q   [B, Hq, Sq, D] RA_FP8_E4M3;  k [B, Hkv, Skv, D] RA_FP8_E4M3;  D 64 or 128
+ * vt  [B, Hkv, D, S_pad] RA_FP8_E4M3, V transposed (tokens contiguous), S_pad = Skv
+ *     rounded up to 16, rows 16-byte aligned; columns Skv .. S_pad-1 are read and must
+ *     hold finite codes (ra_fp8_quantize writes 0 there)
+ * q_descale [B, Hq], k_descale and v_descale [B, Hkv]: RA_F32, finite and > 0
+ * p   as for ra_attn_fwd;  o [B, Hq, Sq, D] RA_BF16 or RA_F32;  lse [B, Hq, Sq] RA_F32
+ * Errors as for ra_attn_fwd; RA_ERR_SHAPE also when one head's byte offsets exceed
+ * 2^31.  Outputs must not overlap the inputs.
+ */
+int ra_attn_fwd_fp8(const ra_tensor *q, const ra_tensor *k, const ra_tensor *vt,
+                    const ra_tensor *q_descale, const ra_tensor *k_descale,
+                    const ra_tensor *v_descale, const ra_attn_params *p, ra_tensor *o,
+                    ra_tensor *lse, ra_stream stream);
+int ra_attn_fwd_fp8_validate(const ra_tensor *q, const ra_tensor *k, const ra_tensor *vt,
+                             const ra_tensor *q_descale, const ra_tensor *k_descale,
+                             const ra_tensor *v_descale, const ra_attn_params *p,
+                             const ra_tensor *o, const ra_tensor *lse);
 
 /* Static message for a status code (never NULL). */
 const char *ra_status_string(int status);

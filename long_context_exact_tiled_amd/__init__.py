@@ -28,6 +28,7 @@ __all__ = [
     "status_string", "version", "lib", "LIB_PATH", "RaError", "STATUS",
     "attn_fwd_varlen", "attn_fwd_varlen_validate", "attn_bwd_varlen", "attn_bwd_varlen_validate",
     "attn_bwd_accum", "attn_bwd_accum_validate", "ring_attn_bwd_chunked",
+    "fp8_quantize", "fp8_quantize_validate", "attn_fwd_fp8", "attn_fwd_fp8_validate",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libra.so")
@@ -37,7 +38,7 @@ STATUS = {
     -5: "RA_ERR_ALIGN", -6: "RA_ERR_RANGE", -7: "RA_ERR_UNSUPPORTED", -8: "RA_ERR_HIP",
     -9: "RA_ERR_WORKSPACE",
 }
-RA_F32, RA_BF16 = 0, 1
+RA_F32, RA_BF16, RA_FP8_E4M3 = 0, 1, 2
 MAX_MERGE_PARTS = 64
 
 
@@ -92,6 +93,11 @@ def lib() -> ctypes.CDLL:
             "ra_attn_bwd_workspace_size": [T, T, PP],
             "ra_attn_bwd_accum": [T, T, T, T, T, T, PP, T, T, T, vp, sz, vp],
             "ra_attn_bwd_accum_validate": [T, T, T, T, T, T, PP, T, T, T],
+            "ra_fp8_quantize": [T, T, T, i32, vp, sz, vp],
+            "ra_fp8_quantize_validate": [T, T, T, i32],
+            "ra_fp8_quantize_workspace_size": [T],
+            "ra_attn_fwd_fp8": [T, T, T, T, T, T, PP, T, T, vp],
+            "ra_attn_fwd_fp8_validate": [T, T, T, T, T, T, PP, T, T],
             "ra_status_string": [ctypes.c_int],
             "ra_version": [],
         }
@@ -100,6 +106,7 @@ def lib() -> ctypes.CDLL:
             fn.argtypes = args
             fn.restype = ctypes.c_int
         L.ra_attn_bwd_workspace_size.restype = ctypes.c_size_t
+        L.ra_fp8_quantize_workspace_size.restype = ctypes.c_size_t
         L.ra_status_string.restype = ctypes.c_char_p
         _LIB = L
     return _LIB
@@ -123,6 +130,8 @@ def _dtype_code(t: torch.Tensor) -> int:
         return RA_F32
     if t.dtype == torch.bfloat16:
         return RA_BF16
+    if t.dtype == torch.float8_e4m3fn:
+        return RA_FP8_E4M3
     raise RaError(-2, f"RA_ERR_DTYPE: unsupported torch dtype {t.dtype}")
 
 
@@ -181,6 +190,58 @@ def attn_fwd_validate(q, k, v, out, lse, *, causal=False, num_chunks=1, start_ch
     p = _params(causal, num_chunks, start_chunk, q_offset, kv_offset, scale)
     return int(lib().ra_attn_fwd_validate(desc(q), desc(k), desc(v), ctypes.byref(p),
                                           desc(out), desc(lse)))
+
+
+def fp8_quantize(x: torch.Tensor, *, transpose: bool = False, out=None, descale=None,
+                 workspace: Optional[torch.Tensor] = None):
+    """bf16 [B,H,S,D] -> (e4m3 codes, fp32 descale [B,H]) with one scale per (batch, head);
+    transpose=True gives codes [B,H,D,S_pad] (S_pad = S rounded up to 16), the V^T layout
+    attn_fwd_fp8 reads."""
+    B, H, S, D = x.shape
+    if out is None:
+        shape = (B, H, D, (S + 15) // 16 * 16) if transpose else (B, H, S, D)
+        out = torch.empty(shape, dtype=torch.float8_e4m3fn, device=x.device)
+    if descale is None:
+        descale = torch.empty(B, H, dtype=torch.float32, device=x.device)
+    if workspace is None:
+        need = int(lib().ra_fp8_quantize_workspace_size(desc(x)))
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=x.device)
+    _check(lib().ra_fp8_quantize(desc(x), desc(out), desc(descale), int(bool(transpose)),
+                                 workspace.data_ptr(), workspace.numel(), _stream(x)))
+    return out, descale
+
+
+def fp8_quantize_validate(x, out, descale, *, transpose=False) -> int:
+    """Host-side argument check of fp8_quantize (no device access); returns the status."""
+    return int(lib().ra_fp8_quantize_validate(desc(x), desc(out), desc(descale),
+                                              int(bool(transpose))))
+
+
+def attn_fwd_fp8(q, k, vt, q_descale, k_descale, v_descale, *, causal: bool = False,
+                 num_chunks: int = 1, start_chunk: int = 0, q_offset: int = 0,
+                 kv_offset: int = 0, scale: Optional[float] = None, out=None, lse=None,
+                 out_dtype: torch.dtype = torch.bfloat16):
+    """attn_fwd over e4m3 codes (q, k [B,H,S,D]; vt [B,Hkv,D,S_pad]) with fp32 descales
+    per (batch, head).  Returns (o, lse)."""
+    if out is None:
+        out = torch.empty(q.shape, dtype=out_dtype, device=q.device)
+    if lse is None:
+        lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+    p = _params(causal, num_chunks, start_chunk, q_offset, kv_offset, scale)
+    _check(lib().ra_attn_fwd_fp8(desc(q), desc(k), desc(vt), desc(q_descale), desc(k_descale),
+                                 desc(v_descale), ctypes.byref(p), desc(out), desc(lse),
+                                 _stream(q)))
+    return out, lse
+
+
+def attn_fwd_fp8_validate(q, k, vt, q_descale, k_descale, v_descale, out, lse, *,
+                          causal=False, num_chunks=1, start_chunk=0, q_offset=0, kv_offset=0,
+                          scale=None) -> int:
+    """Host-side argument check of attn_fwd_fp8 (no device access); returns the status."""
+    p = _params(causal, num_chunks, start_chunk, q_offset, kv_offset, scale)
+    return int(lib().ra_attn_fwd_fp8_validate(desc(q), desc(k), desc(vt), desc(q_descale),
+                                              desc(k_descale), desc(v_descale),
+                                              ctypes.byref(p), desc(out), desc(lse)))
 
 
 def _cu_arg(cu_seqlens: torch.Tensor):

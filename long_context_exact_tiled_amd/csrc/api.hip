@@ -11,9 +11,13 @@
 namespace ra {
 namespace {
 
-int64_t esize(int32_t dtype) { return dtype == RA_F32 ? 4 : (dtype == RA_BF16 ? 2 : 0); }
+int64_t esize(int32_t dtype) {
+  return dtype == RA_F32 ? 4 : (dtype == RA_BF16 ? 2 : (dtype == RA_FP8_E4M3 ? 1 : 0));
+}
 
-bool known_dtype(int32_t dtype) { return dtype == RA_F32 || dtype == RA_BF16; }
+bool known_dtype(int32_t dtype) {
+  return dtype == RA_F32 || dtype == RA_BF16 || dtype == RA_FP8_E4M3;
+}
 
 int64_t numel(const ra_tensor *t) {
   int64_t n = 1;
@@ -99,6 +103,7 @@ int check_qkv(const ra_tensor *q, const ra_tensor *k, const ra_tensor *v) {
   RA_TRY(check_tensor(k, 4, 16, false));
   RA_TRY(check_tensor(v, 4, 16, false));
   if (k->dtype != q->dtype || v->dtype != q->dtype) return RA_ERR_DTYPE;
+  if (q->dtype == RA_FP8_E4M3) return RA_ERR_DTYPE;  // fp8 inputs: ra_attn_fwd_fp8
   if (!same_shape(k, v)) return RA_ERR_SHAPE;
   if (k->shape[0] != q->shape[0] || k->shape[3] != q->shape[3]) return RA_ERR_SHAPE;
   const int64_t Hq = q->shape[1], Hkv = k->shape[1];
@@ -141,11 +146,13 @@ int merge_validate(int32_t n, const ra_tensor *o_parts, const ra_tensor *lse_par
   if (!o_parts || !lse_parts || !o || !lse) return RA_ERR_NULL;
   if (n < 1 || n > RA_MAX_MERGE_PARTS) return RA_ERR_RANGE;
   RA_TRY(check_tensor(o, 4, 16, true));
+  if (o->dtype == RA_FP8_E4M3) return RA_ERR_DTYPE;
   RA_TRY(check_lse(lse, o, true));
   for (int i = 0; i < n; ++i) {
     RA_TRY(check_tensor(&o_parts[i], 4, 16, false));
     RA_TRY(check_tensor(&lse_parts[i], 3, 4, false));
     if (o_parts[i].dtype != o_parts[0].dtype) return RA_ERR_DTYPE;
+    if (o_parts[i].dtype == RA_FP8_E4M3) return RA_ERR_DTYPE;
     if (lse_parts[i].dtype != RA_F32) return RA_ERR_DTYPE;
     if (!same_shape(&o_parts[i], o)) return RA_ERR_SHAPE;
     for (int d = 0; d < 3; ++d)
@@ -235,6 +242,81 @@ int bwd_accum_validate(const ra_tensor *q, const ra_tensor *k, const ra_tensor *
   RA_TRY(bwd_validate(q, k, v, o, dout, lse, p, dq, dk, dv, true));
   if (p->num_chunks != 1 || p->start_chunk != 0) return RA_ERR_RANGE;
   return RA_OK;
+}
+
+// One fp32 scale per (batch, head): a [B, H] tensor.
+int check_descale(const ra_tensor *t, int64_t B, int64_t H, bool is_output) {
+  if (!t) return RA_ERR_NULL;
+  RA_TRY(check_tensor(t, 2, 4, is_output));
+  if (t->dtype != RA_F32) return RA_ERR_DTYPE;
+  if (t->shape[0] != B || t->shape[1] != H) return RA_ERR_SHAPE;
+  return RA_OK;
+}
+
+// fp8 forward: q, k codes [B, H, S, D]; vt codes [B, Hkv, D, S_pad] (S_pad = Skv rounded
+// up to 16, tokens contiguous, rows 16-byte aligned); descales; o bf16 or fp32.
+int fp8_validate(const ra_tensor *q, const ra_tensor *k, const ra_tensor *vt,
+                 const ra_tensor *qd, const ra_tensor *kd, const ra_tensor *vd,
+                 const ra_attn_params *p, const ra_tensor *o, const ra_tensor *lse) {
+  if (!q || !k || !vt || !o || !lse || !p) return RA_ERR_NULL;
+  RA_TRY(check_tensor(q, 4, 16, false));
+  RA_TRY(check_tensor(k, 4, 16, false));
+  RA_TRY(check_tensor(vt, 4, 16, false));
+  for (const ra_tensor *t : {q, k, vt})
+    if (t->dtype != RA_FP8_E4M3) return RA_ERR_DTYPE;
+  const int64_t B = q->shape[0], Hq = q->shape[1], Sq = q->shape[2], D = q->shape[3];
+  const int64_t Hkv = k->shape[1], Skv = k->shape[2];
+  if (k->shape[0] != B || k->shape[3] != D) return RA_ERR_SHAPE;
+  if (Hq > 0 && (Hkv == 0 || Hq % Hkv)) return RA_ERR_SHAPE;
+  const int64_t S_pad = (Skv + 15) / 16 * 16;
+  if (vt->shape[0] != B || vt->shape[1] != Hkv || vt->shape[2] != D || vt->shape[3] != S_pad)
+    return RA_ERR_SHAPE;
+  RA_TRY(check_params(p, Skv));
+  RA_TRY(check_tensor(o, 4, 16, true));
+  if (o->dtype != RA_BF16 && o->dtype != RA_F32) return RA_ERR_DTYPE;
+  if (!same_shape(o, q)) return RA_ERR_SHAPE;
+  RA_TRY(check_lse(lse, q, true));
+  RA_TRY(check_grid(q));
+  RA_TRY(check_descale(qd, B, Hq, false));
+  RA_TRY(check_descale(kd, B, Hkv, false));
+  RA_TRY(check_descale(vd, B, Hkv, false));
+  if (D != 64 && D != 128) return RA_ERR_UNSUPPORTED;
+  // the kernel forms byte offsets within one head in 32 bits
+  if (Skv > 0 && ((Skv - 1) * k->stride[2] + D > (int64_t)INT32_MAX ||
+                  (D - 1) * vt->stride[2] + S_pad > (int64_t)INT32_MAX))
+    return RA_ERR_SHAPE;
+  return RA_OK;
+}
+
+// Quantizer: src bf16 [B, H, S, D] (D a multiple of 16, at most 256); dst codes of the
+// same shape, or [B, H, D, S_pad] when transposed; descale [B, H] fp32.
+int quant_validate(const ra_tensor *src, const ra_tensor *dst, const ra_tensor *descale,
+                   int32_t transpose) {
+  if (!src || !dst || !descale) return RA_ERR_NULL;
+  if (transpose != 0 && transpose != 1) return RA_ERR_RANGE;
+  RA_TRY(check_tensor(src, 4, 16, false));
+  RA_TRY(check_tensor(dst, 4, 16, true));
+  if (src->dtype != RA_BF16 || dst->dtype != RA_FP8_E4M3) return RA_ERR_DTYPE;
+  const int64_t B = src->shape[0], H = src->shape[1], S = src->shape[2], D = src->shape[3];
+  if (D % 16 || D > 256) return RA_ERR_UNSUPPORTED;
+  if (transpose) {
+    const int64_t S_pad = (S + 15) / 16 * 16;
+    if (dst->shape[0] != B || dst->shape[1] != H || dst->shape[2] != D || dst->shape[3] != S_pad)
+      return RA_ERR_SHAPE;
+  } else if (!same_shape(src, dst)) {
+    return RA_ERR_SHAPE;
+  }
+  RA_TRY(check_descale(descale, B, H, true));
+  if (B * H > (int64_t)INT32_MAX / 1024 || B * H * ((S + 63) / 64 + 1) > (int64_t)INT32_MAX)
+    return RA_ERR_SHAPE;
+  return RA_OK;
+}
+
+size_t quant_workspace_bytes(const ra_tensor *src) {
+  int32_t nsplit, rps;
+  quant_split(src->shape[2], src->shape[3], nsplit, rps);
+  const size_t n = (size_t)(src->shape[0] * src->shape[1]) * (size_t)nsplit * sizeof(float);
+  return (n + 255) / 256 * 256;
 }
 
 BwdArgs bwd_args(const ra_tensor *q, const ra_tensor *k, const ra_tensor *v, const ra_tensor *o,
@@ -465,6 +547,77 @@ int ra_attn_bwd_varlen(const ra_tensor *q, const ra_tensor *k, const ra_tensor *
   a.cu = cu_seqlens;
   a.n_docs = n_docs;
   return launch_attn_bwd_varlen(a, (int)q->shape[3], p->causal, (hipStream_t)stream);
+}
+
+int ra_attn_fwd_fp8_validate(const ra_tensor *q, const ra_tensor *k, const ra_tensor *vt,
+                             const ra_tensor *q_descale, const ra_tensor *k_descale,
+                             const ra_tensor *v_descale, const ra_attn_params *p,
+                             const ra_tensor *o, const ra_tensor *lse) {
+  return fp8_validate(q, k, vt, q_descale, k_descale, v_descale, p, o, lse);
+}
+
+int ra_attn_fwd_fp8(const ra_tensor *q, const ra_tensor *k, const ra_tensor *vt,
+                    const ra_tensor *q_descale, const ra_tensor *k_descale,
+                    const ra_tensor *v_descale, const ra_attn_params *p, ra_tensor *o,
+                    ra_tensor *lse, ra_stream stream) {
+  RA_TRY(fp8_validate(q, k, vt, q_descale, k_descale, v_descale, p, o, lse));
+  if (numel(q) == 0) return RA_OK;
+  Fp8Args a{};
+  FwdArgs &f = a.f;
+  f.q = q->data; f.k = k->data; f.v = vt->data; f.o = o->data; f.lse = (float *)lse->data;
+  f.q_sb = q->stride[0]; f.q_sh = q->stride[1]; f.q_ss = q->stride[2];
+  f.k_sb = k->stride[0]; f.k_sh = k->stride[1]; f.k_ss = k->stride[2];
+  f.v_sb = vt->stride[0]; f.v_sh = vt->stride[1]; f.v_ss = vt->stride[2];
+  f.o_sb = o->stride[0]; f.o_sh = o->stride[1]; f.o_ss = o->stride[2];
+  f.l_sb = lse->stride[0]; f.l_sh = lse->stride[1];
+  f.B = (int32_t)q->shape[0]; f.Hq = (int32_t)q->shape[1]; f.Sq = (int32_t)q->shape[2];
+  f.Hkv = (int32_t)k->shape[1]; f.Skv = (int32_t)k->shape[2];
+  f.group = f.Hq / f.Hkv;
+  f.num_chunks = p->num_chunks; f.start_chunk = p->start_chunk;
+  f.chunk_len = f.Skv / f.num_chunks;
+  f.q_offset = p->q_offset; f.kv_offset = p->kv_offset;
+  f.scale_log2 = effective_scale(p, q->shape[3]) * kLog2eHost;
+  f.o_is_f32 = o->dtype == RA_F32;
+  a.q_desc = (const float *)q_descale->data;
+  a.k_desc = (const float *)k_descale->data;
+  a.v_desc = (const float *)v_descale->data;
+  a.qd_sb = q_descale->stride[0]; a.qd_sh = q_descale->stride[1];
+  a.kd_sb = k_descale->stride[0]; a.kd_sh = k_descale->stride[1];
+  a.vd_sb = v_descale->stride[0]; a.vd_sh = v_descale->stride[1];
+  a.vt_cols = (int32_t)vt->shape[3];
+  return launch_attn_fwd_fp8(a, (int)q->shape[3], p->causal, (hipStream_t)stream);
+}
+
+int ra_fp8_quantize_validate(const ra_tensor *src, const ra_tensor *dst,
+                             const ra_tensor *descale, int32_t transpose) {
+  return quant_validate(src, dst, descale, transpose);
+}
+
+size_t ra_fp8_quantize_workspace_size(const ra_tensor *src) {
+  if (!src || check_tensor(src, 4, 16, false) != RA_OK) return 0;
+  return quant_workspace_bytes(src);
+}
+
+int ra_fp8_quantize(const ra_tensor *src, ra_tensor *dst, ra_tensor *descale, int32_t transpose,
+                    void *workspace, size_t workspace_bytes, ra_stream stream) {
+  RA_TRY(quant_validate(src, dst, descale, transpose));
+  const size_t need = quant_workspace_bytes(src);
+  if (!workspace || workspace_bytes < need || ((uintptr_t)workspace) % 256)
+    return RA_ERR_WORKSPACE;
+  QuantArgs a{};
+  a.src = (const uint16_t *)src->data;
+  a.dst = (uint8_t *)dst->data;
+  a.descale = (float *)descale->data;
+  a.partial = (float *)workspace;
+  a.s_sb = src->stride[0]; a.s_sh = src->stride[1]; a.s_ss = src->stride[2];
+  a.d_sb = dst->stride[0]; a.d_sh = dst->stride[1]; a.d_s2 = dst->stride[2];
+  a.ds_sb = descale->stride[0]; a.ds_sh = descale->stride[1];
+  a.B = (int32_t)src->shape[0]; a.H = (int32_t)src->shape[1];
+  a.S = (int32_t)src->shape[2]; a.D = (int32_t)src->shape[3];
+  a.S_pad = (a.S + 15) / 16 * 16;
+  a.transpose = transpose;
+  quant_split(a.S, a.D, a.nsplit, a.rows_per_split);
+  return launch_fp8_quantize(a, (hipStream_t)stream);
 }
 
 int ra_attn_bwd_accum_validate(const ra_tensor *q, const ra_tensor *k, const ra_tensor *v,

@@ -1,0 +1,362 @@
+// attn_fwd_fp8 -- exact softmax attention over e4m3 (FP8) inputs with per-head scales,
+// the ring walk and the online softmax of attn_fwd, on gfx950's 32x32x64 f8 MFMA.
+//
+// Sources (page title, host):
+//   [P4] "ms-swift集成FlashAttention 2/3，长文本训练更高效" (maplevalley.com.cn), section
+//        "FlashAttention 如何破局？不只是融合内核": FlashAttention-3 supports the FP8 data
+//        type, halving key/value traffic; tiling and the online softmax as in attn_fwd.
+//   [P2] "Ulysses与Ring-Attention序列并行技术详解" (cnvsn.com): the ring_attention_forward
+//        listing (chunks visited in turn, log-space accumulation).
+//
+// Inputs: q, k codes [B, H, S, D] and v codes TRANSPOSED, [B, Hkv, D, S_pad] (keys
+// contiguous), each with one fp32 descale per (batch, head): value = decode(code) *
+// descale.  The descales of q and k fold into the softmax scale, v's into the epilogue.
+//
+// Design (same skeleton as the bf16 direct kernel):
+//   * 8 waves x 32 query rows per workgroup; K and V^T tiles of KN keys go from global
+//     memory straight into LDS (global_load_lds_dwordx4), double-buffered, 16-byte
+//     chunks XOR-swizzled per row so every operand read is a conflict-free ds_read_b128;
+//   * S^T = K Q^T with 32x32x64 f8 MFMAs (Q in registers as the B operand): lane = one
+//     query row, 16 of each 32 keys -- row max in registers plus one v_permlane32_swap;
+//   * P' = 2^6 * exp2(c s - m) is rounded to e4m3 for O^T += V^T P'^T.  The 2^6 offset
+//     and a lazy-rescale threshold of 2 (log2 units) keep P' <= 256 < 448 while all but
+//     negligible weights (exp(s - max) >= 2^-12) stay in e4m3's normal range; the row
+//     sum adds the unrounded fp32 values, so lse carries no fp8 rounding;
+//   * after the f32 -> e4m3 conversion, one v_permlane32_swap per dword gathers each
+//     64-key group's P'^T so that half h of the wave holds keys 32h .. 32h+31 in order:
+//     the V^T operand is then a plain row read of 32 consecutive key bytes.
+// The A and B operands of the f8 MFMA pair their bytes by (lane half, byte index), and
+// the result has the usual 32x32 layout (both checked on the device).
+#include <math.h>
+
+#include "common.h"
+#include "internal.h"
+
+namespace ra {
+namespace {
+
+typedef int32_t i32x8 __attribute__((ext_vector_type(8)));
+
+// Both operands e4m3 (format codes 0); zero scale operands select the unscaled form.
+__device__ __forceinline__ f32x16 mfma_fp8(const i32x8 &a, const i32x8 &b, const f32x16 &c) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
+__device__ __forceinline__ i32x8 cat8(const u32x4 &lo, const u32x4 &hi) {
+  return i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+               (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+}
+
+constexpr float kP8Shift = 6.f;     // P' = 2^6 P
+constexpr float kLazyFp8 = 2.f;     // running max lags the true one by < 2 (log2 units)
+#ifndef RA_FP8_KN
+#define RA_FP8_KN 128               // keys per LDS tile
+#endif
+
+// 16-byte chunk swizzle of a row of RB bytes: rows sharing a 256-byte bank window
+// keep their slots apart, and 16 consecutive rows at one chunk hit 16 distinct slots.
+template <int RB>
+__device__ __forceinline__ int swz(int r) {
+  return (r / (256 / RB)) % (RB / 16);
+}
+
+template <int D, int KN>
+struct Fp8Tile {
+  static constexpr int NW = 8;
+  static constexpr int K_BYTES = KN * D;        // K tile: KN rows of D bytes
+  static constexpr int V_BYTES = D * KN;        // V^T tile: D rows of KN bytes
+  static constexpr int BUF = K_BYTES + V_BYTES;
+  static constexpr int KBPW = K_BYTES / 1024 / NW;
+  static constexpr int VBPW = V_BYTES / 1024 / NW;
+  static_assert(K_BYTES % (1024 * NW) == 0 && V_BYTES % (1024 * NW) == 0,
+                "tiles split evenly into 1-KiB direct loads per wave");
+  struct Lane {
+    int k_row[KBPW], k_col[KBPW];  // tile row and byte column of this lane's 16 bytes
+    int v_row[VBPW], v_col[VBPW];
+    uint32_t ka, va;               // operand read addresses (slot 0, before XORs)
+  };
+
+  __device__ static void setup(Lane &L, int lane, int wave, uint32_t smem0) {
+#pragma unroll
+    for (int i = 0; i < KBPW; ++i) {
+      const int byte = (wave + NW * i) * 1024 + 16 * lane;
+      const int r = byte / D, p = (byte % D) / 16;
+      L.k_row[i] = r;
+      L.k_col[i] = 16 * (p ^ swz<D>(r));
+    }
+#pragma unroll
+    for (int i = 0; i < VBPW; ++i) {
+      const int byte = (wave + NW * i) * 1024 + 16 * lane;
+      const int r = byte / KN, p = (byte % KN) / 16;
+      L.v_row[i] = r;
+      L.v_col[i] = 16 * (p ^ swz<KN>(r));
+    }
+    const int r = lane & 31, h = lane >> 5;
+    L.ka = smem0 + (uint32_t)(r * D + 16 * ((2 * h) ^ swz<D>(r)));
+    L.va = smem0 + K_BYTES + (uint32_t)(r * KN + 16 * ((2 * h) ^ swz<KN>(r)));
+  }
+
+  // Direct loads of the tile at key kb into the LDS slot at byte offset `slot`.  Rows
+  // past the last key read the last key; V^T columns past the stored row read its last
+  // 16 bytes (both are masked: their weights are exactly 0).
+  __device__ static void load(const Lane &L, const Fp8Args &a, const uint8_t *kbase,
+                              const uint8_t *vbase, int kb, uint32_t slot, int wave) {
+    const FwdArgs &f = a.f;
+#pragma unroll
+    for (int i = 0; i < KBPW; ++i) {
+      const uint32_t blk = (uint32_t)__builtin_amdgcn_readfirstlane(wave + NW * i);
+      const int row = min(kb + L.k_row[i], f.Skv - 1);
+      dma_b128(kbase, (int)(row * f.k_ss) + L.k_col[i], slot + blk * 1024);
+    }
+#pragma unroll
+    for (int i = 0; i < VBPW; ++i) {
+      const uint32_t blk = (uint32_t)__builtin_amdgcn_readfirstlane(wave + NW * i);
+      const int col = min(kb + L.v_col[i], a.vt_cols - 16);
+      dma_b128(vbase, (int)(L.v_row[i] * f.v_ss) + col, slot + K_BYTES + blk * 1024);
+    }
+  }
+
+  // K operand of S^T block mt, head-dim slice m (64 dims): row 32 mt + r, chunks
+  // 4m + 2h + {0, 1}.
+  __device__ static i32x8 k_frag(uint32_t ka, int mt, int m) {
+    const uint32_t base = ka + (uint32_t)(32 * mt * D);
+    const u32x4 lo = lds_read_b128(base ^ (uint32_t)(16 * (4 * m)));
+    const u32x4 hi = lds_read_b128(base ^ (uint32_t)(16 * (4 * m + 1)));
+    return cat8(lo, hi);
+  }
+  // V^T operand of head-dim block dt, key group g (64 keys): row 32 dt + r, chunks
+  // 4g + 2h + {0, 1} (keys 64g + 32h .. +32, in order).
+  __device__ static i32x8 v_frag(uint32_t va, int dt, int g) {
+    const uint32_t base = va + (uint32_t)(32 * dt * KN);
+    const u32x4 lo = lds_read_b128(base ^ (uint32_t)(16 * (4 * g)));
+    const u32x4 hi = lds_read_b128(base ^ (uint32_t)(16 * (4 * g + 1)));
+    return cat8(lo, hi);
+  }
+};
+
+// Next tile of the ring walk (chunks (start + t) mod P; inside a chunk, tiles stop at
+// the last key visible to the block's last query).  t == P means done.
+template <int KN>
+__device__ __forceinline__ void ring_next_fp8(const FwdArgs &a, bool causal, int64_t vis_lim,
+                                              int &t, int &kb, int &kend, int &cend) {
+  kb += KN;
+  while (kb >= kend) {
+    ++t;
+    if (t >= a.num_chunks) return;
+    int c = a.start_chunk + t;
+    if (c >= a.num_chunks) c -= a.num_chunks;
+    kb = c * a.chunk_len;
+    cend = kb + a.chunk_len;
+    kend = cend;
+    if (causal && vis_lim < (int64_t)kend) kend = vis_lim > kb ? (int)vis_lim : kb;
+  }
+}
+
+template <int D, bool CAUSAL, int KN>
+__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+attn_fwd_fp8_kernel(Fp8Args a) {
+  using T = Fp8Tile<D, KN>;
+  constexpr int NMT = KN / 32;  // 32-key S^T blocks per tile
+  constexpr int NG = KN / 64;   // 64-key PV groups per tile
+  constexpr int BM = 32 * T::NW;
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * T::BUF];
+  const FwdArgs &f = a.f;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  const int r32 = lane & 31;
+  const int h = lane >> 5;
+
+  const int HB = f.Hq * f.B;
+  const int bid = blockIdx.x;
+  const int trank = bid / HB;
+  int j = bid - trank * HB;
+  if ((HB & 7) == 0) j = (j & 7) * (HB >> 3) + (j >> 3);
+  const int hq = j % f.Hq;
+  const int b = j / f.Hq;
+  const int qt = f.num_q_tiles - 1 - trank;
+  const int hk = hq / f.group;
+
+  const int q0 = qt * BM;
+  const int qlast = min(q0 + BM, f.Sq) - 1;
+  const uint8_t *qbase = (const uint8_t *)f.q + b * f.q_sb + hq * f.q_sh;
+  const uint8_t *kbase = (const uint8_t *)f.k + b * f.k_sb + hk * f.k_sh;
+  const uint8_t *vbase = (const uint8_t *)f.v + b * f.v_sb + hk * f.v_sh;
+
+  const int qrow = q0 + 32 * wave + r32;
+  const int64_t qpos = f.q_offset + qrow;
+  const int64_t wpos_first = f.q_offset + q0 + 32 * wave_u;
+  const int64_t wpos_last = wpos_first + 31;
+  const bool wave_active = (q0 + 32 * wave_u) < f.Sq;
+  const float c = f.scale_log2 * a.q_desc[b * a.qd_sb + hq * a.qd_sh] *
+                  a.k_desc[b * a.kd_sb + hk * a.kd_sh];
+  const float vdesc = a.v_desc[b * a.vd_sb + hk * a.vd_sh];
+
+  const uint32_t smem0 = lds_offset(smem);
+  typename T::Lane L;
+  T::setup(L, lane, wave, smem0);
+
+  // Q as the B operand: head-dim slice m holds bytes 64m + 32h .. +32 of this row.
+  i32x8 qf[D / 64];
+  {
+    const uint8_t *qr = qbase + (int64_t)min(qrow, f.Sq - 1) * f.q_ss;
+#pragma unroll
+    for (int m = 0; m < D / 64; ++m)
+      qf[m] = cat8(*(const u32x4 *)(qr + 64 * m + 32 * h),
+                   *(const u32x4 *)(qr + 64 * m + 32 * h + 16));
+  }
+
+  f32x16 o[D / 32];
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt) o[dt] = f32x16{};
+  float m_run = -INFINITY;
+  float l_run = 0.f;
+
+  const int64_t vis_lim = f.q_offset + qlast - f.kv_offset + 1;
+  int t = -1, kb = 0, kend = 0, cend = 0;
+  ring_next_fp8<KN>(f, CAUSAL, vis_lim, t, kb, kend, cend);
+  if (t < f.num_chunks) T::load(L, a, kbase, vbase, kb, smem0, wave);
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): Q and the first tile have landed
+  __syncthreads();
+
+  int cur = 0;
+  while (t < f.num_chunks) {
+    const int kb_cur = kb, cend_cur = cend;
+    ring_next_fp8<KN>(f, CAUSAL, vis_lim, t, kb, kend, cend);
+    if (t < f.num_chunks) T::load(L, a, kbase, vbase, kb, smem0 + (cur ^ 1) * T::BUF, wave);
+
+    const int64_t kpos0 = f.kv_offset + kb_cur;
+    if (wave_active && !(CAUSAL && kpos0 > wpos_last)) {
+      const uint32_t slot = (uint32_t)(cur * T::BUF);
+      // S^T = K Q^T
+      f32x16 s[NMT];
+#pragma unroll
+      for (int mt = 0; mt < NMT; ++mt) {
+        s[mt] = f32x16{};
+#pragma unroll
+        for (int m = 0; m < D / 64; ++m) s[mt] = mfma_fp8(T::k_frag(L.ka + slot, mt, m), qf[m], s[mt]);
+      }
+      const int kvalid = min(KN, cend_cur - kb_cur);
+      const bool need_mask = (kvalid < KN) || (CAUSAL && kpos0 + kvalid - 1 > wpos_first);
+      if (need_mask) {
+        int lim = kvalid;  // keys kk < lim are visible to this lane's row
+        if (CAUSAL) {
+          const int64_t vis = qpos - kpos0 + 1;
+          lim = vis < (int64_t)lim ? (vis > 0 ? (int)vis : 0) : lim;
+        }
+        lim -= 4 * h;
+#pragma unroll
+        for (int mt = 0; mt < NMT; ++mt)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int kk = 32 * mt + (i >> 2) * 8 + (i & 3);
+            s[mt][i] = kk < lim ? s[mt][i] : -INFINITY;
+          }
+      }
+      float mx = fmaxf(fmaxf(s[0][0], s[0][1]), s[0][2]);
+#pragma unroll
+      for (int i = 3; i < 15; i += 2) mx = fmaxf(fmaxf(mx, s[0][i]), s[0][i + 1]);
+      mx = fmaxf(mx, s[0][15]);
+#pragma unroll
+      for (int mt = 1; mt < NMT; ++mt)
+#pragma unroll
+        for (int i = 0; i < 16; i += 2) mx = fmaxf(fmaxf(mx, s[mt][i]), s[mt][i + 1]);
+      mx = halves_max(mx) * c;
+      if (__builtin_amdgcn_ballot_w64(mx > m_run + kLazyFp8) != 0) {
+        const float m_new = fmaxf(m_run, mx);
+        const float alpha = m_new == -INFINITY ? 1.f : fast_exp2(m_run - m_new);
+        l_run *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt) o[dt] *= alpha;
+        m_run = m_new;
+      }
+      const float mneg = (m_run == -INFINITY ? 0.f : -m_run) + kP8Shift;
+      // P' -> e4m3: dword a of block mt holds the keys of registers 4a .. 4a+3
+      uint32_t pw[NMT][4];
+      float acc0 = 0.f, acc1 = 0.f;
+#pragma unroll
+      for (int mt = 0; mt < NMT; ++mt)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const float p0 = fast_exp2(fmaf(s[mt][4 * q4 + 0], c, mneg));
+          const float p1 = fast_exp2(fmaf(s[mt][4 * q4 + 1], c, mneg));
+          const float p2 = fast_exp2(fmaf(s[mt][4 * q4 + 2], c, mneg));
+          const float p3 = fast_exp2(fmaf(s[mt][4 * q4 + 3], c, mneg));
+          int w = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, 0, false);
+          w = __builtin_amdgcn_cvt_pk_fp8_f32(p2, p3, w, true);
+          pw[mt][q4] = (uint32_t)w;
+          acc0 += p0 + p1;
+          acc1 += p2 + p3;
+        }
+      l_run += acc0 + acc1;
+      // O^T += V^T P'^T, one 64-key group at a time
+#pragma unroll
+      for (int g = 0; g < NG; ++g) {
+        i32x8 pf;
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          // half 0 keeps block 2g and receives half 1's block 2g; half 1 the reverse
+          const auto sw = __builtin_amdgcn_permlane32_swap(pw[2 * g][q4], pw[2 * g + 1][q4],
+                                                           false, false);
+          pf[2 * q4] = (int)sw[0];
+          pf[2 * q4 + 1] = (int)sw[1];
+        }
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt) o[dt] = mfma_fp8(T::v_frag(L.va + slot, dt, g), pf, o[dt]);
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the next tile's direct loads landed
+    __syncthreads();
+    cur ^= 1;
+  }
+
+  const float l_tot = halves_sum(l_run);
+  const float inv = l_tot > 0.f ? vdesc / l_tot : 0.f;
+  if (qrow < f.Sq) {
+    if (h == 0) {
+      const float lse = l_tot > 0.f ? (m_run - kP8Shift + __log2f(l_tot)) * kLn2 : -INFINITY;
+      f.lse[b * f.l_sb + hq * f.l_sh + qrow] = lse;
+    }
+    const int64_t orow = b * f.o_sb + hq * f.o_sh + (int64_t)qrow * f.o_ss;
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int d = 32 * dt + 8 * g4 + 4 * h;
+        const float x0 = o[dt][4 * g4 + 0] * inv, x1 = o[dt][4 * g4 + 1] * inv;
+        const float x2 = o[dt][4 * g4 + 2] * inv, x3 = o[dt][4 * g4 + 3] * inv;
+        if (f.o_is_f32) {
+          *(float4 *)((float *)f.o + orow + d) = float4{x0, x1, x2, x3};
+        } else {
+          const bf16x2 lo = __builtin_convertvector((f32x2){x0, x1}, bf16x2);
+          const bf16x2 hi = __builtin_convertvector((f32x2){x2, x3}, bf16x2);
+          *(u32x2 *)((uint16_t *)f.o + orow + d) =
+              u32x2{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
+        }
+      }
+  }
+}
+
+template <int D, bool CAUSAL>
+int launch_fp8(const Fp8Args &args, hipStream_t stream) {
+  Fp8Args a = args;
+  constexpr int KN = RA_FP8_KN;
+  a.f.num_q_tiles = (a.f.Sq + 255) / 256;
+  const int64_t blocks = (int64_t)a.f.num_q_tiles * a.f.Hq * a.f.B;
+  if (blocks <= 0) return RA_OK;
+  hipLaunchKernelGGL((attn_fwd_fp8_kernel<D, CAUSAL, KN>), dim3((unsigned)blocks), dim3(512), 0,
+                     stream, a);
+  return hipGetLastError() == hipSuccess ? RA_OK : RA_ERR_HIP;
+}
+
+}  // namespace
+
+int launch_attn_fwd_fp8(const Fp8Args &a, int D, int causal, hipStream_t stream) {
+  if (D == 128) return causal ? launch_fp8<128, true>(a, stream) : launch_fp8<128, false>(a, stream);
+  if (D == 64) return causal ? launch_fp8<64, true>(a, stream) : launch_fp8<64, false>(a, stream);
+  return RA_ERR_UNSUPPORTED;
+}
+
+}  // namespace ra

@@ -1,0 +1,175 @@
+// fp8_quantize -- bf16 [B, H, S, D] -> e4m3 codes with one fp32 scale per (batch, head),
+// optionally transposed to [B, H, D, S_pad] (the V^T layout the FP8 attention reads).
+//
+// [P4] "ms-swift集成FlashAttention 2/3，长文本训练更高效" (maplevalley.com.cn), section
+// "FlashAttention 如何破局？不只是融合内核": FlashAttention-3 supports the FP8 data type,
+// halving the key/value traffic.  The scaling rule is a reading (the pages give none):
+// with a = max |x| over the head, codes = e4m3(clamp(x * (448 / a), -448, 448)) with an
+// fp32 multiply and round-to-nearest-even conversion, descale = a / 448 (an all-zero
+// head: 1, 1); the value of a code is decode(code) * descale.
+//
+// Two passes, both bound by HBM bandwidth and deterministic (a max does not depend on
+// the order it is taken in): partial maxima per (head, row range) into the workspace,
+// then every block folds its head's partials and converts its rows (or, transposed,
+// a 64-token x D tile through LDS).
+#include <math.h>
+
+#include "common.h"
+#include "internal.h"
+
+namespace ra {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr float kE4m3Max = 448.f;
+
+__device__ __forceinline__ float block_max(float v, float *red) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  __syncthreads();  // `red` may still be read from a previous call
+  if (lane == 0) red[wave] = v;
+  __syncthreads();
+  return fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+}
+
+// max |x| of 8 bf16 values
+__device__ __forceinline__ float absmax8(const u32x4 &x) {
+  float m = 0.f;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    m = fmaxf(m, fabsf(bf16_bits_to_float(x[w] & 0xffffu)));
+    m = fmaxf(m, fabsf(bf16_bits_to_float(x[w] >> 16)));
+  }
+  return m;
+}
+
+__global__ void __launch_bounds__(kThreads) quant_amax_kernel(QuantArgs a) {
+  __shared__ float red[4];
+  const int bh = blockIdx.x / a.nsplit, sp = blockIdx.x % a.nsplit;
+  const int b = bh / a.H, h = bh % a.H;
+  const int r0 = sp * a.rows_per_split, r1 = min(a.S, r0 + a.rows_per_split);
+  const int ppr = a.D / 8;  // 16-byte pieces per row
+  const uint16_t *src = a.src + b * a.s_sb + h * a.s_sh;
+  float m = 0.f;
+  for (int p = threadIdx.x; p < (r1 - r0) * ppr; p += kThreads) {
+    const int r = r0 + p / ppr, c = p % ppr;
+    m = fmaxf(m, absmax8(*(const u32x4 *)(src + (int64_t)r * a.s_ss + 8 * c)));
+  }
+  m = block_max(m, red);
+  if (threadIdx.x == 0) a.partial[blockIdx.x] = m;
+}
+
+// The head's max from its partials; r = 448 / a (fp32, correctly rounded division).
+__device__ __forceinline__ float head_ratio(const QuantArgs &a, int bh, bool write_descale,
+                                            float *red) {
+  float m = 0.f;
+  for (int i = threadIdx.x; i < a.nsplit; i += kThreads) m = fmaxf(m, a.partial[bh * a.nsplit + i]);
+  m = block_max(m, red);
+  if (write_descale && threadIdx.x == 0) {
+    const int b = bh / a.H, h = bh % a.H;
+    a.descale[b * a.ds_sb + h * a.ds_sh] = m > 0.f ? m / kE4m3Max : 1.f;
+  }
+  return m > 0.f ? kE4m3Max / m : 1.f;
+}
+
+// Two values -> two e4m3 codes in the low (HI = false) or high 16 bits of `old`.
+template <bool HI>
+__device__ __forceinline__ int cvt2(float x0, float x1, float r, int old) {
+  const float y0 = fminf(fmaxf(x0 * r, -kE4m3Max), kE4m3Max);
+  const float y1 = fminf(fmaxf(x1 * r, -kE4m3Max), kE4m3Max);
+  return __builtin_amdgcn_cvt_pk_fp8_f32(y0, y1, old, HI);
+}
+
+__device__ __forceinline__ u32x2 cvt8(const u32x4 &x, float r) {
+  uint32_t out[2];
+#pragma unroll
+  for (int w2 = 0; w2 < 2; ++w2) {
+    const uint32_t a0 = x[2 * w2], a1 = x[2 * w2 + 1];
+    int v = cvt2<false>(bf16_bits_to_float(a0 & 0xffffu), bf16_bits_to_float(a0 >> 16), r, 0);
+    v = cvt2<true>(bf16_bits_to_float(a1 & 0xffffu), bf16_bits_to_float(a1 >> 16), r, v);
+    out[w2] = (uint32_t)v;
+  }
+  return u32x2{out[0], out[1]};
+}
+
+__global__ void __launch_bounds__(kThreads) quant_convert_kernel(QuantArgs a) {
+  __shared__ float red[4];
+  const int bh = blockIdx.x / a.nsplit, sp = blockIdx.x % a.nsplit;
+  const int b = bh / a.H, h = bh % a.H;
+  const float r = head_ratio(a, bh, sp == 0, red);
+  const int r0 = sp * a.rows_per_split, r1 = min(a.S, r0 + a.rows_per_split);
+  const int ppr = a.D / 8;
+  const uint16_t *src = a.src + b * a.s_sb + h * a.s_sh;
+  uint8_t *dst = a.dst + b * a.d_sb + h * a.d_sh;
+  for (int p = threadIdx.x; p < (r1 - r0) * ppr; p += kThreads) {
+    const int row = r0 + p / ppr, c = p % ppr;
+    const u32x4 x = *(const u32x4 *)(src + (int64_t)row * a.s_ss + 8 * c);
+    *(u32x2 *)(dst + (int64_t)row * a.d_s2 + 8 * c) = cvt8(x, r);
+  }
+}
+
+// Transposed: one block per (head, 64-token tile).  Codes go through LDS as
+// [D][64 + 4] bytes; each output row piece is 16 consecutive tokens of one head dim.
+// Tokens S .. S_pad-1 get code 0.
+constexpr int kTT = 64;           // tokens per tile
+constexpr int kTRow = kTT + 4;    // LDS row bytes (4-byte aligned, spreads banks)
+
+__global__ void __launch_bounds__(kThreads) quant_convert_t_kernel(QuantArgs a, int ntiles) {
+  __shared__ float red[4];
+  __shared__ __attribute__((aligned(16))) uint8_t tile[256 * kTRow];
+  const int bh = blockIdx.x / ntiles, tt = blockIdx.x % ntiles;
+  const int b = bh / a.H, h = bh % a.H;
+  const float r = head_ratio(a, bh, tt == 0, red);
+  const int t0 = tt * kTT;
+  const int ppr = a.D / 8;
+  const uint16_t *src = a.src + b * a.s_sb + h * a.s_sh;
+  for (int p = threadIdx.x; p < kTT * ppr; p += kThreads) {
+    const int tok = p / ppr, c = p % ppr;
+    u32x2 codes = u32x2{0u, 0u};
+    if (t0 + tok < a.S)
+      codes = cvt8(*(const u32x4 *)(src + (int64_t)(t0 + tok) * a.s_ss + 8 * c), r);
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      tile[(8 * c + i) * kTRow + tok] = (uint8_t)(codes[i >> 2] >> (8 * (i & 3)));
+  }
+  __syncthreads();
+  uint8_t *dst = a.dst + b * a.d_sb + h * a.d_sh;
+  for (int p = threadIdx.x; p < a.D * (kTT / 16); p += kThreads) {
+    const int d = p / (kTT / 16), k16 = p % (kTT / 16);
+    const int col = t0 + 16 * k16;
+    if (col >= a.S_pad) continue;
+    const uint32_t *src4 = (const uint32_t *)(tile + d * kTRow + 16 * k16);
+    *(u32x4 *)(dst + (int64_t)d * a.d_s2 + col) = u32x4{src4[0], src4[1], src4[2], src4[3]};
+  }
+}
+
+}  // namespace
+
+// Row ranges of the first pass: about 128 KiB of bf16 per block, at most 1024 per head.
+void quant_split(int64_t S, int64_t D, int32_t &nsplit, int32_t &rows_per_split) {
+  int64_t n = (S * D * 2 + (128 << 10) - 1) / (128 << 10);
+  n = n < 1 ? 1 : (n > 1024 ? 1024 : n);
+  int64_t rps = S > 0 ? (S + n - 1) / n : 1;
+  nsplit = (int32_t)(S > 0 ? (S + rps - 1) / rps : 1);
+  rows_per_split = (int32_t)rps;
+}
+
+int launch_fp8_quantize(const QuantArgs &a, hipStream_t stream) {
+  const int64_t nbh = (int64_t)a.B * a.H;
+  if (nbh == 0) return RA_OK;
+  hipLaunchKernelGGL(quant_amax_kernel, dim3((unsigned)(nbh * a.nsplit)), dim3(kThreads), 0,
+                     stream, a);
+  if (a.transpose) {
+    // at least one tile per head, so that an empty head still gets its descale
+    const int ntiles = a.S_pad > 0 ? (a.S_pad + kTT - 1) / kTT : 1;
+    hipLaunchKernelGGL(quant_convert_t_kernel, dim3((unsigned)(nbh * ntiles)), dim3(kThreads),
+                         0, stream, a, ntiles);
+  } else {
+    hipLaunchKernelGGL(quant_convert_kernel, dim3((unsigned)(nbh * a.nsplit)), dim3(kThreads), 0,
+                       stream, a);
+  }
+  return hipGetLastError() == hipSuccess ? RA_OK : RA_ERR_HIP;
+}
+
+}  // namespace ra

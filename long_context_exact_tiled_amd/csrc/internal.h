@@ -91,6 +91,33 @@ struct BwdArgs {
   int32_t n_docs;
 };
 
+// Attention over e4m3 inputs: the FwdArgs problem (q, k codes; v holds V^T codes
+// [B, Hkv, D, vt_cols] with f.v_sb, f.v_sh its batch/head strides and f.v_ss the stride
+// between its head-dim rows, all in bytes) plus one fp32 descale per (batch, head).
+struct Fp8Args {
+  FwdArgs f;
+  const float *q_desc, *k_desc, *v_desc;
+  int64_t qd_sb, qd_sh, kd_sb, kd_sh, vd_sb, vd_sh;
+  int32_t vt_cols;  // stored keys per V^T row (Skv rounded up to 16)
+};
+
+int launch_attn_fwd_fp8(const Fp8Args &a, int D, int causal, hipStream_t stream);
+
+// Per-head e4m3 quantization of a bf16 tensor [B, H, S, D]: partial maxima, then codes.
+struct QuantArgs {
+  const uint16_t *src;
+  uint8_t *dst;
+  float *descale;
+  float *partial;            // workspace: B*H*nsplit partial maxima
+  int64_t s_sb, s_sh, s_ss;  // src strides (elements)
+  int64_t d_sb, d_sh, d_s2;  // dst strides (bytes); d_s2: token stride, or head-dim row stride (transposed)
+  int64_t ds_sb, ds_sh;      // descale strides
+  int32_t B, H, S, D, S_pad, nsplit, rows_per_split, transpose;
+};
+
+void quant_split(int64_t S, int64_t D, int32_t &nsplit, int32_t &rows_per_split);
+int launch_fp8_quantize(const QuantArgs &a, hipStream_t stream);
+
 size_t bwd_workspace_bytes(int64_t B, int64_t Hq, int64_t Sq);
 int launch_attn_bwd(const BwdArgs &a, int D, int causal, hipStream_t stream);
 int launch_attn_bwd_varlen(const BwdArgs &a, int D, int causal, hipStream_t stream);

@@ -105,6 +105,8 @@ class Workload:
     backward: bool = False
     # packed documents (cu_seqlens drawn by draw_doc_offsets from this workload's seed)
     packed_docs: bool = False
+    # inputs quantized to e4m3 with one scale per (batch, head) before the attention
+    fp8: bool = False
 
 
 def draw_doc_offsets(seed: int, total: int, median: int = 2048, sigma: float = 1.0,
@@ -150,6 +152,10 @@ WORKLOADS: Dict[str, Workload] = {
         name="ring8_rank3_bwd_32k", dtype="bf16",
         q_shape=(1, 32, 4096, 128), kv_shape=(1, 32, 32768, 128),
         causal=True, num_chunks=8, start_chunk=3, q_offset=3 * 4096, seed=1007, backward=True),
+    "qwen7b_gqa_32k_fp8": Workload(
+        name="qwen7b_gqa_32k_fp8", dtype="bf16",
+        q_shape=(1, 7, 32768, 128), kv_shape=(1, 1, 32768, 128),
+        causal=True, seed=1008, fp8=True),
     "llama7b_causal_bwd_16k": Workload(
         name="llama7b_causal_bwd_16k", dtype="bf16",
         q_shape=(1, 32, 16384, 128), kv_shape=(1, 32, 16384, 128),

@@ -200,3 +200,46 @@ def test_bwd_accum_validation(ra):
     # a transposed (overlapping-free but non-unit last stride) accumulator is refused
     assert val(q, k, v, o, do, lse, dq, dk, f32((1, 2, 128, 32)).transpose(2, 3)) == \
         "RA_ERR_STRIDE"
+
+
+def test_fp8_validation(ra):
+    f8 = lambda shape: torch.zeros(shape, dtype=torch.uint8).view(torch.float8_e4m3fn)
+    q, k, vt = f8((1, 4, 64, 128)), f8((1, 2, 40, 128)), f8((1, 2, 128, 48))
+    qd, kd, vd = torch.ones(1, 4), torch.ones(1, 2), torch.ones(1, 2)
+    o, lse = _t((1, 4, 64, 128)), torch.zeros(1, 4, 64)
+    val = lambda *a, **kw: ra.STATUS[ra.attn_fwd_fp8_validate(*a, **kw)]
+    assert val(q, k, vt, qd, kd, vd, o, lse, causal=True) == "RA_OK"
+    assert val(q, k, vt, qd, kd, vd, o.float(), lse, num_chunks=2, start_chunk=1) == "RA_OK"
+    assert val(q, k, f8((1, 2, 128, 40)), qd, kd, vd, o, lse) == "RA_ERR_ALIGN"  # rows of 40 B
+    assert val(q, k, f8((1, 2, 128, 64)), qd, kd, vd, o, lse) == "RA_ERR_SHAPE"  # not S_pad
+    assert val(q, k, f8((1, 2, 40, 128)), qd, kd, vd, o, lse) == "RA_ERR_SHAPE"  # not transposed
+    assert val(q, k, vt, qd, kd, vd, o, lse, num_chunks=3) == "RA_ERR_SHAPE"
+    assert val(q, _t((1, 2, 40, 128)), vt, qd, kd, vd, o, lse) == "RA_ERR_DTYPE"
+    assert val(q, k, vt, torch.ones(1, 2), kd, vd, o, lse) == "RA_ERR_SHAPE"
+    assert val(q, k, vt, qd, kd, vd, q, lse) == "RA_ERR_DTYPE"  # fp8 output refused
+    q64, k64, vt64 = f8((1, 4, 64, 96)), f8((1, 2, 40, 96)), f8((1, 2, 96, 48))
+    assert val(q64, k64, vt64, qd, kd, vd, _t((1, 4, 64, 96)), lse) == "RA_ERR_UNSUPPORTED"
+    # fp8 inputs are refused by the bf16/fp32 entry points and the merge
+    assert ra.STATUS[ra.attn_fwd_validate(q, f8((1, 2, 40, 128)), f8((1, 2, 40, 128)), o,
+                                          lse)] == "RA_ERR_DTYPE"
+    assert ra.STATUS[ra.lse_merge_validate([q], [lse], q, lse)] == "RA_ERR_DTYPE"
+
+
+def test_fp8_quantize_validation(ra):
+    x = _t((1, 3, 37, 64))
+    codes, codes_t = torch.zeros(1, 3, 37, 64, dtype=torch.uint8), torch.zeros(1, 3, 64, 48,
+                                                                              dtype=torch.uint8)
+    as8 = lambda t: t.view(torch.float8_e4m3fn)
+    desc = torch.zeros(1, 3)
+    val = lambda *a, **kw: ra.STATUS[ra.fp8_quantize_validate(*a, **kw)]
+    assert val(x, as8(codes), desc) == "RA_OK"
+    assert val(x, as8(codes_t), desc, transpose=True) == "RA_OK"
+    assert val(x, as8(codes_t), desc) == "RA_ERR_SHAPE"
+    assert val(x, as8(codes), desc, transpose=True) == "RA_ERR_SHAPE"
+    assert val(x.float(), as8(codes), desc) == "RA_ERR_DTYPE"
+    assert val(x, _t((1, 3, 37, 64)), desc) == "RA_ERR_DTYPE"
+    assert val(x, as8(codes), torch.zeros(1, 2)) == "RA_ERR_SHAPE"
+    assert val(x, as8(codes), desc.bfloat16()) == "RA_ERR_DTYPE"
+    assert val(_t((1, 3, 37, 8)), as8(torch.zeros(1, 3, 37, 8, dtype=torch.uint8)), desc) == \
+        "RA_ERR_ALIGN"
+    assert ra.lib().ra_fp8_quantize_workspace_size(ra.desc(x)) >= 3 * 4
