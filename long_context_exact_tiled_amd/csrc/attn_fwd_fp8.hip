@@ -29,6 +29,8 @@
 // the result has the usual 32x32 layout (both checked on the device).
 #include <math.h>
 
+#include <type_traits>
+
 #include "common.h"
 #include "internal.h"
 
@@ -70,10 +72,14 @@ struct Fp8Tile {
   static constexpr int VBPW = V_BYTES / 1024 / NW;
   static_assert(K_BYTES % (1024 * NW) == 0 && V_BYTES % (1024 * NW) == 0,
                 "tiles split evenly into 1-KiB direct loads per wave");
+  static constexpr int KM = D / 64;   // 64-dim slices of a K row
+  static constexpr int NG = KN / 64;   // 64-key groups of a V^T row
   struct Lane {
     int k_row[KBPW], k_col[KBPW];  // tile row and byte column of this lane's 16 bytes
     int v_row[VBPW], v_col[VBPW];
-    uint32_t ka, va;               // operand read addresses (slot 0, before XORs)
+    // operand read addresses in slot 0: K chunk 4m + 2h + e of row r, V^T chunk
+    // 4g + 2h + e of row r (swizzled); block and slot offsets are immediates
+    uint32_t ka[KM][2], va[NG][2];
   };
 
   __device__ static void setup(Lane &L, int lane, int wave, uint32_t smem0) {
@@ -92,8 +98,15 @@ struct Fp8Tile {
       L.v_col[i] = 16 * (p ^ swz<KN>(r));
     }
     const int r = lane & 31, h = lane >> 5;
-    L.ka = smem0 + (uint32_t)(r * D + 16 * ((2 * h) ^ swz<D>(r)));
-    L.va = smem0 + K_BYTES + (uint32_t)(r * KN + 16 * ((2 * h) ^ swz<KN>(r)));
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+#pragma unroll
+      for (int m = 0; m < KM; ++m)
+        L.ka[m][e] = smem0 + (uint32_t)(r * D + 16 * ((4 * m + 2 * h + e) ^ swz<D>(r)));
+#pragma unroll
+      for (int g = 0; g < NG; ++g)
+        L.va[g][e] = smem0 + K_BYTES + (uint32_t)(r * KN + 16 * ((4 * g + 2 * h + e) ^ swz<KN>(r)));
+    }
   }
 
   // Direct loads of the tile at key kb into the LDS slot at byte offset `slot`.  Rows
@@ -117,20 +130,18 @@ struct Fp8Tile {
   }
 
   // K operand of S^T block mt, head-dim slice m (64 dims): row 32 mt + r, chunks
-  // 4m + 2h + {0, 1}.
-  __device__ static i32x8 k_frag(uint32_t ka, int mt, int m) {
-    const uint32_t base = ka + (uint32_t)(32 * mt * D);
-    const u32x4 lo = lds_read_b128(base ^ (uint32_t)(16 * (4 * m)));
-    const u32x4 hi = lds_read_b128(base ^ (uint32_t)(16 * (4 * m + 1)));
-    return cat8(lo, hi);
+  // 4m + 2h + {0, 1}.  SLOT: byte offset of the LDS buffer (a compile-time constant).
+  template <uint32_t SLOT>
+  __device__ static i32x8 k_frag(const Lane &L, int mt, int m) {
+    const uint32_t off = SLOT + (uint32_t)(32 * mt * D);
+    return cat8(lds_read_b128(L.ka[m][0] + off), lds_read_b128(L.ka[m][1] + off));
   }
   // V^T operand of head-dim block dt, key group g (64 keys): row 32 dt + r, chunks
   // 4g + 2h + {0, 1} (keys 64g + 32h .. +32, in order).
-  __device__ static i32x8 v_frag(uint32_t va, int dt, int g) {
-    const uint32_t base = va + (uint32_t)(32 * dt * KN);
-    const u32x4 lo = lds_read_b128(base ^ (uint32_t)(16 * (4 * g)));
-    const u32x4 hi = lds_read_b128(base ^ (uint32_t)(16 * (4 * g + 1)));
-    return cat8(lo, hi);
+  template <uint32_t SLOT>
+  __device__ static i32x8 v_frag(const Lane &L, int dt, int g) {
+    const uint32_t off = SLOT + (uint32_t)(32 * dt * KN);
+    return cat8(lds_read_b128(L.va[g][0] + off), lds_read_b128(L.va[g][1] + off));
   }
 };
 
@@ -221,22 +232,27 @@ attn_fwd_fp8_kernel(Fp8Args a) {
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): Q and the first tile have landed
   __syncthreads();
 
-  int cur = 0;
-  while (t < f.num_chunks) {
+  // One tile: issue the next tile's loads into the other slot, then S^T, softmax and
+  // O^T += V^T P'^T from slot CUR.  Returns false when the walk is done.  The loop runs
+  // the two slots alternately so that every LDS operand offset is an immediate.
+  auto tile = [&](auto cur_c) -> bool {
+    constexpr int CUR = decltype(cur_c)::value;
+    constexpr uint32_t SLOT = (uint32_t)(CUR * T::BUF);
     const int kb_cur = kb, cend_cur = cend;
     ring_next_fp8<KN>(f, CAUSAL, vis_lim, t, kb, kend, cend);
-    if (t < f.num_chunks) T::load(L, a, kbase, vbase, kb, smem0 + (cur ^ 1) * T::BUF, wave);
+    const bool has_next = t < f.num_chunks;
+    if (has_next) T::load(L, a, kbase, vbase, kb, smem0 + (CUR ^ 1) * T::BUF, wave);
 
     const int64_t kpos0 = f.kv_offset + kb_cur;
     if (wave_active && !(CAUSAL && kpos0 > wpos_last)) {
-      const uint32_t slot = (uint32_t)(cur * T::BUF);
       // S^T = K Q^T
       f32x16 s[NMT];
 #pragma unroll
       for (int mt = 0; mt < NMT; ++mt) {
-        s[mt] = f32x16{};
+        s[mt] = mfma_fp8(T::template k_frag<SLOT>(L, mt, 0), qf[0], f32x16{});
 #pragma unroll
-        for (int m = 0; m < D / 64; ++m) s[mt] = mfma_fp8(T::k_frag(L.ka + slot, mt, m), qf[m], s[mt]);
+        for (int m = 1; m < D / 64; ++m)
+          s[mt] = mfma_fp8(T::template k_frag<SLOT>(L, mt, m), qf[m], s[mt]);
       }
       const int kvalid = min(KN, cend_cur - kb_cur);
       const bool need_mask = (kvalid < KN) || (CAUSAL && kpos0 + kvalid - 1 > wpos_first);
@@ -273,8 +289,13 @@ attn_fwd_fp8_kernel(Fp8Args a) {
         m_run = m_new;
       }
       const float mneg = (m_run == -INFINITY ? 0.f : -m_run) + kP8Shift;
-      // P' -> e4m3: dword a of block mt holds the keys of registers 4a .. 4a+3
-      uint32_t pw[NMT][4];
+      // P' -> e4m3, two values per conversion.  The first conversion of a dword fills its
+      // low half and keeps the high half of its `old` operand, which the second
+      // conversion overwrites: `old` is a score that is dead by then, so no register has
+      // to be cleared or copied for it.
+      // Dwords of block mt go straight into the P'^T operand of its 64-key group g = mt/2:
+      // element 2 q4 + (mt & 1) holds the keys of registers 4 q4 .. 4 q4 + 3.
+      i32x8 pf[NG];
       float acc0 = 0.f, acc1 = 0.f;
 #pragma unroll
       for (int mt = 0; mt < NMT; ++mt)
@@ -284,32 +305,37 @@ attn_fwd_fp8_kernel(Fp8Args a) {
           const float p1 = fast_exp2(fmaf(s[mt][4 * q4 + 1], c, mneg));
           const float p2 = fast_exp2(fmaf(s[mt][4 * q4 + 2], c, mneg));
           const float p3 = fast_exp2(fmaf(s[mt][4 * q4 + 3], c, mneg));
-          int w = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, 0, false);
-          w = __builtin_amdgcn_cvt_pk_fp8_f32(p2, p3, w, true);
-          pw[mt][q4] = (uint32_t)w;
+          int w = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, __float_as_int(s[mt][4 * q4 + 3]),
+                                                  false);
+          pf[mt >> 1][2 * q4 + (mt & 1)] = __builtin_amdgcn_cvt_pk_fp8_f32(p2, p3, w, true);
           acc0 += p0 + p1;
           acc1 += p2 + p3;
         }
       l_run += acc0 + acc1;
-      // O^T += V^T P'^T, one 64-key group at a time
+      // O^T += V^T P'^T, one 64-key group at a time.  The swap leaves half 0 with block
+      // 2g's dword of its own and half 1's (keys 4w .. 4w+3 in dword w), half 1 with both
+      // halves' block 2g+1 dwords: half h holds keys 32h .. 32h+31 in order.
 #pragma unroll
       for (int g = 0; g < NG; ++g) {
-        i32x8 pf;
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) {
-          // half 0 keeps block 2g and receives half 1's block 2g; half 1 the reverse
-          const auto sw = __builtin_amdgcn_permlane32_swap(pw[2 * g][q4], pw[2 * g + 1][q4],
+          const auto sw = __builtin_amdgcn_permlane32_swap(pf[g][2 * q4], pf[g][2 * q4 + 1],
                                                            false, false);
-          pf[2 * q4] = (int)sw[0];
-          pf[2 * q4 + 1] = (int)sw[1];
+          pf[g][2 * q4] = (int)sw[0];
+          pf[g][2 * q4 + 1] = (int)sw[1];
         }
 #pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt) o[dt] = mfma_fp8(T::v_frag(L.va + slot, dt, g), pf, o[dt]);
+        for (int dt = 0; dt < D / 32; ++dt)
+          o[dt] = mfma_fp8(T::template v_frag<SLOT>(L, dt, g), pf[g], o[dt]);
       }
     }
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the next tile's direct loads landed
     __syncthreads();
-    cur ^= 1;
+    return has_next;
+  };
+  if (t < f.num_chunks) {
+    while (tile(std::integral_constant<int, 0>{}) && tile(std::integral_constant<int, 1>{})) {
+    }
   }
 
   const float l_tot = halves_sum(l_run);
