@@ -42,6 +42,8 @@
 //     dispatcher spreads over the 8 XCDs -- land on XCDs that share key/value heads.
 #include <math.h>
 
+#include <type_traits>
+
 #include "common.h"
 #include "internal.h"
 
@@ -318,8 +320,9 @@ struct Bf16DirectPath {
     int k_goff[BPW], v_goff[BPW];  // byte offsets of this lane's 16 B in the tile (row 0 = kb)
     int row0;                      // tile row of piece 0; piece i is RSTEP*i rows further
     int k_chunk, v_chunk;          // the 16-byte chunk within the row (the same for every i)
-    uint32_t ka;                   // K operand read address (before the ks XOR), slot 0
-    uint32_t vb;                   // V operand read address (before the dt XOR), slot 0
+    // operand read addresses per LDS slot: K for head-dim step ks, V^T for block dt
+    // (the swizzle XORs applied); block offsets within a slot are immediates
+    uint32_t kx[2][D / 16], vx[2][D / 32];
   };
 
   __device__ static void setup(Lane &L, const FwdArgs &a, int tid, uint32_t smem_base) {
@@ -338,12 +341,28 @@ struct Bf16DirectPath {
       L.v_goff[i] = (int)(r * a.v_ss * 2) + 16 * L.v_chunk;
     }
     const int r = lane & 31, h = lane >> 5;
-    L.ka = smem_base + (uint32_t)(r * RB + 16 * (ksw(r) ^ h));
+    const uint32_t ka = smem_base + (uint32_t)(r * RB + 16 * (ksw(r) ^ h));
     const int g = lane >> 4, ap = lane & 15, z = ap >> 2;
     const int w = 2 * (g & 1) + ((ap & 3) >> 1);
     const int zz = D == 128 ? z : (z >> 1);
-    L.vb = smem_base + TILE_BYTES +
-           (uint32_t)((4 * h + z) * RB + 64 * zz + 16 * w + 8 * (ap & 1));
+    const uint32_t vb = smem_base + TILE_BYTES +
+                        (uint32_t)((4 * h + z) * RB + 64 * zz + 16 * w + 8 * (ap & 1));
+    // The slot-1 addresses pass through an empty asm so that the compiler keeps them in
+    // registers instead of re-deriving them as slot-0 address + 64 KiB (too large for
+    // the 16-bit immediate of an LDS read).
+#pragma unroll
+    for (int sl = 0; sl < 2; ++sl) {
+#pragma unroll
+      for (int ks = 0; ks < D / 16; ++ks) {
+        L.kx[sl][ks] = (ka ^ (uint32_t)(32 * ks)) + sl * BUF_BYTES;
+        if (sl) asm volatile("" : "+v"(L.kx[sl][ks]));
+      }
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt) {
+        L.vx[sl][dt] = (vb ^ (uint32_t)(64 * dt)) + sl * BUF_BYTES;
+        if (sl) asm volatile("" : "+v"(L.vx[sl][dt]));
+      }
+    }
   }
 
   __device__ static void load_q(QFrag &qf, const FwdArgs &a, const elem_t *qbase, int qrow, int h) {
@@ -382,18 +401,17 @@ struct Bf16DirectPath {
     }
   }
 
-  __device__ static u32x4 k_frag(uint32_t ka, int step) {
+  __device__ static u32x4 k_frag(const Lane &L, int sl, int step) {
     const int ks = step / NMT, mt = step % NMT;
-    const uint32_t addr = (ka ^ (uint32_t)(32 * ks)) + (uint32_t)(mt * 32 * RB);
-    return lds_read_b128(addr);
+    return lds_read_b128(L.kx[sl][ks] + (uint32_t)(mt * 32 * RB));
   }
 
-  // S^T[32 keys x 32 queries] for the two 32-key halves of the tile.
-  __device__ static void qk(f32x16 (&s)[NMT], const QFrag &qf, uint32_t ka) {
+  // S^T[32 keys x 32 queries] for the 32-key blocks of the tile in LDS slot sl.
+  __device__ static void qk(f32x16 (&s)[NMT], const QFrag &qf, const Lane &L, int sl) {
     constexpr int NSTEP = NMT * (D / 16);
     u32x4 kf[kDepth];
 #pragma unroll
-    for (int i = 0; i < kDepth; ++i) kf[i] = k_frag(ka, i);
+    for (int i = 0; i < kDepth; ++i) kf[i] = k_frag(L, sl, i);
 #pragma unroll
     for (int mt = 0; mt < NMT; ++mt) s[mt] = f32x16{};
     __builtin_amdgcn_sched_barrier(0);
@@ -401,7 +419,7 @@ struct Bf16DirectPath {
     for (int step = 0; step < NSTEP; ++step) {
       const int ks = step / NMT, mt = step % NMT;
       s[mt] = mfma_bf16(as_bf16x8(kf[step % kDepth]), qf.x[ks], s[mt]);
-      if (step + kDepth < NSTEP) kf[step % kDepth] = k_frag(ka, step + kDepth);
+      if (step + kDepth < NSTEP) kf[step % kDepth] = k_frag(L, sl, step + kDepth);
       __builtin_amdgcn_sched_barrier(0);
     }
   }
@@ -426,25 +444,25 @@ struct Bf16DirectPath {
 
   // V^T operand for PV step (kstep, dt): two transposing 8-byte reads (keys
   // 16*kstep + 4h + 0..3 and + 8), matching the k order of the P^T registers.
-  __device__ static u32x4 v_frag(uint32_t vb, int step) {
+  __device__ static u32x4 v_frag(const Lane &L, int sl, int step) {
     const int kstep = step / (D / 32), dt = step % (D / 32);
-    const uint32_t base = (vb ^ (uint32_t)(64 * dt)) + (uint32_t)(16 * kstep * RB);
+    const uint32_t base = L.vx[sl][dt] + (uint32_t)(16 * kstep * RB);
     const s16x4 lo = lds_read_tr16_b64(base);
     const s16x4 hi = lds_read_tr16_b64(base + 8 * RB);
     u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
     return u32x4{l2[0], l2[1], h2[0], h2[1]};
   }
 
-  __device__ static void pv(f32x16 (&o)[D / 32], const PFrag &pf, uint32_t vb) {
+  __device__ static void pv(f32x16 (&o)[D / 32], const PFrag &pf, const Lane &L, int sl) {
     constexpr int NSTEP = (KN / 16) * (D / 32);
     u32x4 vf[kVDepth];
 #pragma unroll
-    for (int i = 0; i < kVDepth; ++i) vf[i] = v_frag(vb, i);
+    for (int i = 0; i < kVDepth; ++i) vf[i] = v_frag(L, sl, i);
 #pragma unroll
     for (int step = 0; step < NSTEP; ++step) {
       const int kstep = step / (D / 32), dt = step % (D / 32);
       o[dt] = mfma_bf16(as_bf16x8(vf[step % kVDepth]), as_bf16x8(pf.x[kstep]), o[dt]);
-      if (step + kVDepth < NSTEP) vf[step % kVDepth] = v_frag(vb, step + kVDepth);
+      if (step + kVDepth < NSTEP) vf[step % kVDepth] = v_frag(L, sl, step + kVDepth);
     }
   }
 };
@@ -877,8 +895,11 @@ attn_fwd_direct_kernel(FwdArgs a) {
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): Q and the first tile have landed
   __syncthreads();
 
-  int cur = 0;
-  while (t < a.num_chunks) {
+  // One tile from LDS slot `cur` (the next tile's loads go to the other slot); the loop
+  // alternates the slots so that the operand addresses are per-slot registers with
+  // immediate block offsets.  Returns false when the walk is done.
+  auto tile = [&](auto cur_c) -> bool {
+    constexpr int cur = decltype(cur_c)::value;
     const int kb_cur = kb, cend_cur = cend;
     ring_next<KN>(a, CAUSAL, vis_lim, t, kb, kend, cend);
     const bool has_next = t < a.num_chunks;
@@ -891,9 +912,8 @@ attn_fwd_direct_kernel(FwdArgs a) {
     const bool doc_skip =
         VARLEN && (kb_cur + KN <= w_ds_first || (!CAUSAL && kb_cur >= w_de_last));
     if (wave_active && !(CAUSAL && kpos0 > wpos_last) && !doc_skip) {
-      const uint32_t slot = (uint32_t)(cur * Path::BUF_BYTES);
       f32x16 s[NMT];
-      Path::qk(s, qf, L.ka + slot);
+      Path::qk(s, qf, L, cur);
       const int kvalid = min(KN, cend_cur - kb_cur);
       const bool need_mask =
           (kvalid < KN) || (CAUSAL && kpos0 + kvalid - 1 > wpos_first) ||
@@ -939,7 +959,7 @@ attn_fwd_direct_kernel(FwdArgs a) {
       const float mneg = m_run == -INFINITY ? 0.f : -m_run;
       typename Path::PFrag pf;
       l_run += Path::exp_pack(s, c, mneg, pf);
-      Path::pv(o, pf, L.vb + slot);
+      Path::pv(o, pf, L, cur);
     }
 #if RA_FWD_DMA_LATE
     if (has_next)
@@ -947,7 +967,11 @@ attn_fwd_direct_kernel(FwdArgs a) {
 #endif
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the next tile's direct loads landed
     __syncthreads();
-    cur ^= 1;
+    return has_next;
+  };
+  if (t < a.num_chunks) {
+    while (tile(std::integral_constant<int, 0>{}) && tile(std::integral_constant<int, 1>{})) {
+    }
   }
 
   const float l_tot = halves_sum(l_run);
