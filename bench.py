@@ -109,6 +109,10 @@ def cpu_baseline(w, budget_s: float = 15.0):
     blk = 128
     starts = list(range(0, Sq, blk))
     rng.shuffle(starts)
+    if w.fp8:  # the context's codes are set up once, like the inputs, before timing
+        from oracle import fp8 as ofp8
+        kc, kdd = ofp8.quantize_heads(k64.astype(np.float32))
+        vc, vdd = ofp8.quantize_heads(v64.astype(np.float32))
     done_flops, rows, t0 = 0.0, 0, time.perf_counter()
     cu = si.draw_doc_offsets(w.seed, Sq) if w.packed_docs else None
     for a in starts:
@@ -127,6 +131,13 @@ def cpu_baseline(w, budget_s: float = 15.0):
             else:
                 oracle.full_attention(qb[:, :, :n], kk, vv, causal=w.causal, q_offset=a - lo)
                 done_flops += attn_flops(1, 1, n, hi - lo, D, 1, w.causal, a - lo, 0)
+        elif w.fp8:  # the fp8 oracle: quantize the block (per-head rule), then exact
+            # attention of the dequantized values over the context quantized up front
+            qc, qdd = ofp8.quantize_heads(qb.astype(np.float32))
+            ofp8.fp8_attention(qc, kc, vc, qdd, kdd, vdd, causal=w.causal,
+                               q_offset=w.q_offset + a, kv_offset=w.kv_offset)
+            done_flops += attn_flops(1, 1, blk, Skv, D, 1, w.causal, w.q_offset + a,
+                                     w.kv_offset)
         elif w.backward:  # all five products for the block's (query, key) pairs
             nk = min(Skv, w.q_offset + a + blk - w.kv_offset) if w.causal else Skv
             oracle.attention_bwd(qb, k64[:, :, :nk], v64[:, :, :nk], qb, causal=w.causal,
@@ -148,7 +159,9 @@ def cpu_baseline(w, budget_s: float = 15.0):
         "sample": f"{rows} query rows ({rows // blk} blocks of {blk}, random positions) of "
                   f"one head against its {'causal ' if w.causal else ''}"
                   f"{'own document' if cu is not None else str(Skv) + '-key context'}, "
-                  f"{'backward' if w.backward else 'forward'} oracle, fp64 NumPy, {dt:.1f} s",
+                  f"{'backward' if w.backward else ('fp8 forward' if w.fp8 else 'forward')} "
+                  f"oracle{' (context quantized before timing)' if w.fp8 else ''}, fp64 "
+                  f"NumPy, {dt:.1f} s",
     }
 
 
