@@ -12,10 +12,13 @@
 // contiguous), each with one fp32 descale per (batch, head): value = decode(code) *
 // descale.  The descales of q and k fold into the softmax scale, v's into the epilogue.
 //
-// Design (same skeleton as the bf16 direct kernel):
-//   * 8 waves x 32 query rows per workgroup; K and V^T tiles of KN keys go from global
-//     memory straight into LDS (global_load_lds_dwordx4), double-buffered, 16-byte
-//     chunks XOR-swizzled per row so every operand read is a conflict-free ds_read_b128;
+// Design (the bf16 direct kernel's skeleton, shaped for a softmax that now costs more
+// issue time than the MFMAs):
+//   * 4 waves x 32 query rows per workgroup, three workgroups per CU (3 waves per SIMD):
+//     their barriers are independent, so one workgroup's softmax runs under another's
+//     MFMAs; K and V^T tiles of KN keys go from global memory straight into LDS
+//     (global_load_lds_dwordx4), double-buffered, 16-byte chunks XOR-swizzled per row so
+//     every operand read is a conflict-free ds_read_b128;
 //   * S^T = K Q^T with 32x32x64 f8 MFMAs (Q in registers as the B operand): lane = one
 //     query row, 16 of each 32 keys -- row max in registers plus one v_permlane32_swap;
 //   * P' = 2^6 * exp2(c s - m) is rounded to e4m3 for O^T += V^T P'^T.  The 2^6 offset
@@ -51,8 +54,18 @@ __device__ __forceinline__ i32x8 cat8(const u32x4 &lo, const u32x4 &hi) {
 
 constexpr float kP8Shift = 6.f;     // P' = 2^6 P
 constexpr float kLazyFp8 = 2.f;     // running max lags the true one by < 2 (log2 units)
+// Launch shape (measured on the 32K GQA workload, same call): 4 waves x 64-key tiles
+// at 3 waves per SIMD (168 VGPRs, 32 KiB LDS, three workgroups per CU whose barriers are
+// independent) 1.087 ms; 8 waves x 128-key tiles at 2 per SIMD 1.178 ms; 4 x 64 at 2
+// per SIMD 1.155 ms.
 #ifndef RA_FP8_KN
-#define RA_FP8_KN 128               // keys per LDS tile
+#define RA_FP8_KN 64                // keys per LDS tile
+#endif
+#ifndef RA_FP8_NW
+#define RA_FP8_NW 4                 // waves (of 32 query rows) per workgroup
+#endif
+#ifndef RA_FP8_WPE
+#define RA_FP8_WPE 3                // waves per SIMD the register budget is sized for
 #endif
 
 // 16-byte chunk swizzle of a row of RB bytes: rows sharing a 256-byte bank window
@@ -62,9 +75,9 @@ __device__ __forceinline__ int swz(int r) {
   return (r / (256 / RB)) % (RB / 16);
 }
 
-template <int D, int KN>
+template <int D, int KN, int NW_>
 struct Fp8Tile {
-  static constexpr int NW = 8;
+  static constexpr int NW = NW_;
   static constexpr int K_BYTES = KN * D;        // K tile: KN rows of D bytes
   static constexpr int V_BYTES = D * KN;        // V^T tile: D rows of KN bytes
   static constexpr int BUF = K_BYTES + V_BYTES;
@@ -163,10 +176,10 @@ __device__ __forceinline__ void ring_next_fp8(const FwdArgs &a, bool causal, int
   }
 }
 
-template <int D, bool CAUSAL, int KN>
-__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+template <int D, bool CAUSAL, int KN, int NW, int WPE>
+__global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
 attn_fwd_fp8_kernel(Fp8Args a) {
-  using T = Fp8Tile<D, KN>;
+  using T = Fp8Tile<D, KN, NW>;
   constexpr int NMT = KN / 32;  // 32-key S^T blocks per tile
   constexpr int NG = KN / 64;   // 64-key PV groups per tile
   constexpr int BM = 32 * T::NW;
@@ -368,12 +381,12 @@ attn_fwd_fp8_kernel(Fp8Args a) {
 template <int D, bool CAUSAL>
 int launch_fp8(const Fp8Args &args, hipStream_t stream) {
   Fp8Args a = args;
-  constexpr int KN = RA_FP8_KN;
-  a.f.num_q_tiles = (a.f.Sq + 255) / 256;
+  constexpr int KN = RA_FP8_KN, NW = RA_FP8_NW;
+  a.f.num_q_tiles = (a.f.Sq + 32 * NW - 1) / (32 * NW);
   const int64_t blocks = (int64_t)a.f.num_q_tiles * a.f.Hq * a.f.B;
   if (blocks <= 0) return RA_OK;
-  hipLaunchKernelGGL((attn_fwd_fp8_kernel<D, CAUSAL, KN>), dim3((unsigned)blocks), dim3(512), 0,
-                     stream, a);
+  hipLaunchKernelGGL((attn_fwd_fp8_kernel<D, CAUSAL, KN, NW, RA_FP8_WPE>), dim3((unsigned)blocks),
+                     dim3(64 * NW), 0, stream, a);
   return hipGetLastError() == hipSuccess ? RA_OK : RA_ERR_HIP;
 }
 
