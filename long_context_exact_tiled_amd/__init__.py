@@ -29,6 +29,7 @@ __all__ = [
     "attn_fwd_varlen", "attn_fwd_varlen_validate", "attn_bwd_varlen", "attn_bwd_varlen_validate",
     "attn_bwd_accum", "attn_bwd_accum_validate", "ring_attn_bwd_chunked",
     "fp8_quantize", "fp8_quantize_validate", "attn_fwd_fp8", "attn_fwd_fp8_validate",
+    "ring_attn_fp8_chunked",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libra.so")
@@ -444,6 +445,31 @@ def ring_attn_chunked(q, k, v, *, num_chunks: int, start_chunk: int = 0, causal:
         o_parts.append(o_c)
         lse_parts.append(l_c)
     return lse_merge(o_parts, lse_parts, out_dtype=out_dtype or q.dtype)
+
+
+def ring_attn_fp8_chunked(q, k, vt, q_descale, k_descale, v_descale, *, num_chunks: int,
+                          start_chunk: int = 0, causal: bool = False, q_offset: int = 0,
+                          kv_offset: int = 0, scale: Optional[float] = None,
+                          out_dtype: torch.dtype = torch.bfloat16):
+    """ring_attn_chunked over e4m3 codes: one attn_fwd_fp8 per visible chunk into fp32
+    partials, then one lse_merge.  Chunks of vt [B,Hkv,D,S_pad] are column slices, so
+    Skv / num_chunks must be a multiple of 16."""
+    Skv = k.shape[2]
+    L = Skv // num_chunks
+    chunks = ring_visible_chunks(q.shape[2], Skv, num_chunks=num_chunks,
+                                 start_chunk=start_chunk, causal=causal, q_offset=q_offset,
+                                 kv_offset=kv_offset)
+    if not chunks:
+        chunks = [start_chunk]  # every row empty: one call yields o = 0, lse = -inf
+    o_parts, lse_parts = [], []
+    for c in chunks:
+        sl = slice(c * L, (c + 1) * L)
+        o_c, l_c = attn_fwd_fp8(q, k[:, :, sl], vt[:, :, :, sl], q_descale, k_descale, v_descale,
+                                causal=causal, q_offset=q_offset, kv_offset=kv_offset + c * L,
+                                scale=scale, out_dtype=torch.float32)
+        o_parts.append(o_c)
+        lse_parts.append(l_c)
+    return lse_merge(o_parts, lse_parts, out_dtype=out_dtype)
 
 
 def ring_attn_bwd_chunked(q, k, v, o, dout, lse, *, num_chunks: int, start_chunk: int = 0,

@@ -205,3 +205,24 @@ def test_qwen7b_gqa_32k_fp8_workload_sampled_rows():
     got_o = np.stack([o_n[b, h, i] for (b, h, i) in idx])
     got_l = np.array([l_n[b, h, i] for (b, h, i) in idx])
     _check(got_o, got_l, o_ref, l_ref, bound, "o sampled")
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_fp8_ring_chunked_and_fused(causal):
+    """One device's ring share in fp8, chunk by chunk (fp32 partials + lse_merge) and
+    fused: both within the derived bound of the exact result.  Merging weighs each
+    chunk's error by the chunk's share of the row, so the bound carries over."""
+    B, Hq, Hkv, Sq, P, L, start, q_off = 1, 4, 2, 256, 4, 208, 1, 500
+    say(f"fp8 ring causal={causal}")
+    (qc, kc, vtc, qd, kd, vd), (q, k, v) = _fp8_inputs(B, Hq, Hkv, Sq, P * L, 128,
+                                                        77 + int(causal))
+    kw = dict(causal=causal, num_chunks=P, start_chunk=start, q_offset=q_off)
+    o_c, l_c = ra.ring_attn_fp8_chunked(qc, kc, vtc, qd, kd, vd, **kw)
+    o_f, l_f = ra.attn_fwd_fp8(qc, kc, vtc, qd, kd, vd, **kw)
+    torch.cuda.synchronize()
+    o_ref, l_ref = oracle.full_attention(q, k, v, causal=causal, q_offset=q_off)
+    rows = [(0, h, i) for h in range(Hq) for i in range(Sq)]
+    bound = ofp8.p_rounding_bound(q, k, v, rows, causal=causal,
+                                  q_offset=q_off).reshape(o_ref.shape)
+    for o, l, what in ((o_c, l_c, "chunked"), (o_f, l_f, "fused")):
+        _check(to_np64(o), l.cpu().numpy().astype(np.float64), o_ref, l_ref, bound, what)
