@@ -45,6 +45,46 @@ constexpr int TN = 64;  // rows per LDS tile of queries in bwd_dkdv
 #ifndef RA_BWD_DKDV_PIPE
 #define RA_BWD_DKDV_PIPE 1  // software-pipelined dK/dV tile
 #endif
+#ifndef RA_BWD_SCORE_ASM
+#define RA_BWD_SCORE_ASM 1  // dK/dV kernel: register placement by inline-asm MFMAs
+#endif
+
+// Register placement in the dK/dV kernel (one wave per SIMD, ~370 live registers).  The
+// compiler's choice -- every MFMA accumulator in VGPRs, other values spilled to AGPRs --
+// cost ≈220 AGPR->VGPR copies per 64 MFMAs.  Here the MFMAs are written out so that
+// the dK, dV accumulators and the resident K^T, V^T operands live in AGPRs (MFMAs read
+// and write them there; no VALU touches them inside the loop) and the score products
+// S, dP (read by the softmax VALU work) in VGPRs: no copies at all.  The compiler does
+// not see these MFMAs, so every consumer is placed where no wait states are needed: a
+// score chain's results are first read two MFMAs (≥64 clk) after its last step, the
+// P/dS operands are written at least eight MFMAs before their use, chained
+// accumulators overlap exactly, and the epilogue waits explicitly.
+// dK or dV += A B (accumulator in AGPRs, A and B in VGPRs)
+__device__ __forceinline__ void mfma_grad(f32x16 &acc, const bf16x8 &a, const bf16x8 &b) {
+#if RA_BWD_SCORE_ASM
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+#else
+  acc = mfma_bf16(a, b, acc);
+#endif
+}
+// S or dP: first step of a chain (C = 0) and further steps; the B operand (the key/value
+// rows kept for the whole workgroup) is read straight from AGPRs, the result is a VGPR.
+__device__ __forceinline__ f32x16 mfma_score0_ab(const bf16x8 &a, const bf16x8 &b) {
+#if RA_BWD_SCORE_ASM
+  f32x16 d;
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "a"(b));
+  return d;
+#else
+  return mfma_bf16(a, b, f32x16{});
+#endif
+}
+__device__ __forceinline__ void mfma_score_ab(f32x16 &acc, const bf16x8 &a, const bf16x8 &b) {
+#if RA_BWD_SCORE_ASM
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "a"(b));
+#else
+  acc = mfma_bf16(a, b, acc);
+#endif
+}
 
 // 16-byte-chunk swizzle of a tile row: for 16 consecutive rows at one chunk the physical
 // chunks differ (row-wise reads), and for 4 consecutive rows at 4 consecutive chunks
@@ -386,12 +426,24 @@ bwd_dkdv_kernel(BwdArgs a, int num_kv_tiles) {
     kf[ks] = as_bf16x8(*(const u32x4 *)(kb_ + (int64_t)kr * a.k_ss + 16 * ks + 8 * h));
     vf[ks] = as_bf16x8(*(const u32x4 *)(vb_ + (int64_t)kr * a.v_ss + 16 * ks + 8 * h));
   }
+#if RA_BWD_SCORE_ASM
+  // K^T and V^T are only ever MFMA B operands from here on: keep them in AGPRs
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) {
+    asm volatile("" : "+a"(kf[ks]));
+    asm volatile("" : "+a"(vf[ks]));
+  }
+#endif
 
   f32x16 dk[D / 32], dv[D / 32];
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt) {
     dk[dt] = f32x16{};
     dv[dt] = f32x16{};
+#if RA_BWD_SCORE_ASM
+    asm volatile("" : "+a"(dk[dt]));  // the accumulators live in AGPRs from the start
+    asm volatile("" : "+a"(dv[dt]));
+#endif
   }
 
   typename Tile::Lane TL;
@@ -495,9 +547,8 @@ bwd_dkdv_kernel(BwdArgs a, int num_kv_tiles) {
       };
       const bool nm0 = qv0 < 32 || (CAUSAL && wk_last > qpos0) || doc_cross(q0);
       const bool nm1 = qv1 < 32 || (CAUSAL && wk_last > qpos0 + 32) || doc_cross(q0 + 32);
-      f32x16 s0 = f32x16{}, dp0 = f32x16{}, s1 = f32x16{}, dp1 = f32x16{};
+      f32x16 s0, dp0, s1, dp1;
       u32x4 pf0[2], dsf0[2], pf1[2], dsf1[2];
-      f32x4 l4[4], d4[4];
       auto operand = [&](int i) -> u32x4 {
         const int stage = i / NST, j = i % NST;
         const int qs = stage & 1;
@@ -506,32 +557,28 @@ bwd_dkdv_kernel(BwdArgs a, int num_kv_tiles) {
         const int pj = j >> 1, s2 = pj / (D / 32), dt = pj % (D / 32);
         return Tile::tr_read((j & 1) ? qo : qo + Tile::BYTES, tp0, tp1, 16 * s2, dt);
       };
-      auto stats_read = [&](int qs) {
-        const uint32_t st = slot + 2 * Tile::BYTES + (uint32_t)(4 * 32 * qs);
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          l4[g] = *(const __attribute__((address_space(3))) f32x4 *)(size_t)(
-              st + (uint32_t)(4 * (8 * g + 4 * h)));
-          d4[g] = *(const __attribute__((address_space(3))) f32x4 *)(size_t)(
-              st + (uint32_t)(4 * TN + 4 * (8 * g + 4 * h)));
-        }
-      };
-      // P and dS of 4 elements (element group g) of one step
+      // P and dS of 4 elements (element group g) of step qs; the group's lse and delta
+      // (4 rows each) are read from LDS here, so only 8 of them are live at a time
       auto pds = [&](const f32x16 &sv_, const f32x16 &dpv, bool nm, int qv, int64_t sfirst,
-                     int g, u32x4 (&pf)[2], u32x4 (&dsf)[2]) {
+                     int qs, int g, u32x4 (&pf)[2], u32x4 (&dsf)[2]) {
+        const uint32_t st = slot + 2 * Tile::BYTES + (uint32_t)(4 * 32 * qs);
+        const f32x4 lg = *(const __attribute__((address_space(3))) f32x4 *)(size_t)(
+            st + (uint32_t)(4 * (8 * g + 4 * h)));
+        const f32x4 dg = *(const __attribute__((address_space(3))) f32x4 *)(size_t)(
+            st + (uint32_t)(4 * TN + 4 * (8 * g + 4 * h)));
         float pv[4], dv4[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int i = 4 * g + e;
           const int qi = (i >> 2) * 8 + 4 * h + (i & 3);
-          float p = fast_exp2(fmaf(sv_[i], c, -l4[g][e]));
+          float p = fast_exp2(fmaf(sv_[i], c, -lg[e]));
           if (nm && (qi >= qv || (CAUSAL && kpos > sfirst + qi))) p = 0.f;
           if (VARLEN && nm) {  // packed documents (offsets are 0): the key's document only
             const int64_t qabs = sfirst + qi;
             if (qabs >= de || (!CAUSAL && qabs < ds)) p = 0.f;
           }
           pv[e] = p;
-          dv4[e] = p * (dpv[i] - d4[g][e]);
+          dv4[e] = p * (dpv[i] - dg[e]);
         }
         const int s2 = g >> 1;
         const bf16x2 p01 = __builtin_convertvector((f32x2){pv[0], pv[1]}, bf16x2);
@@ -551,32 +598,38 @@ bwd_dkdv_kernel(BwdArgs a, int num_kv_tiles) {
 #pragma unroll
       for (int i = 0; i < NST; ++i) {
         const bf16x8 A = as_bf16x8(op[i % kDep]);
-        if (i & 1) dp0 = mfma_bf16(A, vf[i >> 1], dp0); else s0 = mfma_bf16(A, kf[i >> 1], s0);
+        if (i < 2) {
+          if (i & 1) dp0 = mfma_score0_ab(A, vf[0]); else s0 = mfma_score0_ab(A, kf[0]);
+        } else {
+          if (i & 1) mfma_score_ab(dp0, A, vf[i >> 1]); else mfma_score_ab(s0, A, kf[i >> 1]);
+        }
         op[i % kDep] = operand(i + kDep);
         __builtin_amdgcn_sched_barrier(0);
       }
-      stats_read(0);
       // stage 1: S, dP of step 1 | P, dS of step 0
 #pragma unroll
       for (int j = 0; j < NST; ++j) {
         const int i = NST + j;
         const bf16x8 A = as_bf16x8(op[i % kDep]);
-        if (j & 1) dp1 = mfma_bf16(A, vf[j >> 1], dp1); else s1 = mfma_bf16(A, kf[j >> 1], s1);
+        if (j < 2) {
+          if (j & 1) dp1 = mfma_score0_ab(A, vf[0]); else s1 = mfma_score0_ab(A, kf[0]);
+        } else {
+          if (j & 1) mfma_score_ab(dp1, A, vf[j >> 1]); else mfma_score_ab(s1, A, kf[j >> 1]);
+        }
         op[i % kDep] = operand(i + kDep);
-        if (j % (NST / 4) == 1) pds(s0, dp0, nm0, qv0, qpos0, j / (NST / 4), pf0, dsf0);
+        if (j % (NST / 4) == 1) pds(s0, dp0, nm0, qv0, qpos0, 0, j / (NST / 4), pf0, dsf0);
         __builtin_amdgcn_sched_barrier(0);
       }
-      stats_read(1);
       // stage 2: dV, dK of step 0 | P, dS of step 1
 #pragma unroll
       for (int j = 0; j < NST; ++j) {
         const int i = 2 * NST + j;
         const bf16x8 A = as_bf16x8(op[i % kDep]);
         const int pj = j >> 1, s2 = pj / (D / 32), dt = pj % (D / 32);
-        if (j & 1) dk[dt] = mfma_bf16(A, as_bf16x8(dsf0[s2]), dk[dt]);
-        else dv[dt] = mfma_bf16(A, as_bf16x8(pf0[s2]), dv[dt]);
+        if (j & 1) mfma_grad(dk[dt], A, as_bf16x8(dsf0[s2]));
+        else mfma_grad(dv[dt], A, as_bf16x8(pf0[s2]));
         op[i % kDep] = operand(i + kDep);
-        if (j % (NST / 4) == 1) pds(s1, dp1, nm1, qv1, qpos0 + 32, j / (NST / 4), pf1, dsf1);
+        if (j % (NST / 4) == 1) pds(s1, dp1, nm1, qv1, qpos0 + 32, 1, j / (NST / 4), pf1, dsf1);
         __builtin_amdgcn_sched_barrier(0);
       }
       // stage 3: dV, dK of step 1
@@ -585,8 +638,8 @@ bwd_dkdv_kernel(BwdArgs a, int num_kv_tiles) {
         const int i = 3 * NST + j;
         const bf16x8 A = as_bf16x8(op[i % kDep]);
         const int pj = j >> 1, s2 = pj / (D / 32), dt = pj % (D / 32);
-        if (j & 1) dk[dt] = mfma_bf16(A, as_bf16x8(dsf1[s2]), dk[dt]);
-        else dv[dt] = mfma_bf16(A, as_bf16x8(pf1[s2]), dv[dt]);
+        if (j & 1) mfma_grad(dk[dt], A, as_bf16x8(dsf1[s2]));
+        else mfma_grad(dv[dt], A, as_bf16x8(pf1[s2]));
         if (i + kDep < 4 * NST) op[i % kDep] = operand(i + kDep);
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -654,6 +707,11 @@ bwd_dkdv_kernel(BwdArgs a, int num_kv_tiles) {
     cur ^= 1;
   }
 
+#if RA_BWD_SCORE_ASM
+  // the compiler does not see the asm MFMAs: give their results time to land before
+  // the epilogue reads the accumulators
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+#endif
   if (krow < a.Skv) {
     const int64_t krow_dk = b * a.dk_sb + hk * a.dk_sh + (int64_t)krow * a.dk_ss;
     const int64_t krow_dv = b * a.dv_sb + hk * a.dv_sh + (int64_t)krow * a.dv_ss;
