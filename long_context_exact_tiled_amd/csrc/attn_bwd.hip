@@ -568,18 +568,22 @@ bwd_dkdv_kernel(BwdArgs a, int num_kv_tiles) {
             st + (uint32_t)(4 * TN + 4 * (8 * g + 4 * h)));
         float pv[4], dv4[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int i = 4 * g + e;
-          const int qi = (i >> 2) * 8 + 4 * h + (i & 3);
-          float p = fast_exp2(fmaf(sv_[i], c, -lg[e]));
-          if (nm && (qi >= qv || (CAUSAL && kpos > sfirst + qi))) p = 0.f;
-          if (VARLEN && nm) {  // packed documents (offsets are 0): the key's document only
-            const int64_t qabs = sfirst + qi;
-            if (qabs >= de || (!CAUSAL && qabs < ds)) p = 0.f;
+        for (int e = 0; e < 4; ++e) pv[e] = fast_exp2(fmaf(sv_[4 * g + e], c, -lg[e]));
+        // the element mask only in steps that need it (a wave-uniform branch)
+        if (__builtin_amdgcn_readfirstlane((int)nm)) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int i = 4 * g + e;
+            const int qi = (i >> 2) * 8 + 4 * h + (i & 3);
+            if (qi >= qv || (CAUSAL && kpos > sfirst + qi)) pv[e] = 0.f;
+            if (VARLEN) {  // packed documents (offsets are 0): the key's document only
+              const int64_t qabs = sfirst + qi;
+              if (qabs >= de || (!CAUSAL && qabs < ds)) pv[e] = 0.f;
+            }
           }
-          pv[e] = p;
-          dv4[e] = p * (dpv[i] - dg[e]);
         }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dv4[e] = pv[e] * (dpv[4 * g + e] - dg[e]);
         const int s2 = g >> 1;
         const bf16x2 p01 = __builtin_convertvector((f32x2){pv[0], pv[1]}, bf16x2);
         const bf16x2 p23 = __builtin_convertvector((f32x2){pv[2], pv[3]}, bf16x2);
