@@ -450,6 +450,17 @@ bwd_dkdv_kernel(BwdArgs a, int num_kv_tiles) {
   Tile::setup(TL, lane, wave);
   const uint32_t qpart = Tile::row_part(r32, h);
   const uint32_t tp0 = Tile::tr_part(lane, 0), tp1 = Tile::tr_part(lane, 1);
+  // swizzled operand offsets of this lane within a tile: row reads per head-dim step ks,
+  // transposed reads per sub-read s and head-dim block dt (a slot base is added once per
+  // tile, the block offsets are immediates)
+  uint32_t rx[D / 16], tx[2][D / 32];
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) rx[ks] = qpart ^ (uint32_t)(32 * ks);
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt) {
+    tx[0][dt] = tp0 ^ (uint32_t)(64 * dt);
+    tx[1][dt] = tp1 ^ (uint32_t)(64 * dt);
+  }
 
   // First query row that can see this workgroup's first key (causal), as a tile start.
   int qstart = 0;
@@ -549,13 +560,25 @@ bwd_dkdv_kernel(BwdArgs a, int num_kv_tiles) {
       const bool nm1 = qv1 < 32 || (CAUSAL && wk_last > qpos0 + 32) || doc_cross(q0 + 32);
       f32x16 s0, dp0, s1, dp1;
       u32x4 pf0[2], dsf0[2], pf1[2], dsf1[2];
+      uint32_t rb[D / 16], tb[2][D / 32];  // this tile's operand addresses
+#pragma unroll
+      for (int ks = 0; ks < D / 16; ++ks) rb[ks] = slot + rx[ks];
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt) {
+        tb[0][dt] = slot + tx[0][dt];
+        tb[1][dt] = slot + tx[1][dt];
+      }
       auto operand = [&](int i) -> u32x4 {
         const int stage = i / NST, j = i % NST;
         const int qs = stage & 1;
-        const uint32_t qo = slot + (uint32_t)(32 * qs * Tile::RB);
-        if (stage < 2) return Tile::row_read((j & 1) ? qo + Tile::BYTES : qo, qpart, j >> 1);
+        const uint32_t qo = (uint32_t)(32 * qs * Tile::RB);
+        if (stage < 2) return lds_read_b128(rb[j >> 1] + qo + ((j & 1) ? Tile::BYTES : 0u));
         const int pj = j >> 1, s2 = pj / (D / 32), dt = pj % (D / 32);
-        return Tile::tr_read((j & 1) ? qo : qo + Tile::BYTES, tp0, tp1, 16 * s2, dt);
+        const uint32_t off = qo + ((j & 1) ? 0u : (uint32_t)Tile::BYTES) +
+                             (uint32_t)(16 * s2 * Tile::RB);
+        const u32x2 l2 = __builtin_bit_cast(u32x2, lds_read_tr16_b64(tb[0][dt] + off));
+        const u32x2 h2 = __builtin_bit_cast(u32x2, lds_read_tr16_b64(tb[1][dt] + off));
+        return u32x4{l2[0], l2[1], h2[0], h2[1]};
       };
       // P and dS of 4 elements (element group g) of step qs; the group's lse and delta
       // (4 rows each) are read from LDS here, so only 8 of them are live at a time
