@@ -580,15 +580,20 @@ bwd_dkdv_kernel(BwdArgs a, int num_kv_tiles) {
         const u32x2 h2 = __builtin_bit_cast(u32x2, lds_read_tr16_b64(tb[1][dt] + off));
         return u32x4{l2[0], l2[1], h2[0], h2[1]};
       };
-      // P and dS of 4 elements (element group g) of step qs; the group's lse and delta
-      // (4 rows each) are read from LDS here, so only 8 of them are live at a time
+      // lse and delta of the 4 rows of element group g of step qs, read one group ahead
+      // of their use (only 16 of them are live at a time)
+      const uint32_t sbase = slot + 2 * Tile::BYTES + (uint32_t)(16 * h);
+      auto stats_rd = [&](int qs, int g, f32x4 &lg, f32x4 &dg) {
+        const uint32_t at = sbase + (uint32_t)(4 * 32 * qs + 32 * g);
+        lg = *(const __attribute__((address_space(3))) f32x4 *)(size_t)at;
+        dg = *(const __attribute__((address_space(3))) f32x4 *)(size_t)(at + 4 * TN);
+      };
+      f32x4 lgn, dgn;  // the next group's
+      // P and dS of 4 elements (element group g) of step qs
       auto pds = [&](const f32x16 &sv_, const f32x16 &dpv, bool nm, int qv, int64_t sfirst,
                      int qs, int g, u32x4 (&pf)[2], u32x4 (&dsf)[2]) {
-        const uint32_t st = slot + 2 * Tile::BYTES + (uint32_t)(4 * 32 * qs);
-        const f32x4 lg = *(const __attribute__((address_space(3))) f32x4 *)(size_t)(
-            st + (uint32_t)(4 * (8 * g + 4 * h)));
-        const f32x4 dg = *(const __attribute__((address_space(3))) f32x4 *)(size_t)(
-            st + (uint32_t)(4 * TN + 4 * (8 * g + 4 * h)));
+        const f32x4 lg = lgn, dg = dgn;
+        if (qs == 0 || g < 3) stats_rd(qs + (g == 3), (g + 1) & 3, lgn, dgn);
         float pv[4], dv4[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) pv[e] = fast_exp2(fmaf(sv_[4 * g + e], c, -lg[e]));
@@ -631,6 +636,7 @@ bwd_dkdv_kernel(BwdArgs a, int num_kv_tiles) {
           if (i & 1) mfma_score_ab(dp0, A, vf[i >> 1]); else mfma_score_ab(s0, A, kf[i >> 1]);
         }
         op[i % kDep] = operand(i + kDep);
+        if (i == NST - 4) stats_rd(0, 0, lgn, dgn);
         __builtin_amdgcn_sched_barrier(0);
       }
       // stage 1: S, dP of step 1 | P, dS of step 0
