@@ -326,22 +326,29 @@ bwd_dq_kernel(BwdArgs a, int num_q_tiles) {
           s = mfma_bf16(as_bf16x8(Tile::row_read(ko, kpart, ks)), qf[ks], s);
           dp = mfma_bf16(as_bf16x8(Tile::row_read(vo, kpart, ks)), df[ks], dp);
         }
-        // P^T and dS^T (lane: one query row, 16 of the 32 keys of this half)
+        // P^T and dS^T (lane: one query row, 16 of the 32 keys of this half); the element
+        // mask only where this 32-key half needs it (a wave-uniform branch)
+        float pv[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) pv[i] = fast_exp2(fmaf(s[i], c, -lse2));
+        const bool nm = (kvalid < 32 * (mt + 1)) ||
+                        (CAUSAL && kpos0 + 32 * mt + 31 > wpos_first) ||
+                        (VARLEN && need_mask);
+        if (__builtin_amdgcn_readfirstlane((int)nm)) {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int kk = 32 * mt + (i >> 2) * 8 + 4 * h + (i & 3);
+            if (kk >= lim || (VARLEN && kk < lo)) pv[i] = 0.f;
+          }
+        }
         u32x4 dsf[2];
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
           for (int w = 0; w < 4; ++w) {
-            float d2[2];
-#pragma unroll
-            for (int e = 0; e < 2; ++e) {
-              const int i = 8 * s2 + 2 * w + e;
-              const int kk = 32 * mt + (i >> 2) * 8 + 4 * h + (i & 3);
-              float p = fast_exp2(fmaf(s[i], c, -lse2));
-              if (need_mask && (kk >= lim || (VARLEN && kk < lo))) p = 0.f;
-              d2[e] = p * (dp[i] - dlt);
-            }
-            const bf16x2 pk = __builtin_convertvector((f32x2){d2[0], d2[1]}, bf16x2);
+            const int i = 8 * s2 + 2 * w;
+            const bf16x2 pk = __builtin_convertvector(
+                (f32x2){pv[i] * (dp[i] - dlt), pv[i + 1] * (dp[i + 1] - dlt)}, bf16x2);
             dsf[s2][w] = __builtin_bit_cast(uint32_t, pk);
           }
         // dQ^T[D x 32 q] += K^T[D x 32 keys] dS^T[32 keys x 32 q]
