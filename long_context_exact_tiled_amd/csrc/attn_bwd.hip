@@ -78,6 +78,16 @@ __device__ __forceinline__ f32x16 mfma_score0_ab(const bf16x8 &a, const bf16x8 &
   return mfma_bf16(a, b, f32x16{});
 #endif
 }
+__device__ __forceinline__ f32x16 mfma_score_c_ab(const bf16x8 &a, const bf16x8 &b,
+                                                   const f32x16 &c) {
+#if RA_BWD_SCORE_ASM
+  f32x16 d;
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %3" : "=&v"(d) : "v"(a), "a"(b), "v"(c));
+  return d;
+#else
+  return mfma_bf16(a, b, c);
+#endif
+}
 __device__ __forceinline__ void mfma_score_ab(f32x16 &acc, const bf16x8 &a, const bf16x8 &b) {
 #if RA_BWD_SCORE_ASM
   asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "a"(b));
@@ -498,25 +508,27 @@ bwd_dkdv_kernel(BwdArgs a, int num_kv_tiles) {
   const int nqt = qstart >= qend ? 0 : (qend - qstart + TN - 1) / TN;
   const int total = nqt * a.group;  // (query head, query tile) pairs
 
-  auto issue = [&](int it, uint32_t slot) {
-    const int hq = hk * a.group + it / nqt;
-    const int q0 = qstart + (it % nqt) * TN;
+  // tile `it` is query tile qt of query head hk * group + hg (qt fastest); the pair is
+  // advanced by one per tile instead of divided out of it
+  auto issue = [&](int hg, int qt, uint32_t slot) {
+    const int hq = hk * a.group + hg;
+    const int q0 = qstart + qt * TN;
     const uint16_t *qb = (const uint16_t *)a.q + b * a.q_sb + hq * a.q_sh;
     const uint16_t *dob = (const uint16_t *)a.dout + b * a.do_sb + hq * a.do_sh;
     Tile::load(TL, qb, a.q_ss, q0, a.Sq, slot, wave);
     Tile::load(TL, dob, a.do_ss, q0, a.Sq, slot + Tile::BYTES, wave);
   };
-  // lse (as exp2 offsets) and delta of the tile's 64 rows: 32 threads of wave 0
-  auto stats = [&](int it, float &val) {
-    const int hq = hk * a.group + it / nqt;
-    const int q0 = qstart + (it % nqt) * TN;
+  // lse (as exp2 offsets) and -delta of the tile's 64 rows: threads 0-127
+  auto stats = [&](int hg, int qt, float &val) {
+    const int hq = hk * a.group + hg;
+    const int q0 = qstart + qt * TN;
     const int i = tid & 63;
     const int q = min(q0 + i, a.Sq - 1);
     if (tid < 64) {
       const float l = a.lse[b * a.l_sb + hq * a.l_sh + q];
       val = l == -INFINITY ? INFINITY : l * kLog2e;
     } else if (tid < 128) {
-      val = a.delta[((int64_t)b * a.Hq + hq) * a.Sq + q];
+      val = -a.delta[((int64_t)b * a.Hq + hq) * a.Sq + q];  // stored negated
     }
   };
   auto stats_store = [&](float val, uint32_t slot) {
@@ -528,22 +540,30 @@ bwd_dkdv_kernel(BwdArgs a, int num_kv_tiles) {
 
   float sv = 0.f;
   if (total > 0) {
-    issue(0, smem0);
-    stats(0, sv);
+    issue(0, 0, smem0);
+    stats(0, 0, sv);
     stats_store(sv, smem0);
   }
   __builtin_amdgcn_s_waitcnt(0x0F70);
   __syncthreads();
 
   int cur = 0;
+  int qt_c = 0, hg_c = 0;  // this tile's query tile and head within the group
   for (int it = 0; it < total; ++it) {
     const uint32_t slot = smem0 + cur * SLOT;
     const bool has_next = it + 1 < total;
-    if (has_next) {
-      issue(it + 1, smem0 + (cur ^ 1) * SLOT);
-      stats(it + 1, sv);
+    int qt_n = qt_c + 1, hg_n = hg_c;
+    if (qt_n == nqt) {
+      qt_n = 0;
+      ++hg_n;
     }
-    const int q0 = qstart + (it % nqt) * TN;
+    if (has_next) {
+      issue(hg_n, qt_n, smem0 + (cur ^ 1) * SLOT);
+      stats(hg_n, qt_n, sv);
+    }
+    const int q0 = qstart + qt_c * TN;
+    qt_c = qt_n;
+    hg_c = hg_n;
     const int64_t qpos0 = a.q_offset + q0;
 #if RA_BWD_DKDV_PIPE
     // The two 32-query steps of the tile as one stream of 4*NST MFMAs, operands read
@@ -587,20 +607,31 @@ bwd_dkdv_kernel(BwdArgs a, int num_kv_tiles) {
         const u32x2 h2 = __builtin_bit_cast(u32x2, lds_read_tr16_b64(tb[1][dt] + off));
         return u32x4{l2[0], l2[1], h2[0], h2[1]};
       };
-      // lse and delta of the 4 rows of element group g of step qs, read one group ahead
-      // of their use (only 16 of them are live at a time)
+      // lse of the 4 rows of element group g of step qs, read one group ahead of its use
       const uint32_t sbase = slot + 2 * Tile::BYTES + (uint32_t)(16 * h);
-      auto stats_rd = [&](int qs, int g, f32x4 &lg, f32x4 &dg) {
-        const uint32_t at = sbase + (uint32_t)(4 * 32 * qs + 32 * g);
-        lg = *(const __attribute__((address_space(3))) f32x4 *)(size_t)at;
-        dg = *(const __attribute__((address_space(3))) f32x4 *)(size_t)(at + 4 * TN);
+      auto stats_rd = [&](int qs, int g, f32x4 &lg) {
+        lg = *(const __attribute__((address_space(3))) f32x4 *)(size_t)(
+            sbase + (uint32_t)(4 * 32 * qs + 32 * g));
       };
-      f32x4 lgn, dgn;  // the next group's
+      // -D of the 16 rows of this lane's elements in step qs: the initial accumulator of
+      // the step's dP chain, so that dP - D comes out of the MFMAs
+      auto negd_rd = [&](int qs) -> f32x16 {
+        f32x16 r;
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const f32x4 v4 = *(const __attribute__((address_space(3))) f32x4 *)(size_t)(
+              sbase + (uint32_t)(4 * TN + 4 * 32 * qs + 32 * g));
+#pragma unroll
+          for (int e = 0; e < 4; ++e) r[4 * g + e] = v4[e];
+        }
+        return r;
+      };
+      f32x4 lgn;  // the next group's
       // P and dS of 4 elements (element group g) of step qs
       auto pds = [&](const f32x16 &sv_, const f32x16 &dpv, bool nm, int qv, int64_t sfirst,
                      int qs, int g, u32x4 (&pf)[2], u32x4 (&dsf)[2]) {
-        const f32x4 lg = lgn, dg = dgn;
-        if (qs == 0 || g < 3) stats_rd(qs + (g == 3), (g + 1) & 3, lgn, dgn);
+        const f32x4 lg = lgn;
+        if (qs == 0 || g < 3) stats_rd(qs + (g == 3), (g + 1) & 3, lgn);
         float pv[4], dv4[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) pv[e] = fast_exp2(fmaf(sv_[4 * g + e], c, -lg[e]));
@@ -618,7 +649,7 @@ bwd_dkdv_kernel(BwdArgs a, int num_kv_tiles) {
           }
         }
 #pragma unroll
-        for (int e = 0; e < 4; ++e) dv4[e] = pv[e] * (dpv[4 * g + e] - dg[e]);
+        for (int e = 0; e < 4; ++e) dv4[e] = pv[e] * dpv[4 * g + e];  // dpv holds dP - D
         const int s2 = g >> 1;
         const bf16x2 p01 = __builtin_convertvector((f32x2){pv[0], pv[1]}, bf16x2);
         const bf16x2 p23 = __builtin_convertvector((f32x2){pv[2], pv[3]}, bf16x2);
@@ -629,6 +660,9 @@ bwd_dkdv_kernel(BwdArgs a, int num_kv_tiles) {
         dsf[s2][2 * (g & 1)] = __builtin_bit_cast(uint32_t, d01);
         dsf[s2][2 * (g & 1) + 1] = __builtin_bit_cast(uint32_t, d23);
       };
+      // step 0's -D read first: it lands before the first operand the MFMAs wait for
+      const f32x16 nd0 = negd_rd(0);
+      f32x16 nd1;
       u32x4 op[kDep];
 #pragma unroll
       for (int i = 0; i < kDep; ++i) op[i] = operand(i);
@@ -638,12 +672,16 @@ bwd_dkdv_kernel(BwdArgs a, int num_kv_tiles) {
       for (int i = 0; i < NST; ++i) {
         const bf16x8 A = as_bf16x8(op[i % kDep]);
         if (i < 2) {
-          if (i & 1) dp0 = mfma_score0_ab(A, vf[0]); else s0 = mfma_score0_ab(A, kf[0]);
+          if (i & 1) dp0 = mfma_score_c_ab(A, vf[0], nd0); else s0 = mfma_score0_ab(A, kf[0]);
         } else {
           if (i & 1) mfma_score_ab(dp0, A, vf[i >> 1]); else mfma_score_ab(s0, A, kf[i >> 1]);
         }
         op[i % kDep] = operand(i + kDep);
-        if (i == NST - 4) stats_rd(0, 0, lgn, dgn);
+        // the MFMA reads its C operand over several cycles: the -D registers are not
+        // reallocated until two MFMAs later
+        if (i == 3) asm volatile("" ::"v"(nd0));
+        if (i == NST / 2) nd1 = negd_rd(1);
+        if (i == NST - 4) stats_rd(0, 0, lgn);
         __builtin_amdgcn_sched_barrier(0);
       }
       // stage 1: S, dP of step 1 | P, dS of step 0
@@ -652,11 +690,12 @@ bwd_dkdv_kernel(BwdArgs a, int num_kv_tiles) {
         const int i = NST + j;
         const bf16x8 A = as_bf16x8(op[i % kDep]);
         if (j < 2) {
-          if (j & 1) dp1 = mfma_score0_ab(A, vf[0]); else s1 = mfma_score0_ab(A, kf[0]);
+          if (j & 1) dp1 = mfma_score_c_ab(A, vf[0], nd1); else s1 = mfma_score0_ab(A, kf[0]);
         } else {
           if (j & 1) mfma_score_ab(dp1, A, vf[j >> 1]); else mfma_score_ab(s1, A, kf[j >> 1]);
         }
         op[i % kDep] = operand(i + kDep);
+        if (j == 3) asm volatile("" ::"v"(nd1));
         if (j % (NST / 4) == 1) pds(s0, dp0, nm0, qv0, qpos0, 0, j / (NST / 4), pf0, dsf0);
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -716,7 +755,7 @@ bwd_dkdv_kernel(BwdArgs a, int num_kv_tiles) {
           float p = fast_exp2(fmaf(s[i], c, -l4[e]));
           if (need_mask && (qi >= qvalid || (CAUSAL && kpos > sfirst + qi))) p = 0.f;
           pv[e] = p;
-          dv4[e] = p * (dp[i] - d4[e]);
+          dv4[e] = p * (dp[i] + d4[e]);
         }
         // element i = 4g + e belongs to k-step s2 = g/2, slot w = 2*(g%2) + e/2
         const int s2 = g >> 1;
