@@ -168,8 +168,10 @@ def cpu_baseline(w, budget_s: float = 15.0):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    # untimed steps: the GPU's clocks take tens of milliseconds of load to settle (five
+    # warm-up steps of the headline measured 2 % slower than a hundred)
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", default="qwen7b_ulysses4_rank0_32k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
