@@ -401,6 +401,7 @@ def main():
         extra["permute_cold_ms_per_step"] = float(np.median(cold))
         extra["permute_cold_GBps"] = moved / (np.median(cold) * 1e-3) / 1e9
     extra["attn_fwd_ms"] = attn_avg
+    extra["attn_fwd_ms_median"] = float(np.median(attn_ms))
     extra["attn_fwd_ms_min"] = float(np.min(attn_ms))
     extra["attn_flops"] = flops
 

@@ -39,6 +39,9 @@ constexpr int TN = 64;  // rows per LDS tile of queries in bwd_dkdv
 #ifndef RA_BWD_DQ_UNROLL
 #define RA_BWD_DQ_UNROLL 2  // 32-key halves of a dQ tile unrolled together
 #endif
+#ifndef RA_BWD_DQ_NW
+#define RA_BWD_DQ_NW 8  // waves (32 query rows each) per dQ workgroup
+#endif
 #ifndef RA_BWD_DQ_KT
 #define RA_BWD_DQ_KT 64  // keys per LDS tile in bwd_dq (128 measured equal)
 #endif
@@ -221,9 +224,9 @@ __device__ __forceinline__ void ring_next_bwd(const BwdArgs &a, bool causal, int
 //   dQ^T += K^T_mt dS^T_mt                          (16 MFMAs over the tile)
 // ---------------------------------------------------------------------------------
 template <int D, bool CAUSAL, bool VARLEN, bool ACC>
-__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ void __launch_bounds__(64 * RA_BWD_DQ_NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 bwd_dq_kernel(BwdArgs a, int num_q_tiles) {
-  constexpr int NW = 8, BM = 32 * NW;
+  constexpr int NW = RA_BWD_DQ_NW, BM = 32 * NW;
   constexpr int KT = RA_BWD_DQ_KT;  // keys per LDS tile
   using Tile = STile<D, NW, KT>;
   __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * 2 * Tile::BYTES];
@@ -844,11 +847,12 @@ int launch_bwd(const BwdArgs &a, hipStream_t stream) {
   }
   // 3. dQ
   {
-    const int nqt = (a.Sq + 255) / 256;
+    constexpr int BM = 32 * RA_BWD_DQ_NW;
+    const int nqt = (a.Sq + BM - 1) / BM;
     const int64_t blocks = (int64_t)nqt * a.Hq * a.B;
     if (blocks > 0)
-      hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, VARLEN, ACC>), dim3((unsigned)blocks), dim3(512), 0,
-                         stream, a, nqt);
+      hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, VARLEN, ACC>), dim3((unsigned)blocks),
+                         dim3(64 * RA_BWD_DQ_NW), 0, stream, a, nqt);
   }
   return hipGetLastError() == hipSuccess ? RA_OK : RA_ERR_HIP;
 }
