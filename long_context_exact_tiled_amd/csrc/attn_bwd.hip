@@ -42,6 +42,9 @@ constexpr int TN = 64;  // rows per LDS tile of queries in bwd_dkdv
 #ifndef RA_BWD_DQ_NW
 #define RA_BWD_DQ_NW 8  // waves (32 query rows each) per dQ workgroup
 #endif
+#ifndef RA_BWD_DQ_HALF_LOADERS
+#define RA_BWD_DQ_HALF_LOADERS 1  // dQ: K/V tiles loaded by waves NW/2 .. NW-1 only
+#endif
 #ifndef RA_BWD_DQ_KT
 #define RA_BWD_DQ_KT 64  // keys per LDS tile in bwd_dq (128 measured equal)
 #endif
@@ -272,8 +275,20 @@ bwd_dq_kernel(BwdArgs a, int num_q_tiles) {
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt) dq[dt] = f32x16{};
 
-  typename Tile::Lane TL;
-  Tile::setup(TL, lane, wave);
+  // K/V tile loads by half of the waves (one per SIMD), which thereby start each tile's
+  // MFMAs later than the other half: the two waves of a SIMD alternate MFMA and
+  // softmax phases instead of running them together
+  constexpr int NL = RA_BWD_DQ_HALF_LOADERS ? NW / 2 : NW;
+  using LTile = STile<D, NL, KT>;
+  const int lw = __builtin_amdgcn_readfirstlane(wave) - (NW - NL);
+  typename LTile::Lane TL;
+  if (lw >= 0) LTile::setup(TL, lane, lw);
+  auto load_kv = [&](int kbx, uint32_t lds) {
+    if (lw >= 0) {
+      LTile::load(TL, kbase, a.k_ss, kbx, a.Skv, lds, lw);
+      LTile::load(TL, vbase, a.v_ss, kbx, a.Skv, lds + Tile::BYTES, lw);
+    }
+  };
   const uint32_t kpart = Tile::row_part(r32, h);  // rows r32 (+32 per mt)
   const uint32_t tp0 = Tile::tr_part(lane, 0), tp1 = Tile::tr_part(lane, 1);
 
@@ -297,10 +312,7 @@ bwd_dq_kernel(BwdArgs a, int num_q_tiles) {
     if (!CAUSAL) kend = __builtin_amdgcn_readfirstlane(max(l_de, l_ds));
     if (kb >= kend) t = a.num_chunks;
   }
-  if (t < a.num_chunks) {
-    Tile::load(TL, kbase, a.k_ss, kb, a.Skv, smem0, wave);
-    Tile::load(TL, vbase, a.v_ss, kb, a.Skv, smem0 + Tile::BYTES, wave);
-  }
+  if (t < a.num_chunks) load_kv(kb, smem0);
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
   __syncthreads();
 
@@ -308,11 +320,7 @@ bwd_dq_kernel(BwdArgs a, int num_q_tiles) {
   while (t < a.num_chunks) {
     const int kb_cur = kb, cend_cur = cend;
     ring_next_bwd<KT>(a, CAUSAL, vis_lim, t, kb, kend, cend);
-    if (t < a.num_chunks) {
-      const uint32_t nx = smem0 + (cur ^ 1) * 2 * Tile::BYTES;
-      Tile::load(TL, kbase, a.k_ss, kb, a.Skv, nx, wave);
-      Tile::load(TL, vbase, a.v_ss, kb, a.Skv, nx + Tile::BYTES, wave);
-    }
+    if (t < a.num_chunks) load_kv(kb, smem0 + (cur ^ 1) * 2 * Tile::BYTES);
     const int64_t kpos0 = a.kv_offset + kb_cur;
     const bool doc_skip =
         VARLEN && (kb_cur + KT <= w_ds_first || (!CAUSAL && kb_cur >= w_de_last));

@@ -68,6 +68,9 @@ constexpr int kBf16Waves = RA_FWD_BF16_WAVES;  // 8 measured faster than 2 x 4
 #ifndef RA_FWD_DIRECT_WAVES
 #define RA_FWD_DIRECT_WAVES 8  // waves per workgroup on the bf16 direct path
 #endif
+#ifndef RA_FWD_LOADER_MAP
+#define RA_FWD_LOADER_MAP 1  // bf16 direct kernel: 0 every wave loads, 1 waves NW/2.., 2 odd waves
+#endif
 #ifndef RA_FWD_DMA_LATE
 #define RA_FWD_DMA_LATE 0
 #endif
@@ -860,6 +863,21 @@ attn_fwd_direct_kernel(FwdArgs a) {
 
   typename Path::Lane L;
   Path::setup(L, a, tid, lds_offset(smem));
+  // Tile loads: by waves NW/2 .. NW-1 only (one per SIMD: waves are placed on the SIMDs
+  // round-robin).  Issuing a tile's direct loads holds a wave for about as long as one
+  // MFMA phase, so the loading wave of each SIMD starts its QK^T MFMAs that much later
+  // than the other: the two waves then alternate MFMA and softmax phases instead of
+  // running them together (4.5 % on the 32K causal GQA workload).  Odd waves as loaders
+  // (both on the same two SIMDs) measured no gain.
+  using LoadPath = Bf16DirectPath<D, (RA_FWD_LOADER_MAP ? NW / 2 : NW), KN>;
+  const int lw = RA_FWD_LOADER_MAP == 0 ? wave_u
+                 : RA_FWD_LOADER_MAP == 1 ? wave_u - NW / 2
+                                          : ((wave_u & 1) ? (wave_u >> 1) : -1);
+  typename LoadPath::Lane LL;
+  if (lw >= 0) LoadPath::setup(LL, a, 64 * lw + lane, lds_offset(smem));
+  auto load_tile = [&](int kbx, uint32_t slot) {
+    if (lw >= 0) LoadPath::load_tile(LL, a, kbase, vbase, kbx, slot, lw);
+  };
   typename Path::QFrag qf;
   Path::load_q(qf, a, qbase, qrow, h);
 
@@ -891,7 +909,7 @@ attn_fwd_direct_kernel(FwdArgs a) {
     if (kb >= kend) t = a.num_chunks;
   }
   const uint32_t smem0 = lds_offset(smem);
-  if (t < a.num_chunks) Path::load_tile(L, a, kbase, vbase, kb, smem0, wave);
+  if (t < a.num_chunks) load_tile(kb, smem0);
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): Q and the first tile have landed
   __syncthreads();
 
@@ -905,7 +923,7 @@ attn_fwd_direct_kernel(FwdArgs a) {
     const bool has_next = t < a.num_chunks;
 #if !RA_FWD_DMA_LATE
     if (has_next)
-      Path::load_tile(L, a, kbase, vbase, kb, smem0 + (cur ^ 1) * Path::BUF_BYTES, wave);
+      load_tile(kb, smem0 + (cur ^ 1) * Path::BUF_BYTES);
 #endif
 
     const int64_t kpos0 = a.kv_offset + kb_cur;
@@ -963,7 +981,7 @@ attn_fwd_direct_kernel(FwdArgs a) {
     }
 #if RA_FWD_DMA_LATE
     if (has_next)
-      Path::load_tile(L, a, kbase, vbase, kb, smem0 + (cur ^ 1) * Path::BUF_BYTES, wave);
+      load_tile(kb, smem0 + (cur ^ 1) * Path::BUF_BYTES);
 #endif
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the next tile's direct loads landed
     __syncthreads();
