@@ -42,8 +42,8 @@ constexpr int TN = 64;  // rows per LDS tile of queries in bwd_dkdv
 #ifndef RA_BWD_DQ_NW
 #define RA_BWD_DQ_NW 8  // waves (32 query rows each) per dQ workgroup
 #endif
-#ifndef RA_BWD_DQ_HALF_LOADERS
-#define RA_BWD_DQ_HALF_LOADERS 1  // dQ: K/V tiles loaded by waves NW/2 .. NW-1 only
+#ifndef RA_BWD_DQ_LOADERS
+#define RA_BWD_DQ_LOADERS (RA_BWD_DQ_NW / 2)  // dQ: waves (the last ones) that load K/V tiles
 #endif
 #ifndef RA_BWD_DKDV_LOADERS
 #define RA_BWD_DKDV_LOADERS 2  // dK/dV: waves that issue the Q/dO tile loads (the last ones)
@@ -281,7 +281,7 @@ bwd_dq_kernel(BwdArgs a, int num_q_tiles) {
   // K/V tile loads by half of the waves (one per SIMD), which thereby start each tile's
   // MFMAs later than the other half: the two waves of a SIMD alternate MFMA and
   // softmax phases instead of running them together
-  constexpr int NL = RA_BWD_DQ_HALF_LOADERS ? NW / 2 : NW;
+  constexpr int NL = RA_BWD_DQ_LOADERS;
   using LTile = STile<D, NL, KT>;
   const int lw = __builtin_amdgcn_readfirstlane(wave) - (NW - NL);
   typename LTile::Lane TL;
