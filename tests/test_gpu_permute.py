@@ -28,6 +28,8 @@ def _bits(t: torch.Tensor) -> np.ndarray:
     (2, 37, 6, 64, "bf16"),
     (8, 5, 8, 128, "f32"),
     (1, 19, 3, 64, "f32"),
+    (3, 11, 6, 96, "bf16"),       # 192-byte rows: the flat kernel
+    (2, 70, 4, 32, "bf16"),       # 64-byte rows: the flat kernel
 ])
 def test_permute_all_ranks_both_directions(P, Sl, H, D, dtype):
     say(f"permute P={P} Sl={Sl} H={H} D={D} {dtype}")
