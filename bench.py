@@ -107,8 +107,13 @@ def cpu_baseline(w, budget_s: float = 15.0):
     k64 = si.bf16_bits_to_f32(si.bf16_bits(k)).astype(np.float64)
     v64 = si.bf16_bits_to_f32(si.bf16_bits(v)).astype(np.float64)
     blk = 128
-    starts = list(range(0, Sq, blk))
-    rng.shuffle(starts)
+    # Passes over the sequence (a fresh random order of its 128-row blocks each, one pass
+    # per query head at most) until the time budget is spent.
+    starts = []
+    for _ in range(B * Hq):
+        order = list(range(0, Sq, blk))
+        rng.shuffle(order)
+        starts += order
     if w.fp8:  # the context's codes are set up once, like the inputs, before timing
         from oracle import fp8 as ofp8
         kc, kdd = ofp8.quantize_heads(k64.astype(np.float32))
@@ -156,8 +161,9 @@ def cpu_baseline(w, budget_s: float = 15.0):
     return {
         "value": done_flops / dt / 1e12, "unit": "TFLOP/s", "cores": blas_threads(),
         "kind": "oracle",
-        "sample": f"{rows} query rows ({rows // blk} blocks of {blk}, random positions) of "
-                  f"one head against its {'causal ' if w.causal else ''}"
+        "sample": f"{rows} query rows ({rows // blk} blocks of {blk} at random positions, "
+                  f"{math.ceil(rows / Sq)} pass(es) over the sequence) of one head against its "
+                  f"{'causal ' if w.causal else ''}"
                   f"{'own document' if cu is not None else str(Skv) + '-key context'}, "
                   f"{'backward' if w.backward else ('fp8 forward' if w.fp8 else 'forward')} "
                   f"oracle{' (context quantized before timing)' if w.fp8 else ''}, fp64 "
