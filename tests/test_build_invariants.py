@@ -16,8 +16,9 @@ import pytest
 
 from long_context_exact_tiled_amd import build as B
 
-HOT = ("attn_fwd_direct_kernel", "bwd_dq_kernel", "bwd_dkdv_kernel", "lse_merge_kernel",
-       "permute_kernel")
+HOT = ("attn_fwd_direct_kernel", "attn_fwd_fp8_kernel", "bwd_dq_kernel", "bwd_dkdv_kernel",
+       "lse_merge_kernel", "permute_kernel", "permute_rows_kernel", "quant_amax_kernel",
+       "quant_convert_kernel", "quant_convert_t_kernel", "bwd_delta_kernel")
 
 
 def _asm(src):
@@ -34,8 +35,7 @@ def _asm(src):
 def asm():
     if not (shutil.which("hipcc") or os.path.exists("/opt/rocm/bin/hipcc")):
         pytest.skip("hipcc not available")
-    return {src: _asm(src) for src in ("attn_fwd.hip", "attn_bwd.hip", "lse_merge.hip",
-                                       "ulysses_permute.hip")}
+    return {src: _asm(src) for src in B.SOURCES if src != "api.hip"}
 
 
 def test_m0_only_in_dma_sequences(asm):
