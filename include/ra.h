@@ -71,7 +71,22 @@ typedef struct {
   int64_t q_offset;     /* global position of query row 0 (>= 0) */
   int64_t kv_offset;    /* global position of key row 0 (>= 0) */
   float scale;          /* score scale; <= 0 selects 1/sqrt(D) */
+  /* Optional (present when struct_size >= RA_ATTN_PARAMS_SIZE_V2): DEVICE pointer to a
+   * uint64 work counter, 8-byte aligned and zero before its first use, or NULL.  The
+   * bf16 forward kernels (ra_attn_fwd, ra_attn_fwd_varlen) use it when B * Hq is not a
+   * multiple of 8: each workgroup then takes the next query tile from the counter when
+   * it starts, heaviest first, so XCDs that run faster take more tiles (the launch
+   * places workgroups on XCDs in a fixed round-robin order, and XCD speeds differ).
+   * Every call leaves the counter as it found it.  Results never depend on the
+   * counter's value; the tile order does (zero gives heaviest first).  Calls that share
+   * a counter must not overlap in time: use one counter per stream.  Other entry points,
+   * and shapes with B * Hq a multiple of 8, ignore it.  NULL: the fixed order. */
+  uint64_t *sched;
 } ra_attn_params;
+
+/* struct_size of ra_attn_params without / with the sched field; both are accepted. */
+#define RA_ATTN_PARAMS_SIZE_V1 40
+#define RA_ATTN_PARAMS_SIZE_V2 48
 
 typedef void *ra_stream; /* a hipStream_t */
 

@@ -61,7 +61,22 @@ class RaAttnParams(ctypes.Structure):
     _fields_ = [("struct_size", ctypes.c_uint32), ("causal", ctypes.c_int32),
                 ("num_chunks", ctypes.c_int32), ("start_chunk", ctypes.c_int32),
                 ("q_offset", ctypes.c_int64), ("kv_offset", ctypes.c_int64),
-                ("scale", ctypes.c_float)]
+                ("scale", ctypes.c_float), ("sched", ctypes.c_void_p)]
+
+
+# One zero-initialised uint64 work counter per (device, stream) for the bf16 forward's
+# tile order (ra_attn_params.sched): calls on one stream never overlap, and every call
+# leaves the counter as it found it.
+_SCHED = {}
+
+
+def _sched_counter(t: torch.Tensor) -> int:
+    key = (t.device.index, torch.cuda.current_stream(t.device).cuda_stream)
+    c = _SCHED.get(key)
+    if c is None:
+        c = torch.zeros(1, dtype=torch.int64, device=t.device)
+        _SCHED[key] = c
+    return c.data_ptr()
 
 
 _LIB = None
@@ -172,14 +187,17 @@ def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: bool 
              num_chunks: int = 1, start_chunk: int = 0, q_offset: int = 0, kv_offset: int = 0,
              scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
              lse: Optional[torch.Tensor] = None,
-             out_dtype: Optional[torch.dtype] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+             out_dtype: Optional[torch.dtype] = None,
+             sched: bool = True) -> Tuple[torch.Tensor, torch.Tensor]:
     """Exact attention of q [B,Hq,Sq,D] over k, v [B,Hkv,Skv,D] split into ``num_chunks``
-    chunks visited from ``start_chunk`` in ring order.  Returns (o, lse)."""
+    chunks visited from ``start_chunk`` in ring order.  Returns (o, lse).  ``sched``
+    passes this stream's work counter (tile order only; results are the same)."""
     if out is None:
         out = torch.empty(q.shape, dtype=out_dtype or q.dtype, device=q.device)
     if lse is None:
         lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
     p = _params(causal, num_chunks, start_chunk, q_offset, kv_offset, scale)
+    p.sched = _sched_counter(q) if sched and q.is_cuda else None
     dq, dk, dv, do, dl = desc(q), desc(k), desc(v), desc(out), desc(lse)
     _check(lib().ra_attn_fwd(dq, dk, dv, ctypes.byref(p), do, dl, _stream(q)))
     return out, lse
@@ -256,16 +274,18 @@ def _cu_arg(cu_seqlens: torch.Tensor):
 def attn_fwd_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens: torch.Tensor,
                     *, causal: bool = False, scale: Optional[float] = None,
                     out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
-                    out_dtype: Optional[torch.dtype] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+                    out_dtype: Optional[torch.dtype] = None,
+                    sched: bool = True) -> Tuple[torch.Tensor, torch.Tensor]:
     """Attention over packed documents: q [B,Hq,T,D], k, v [B,Hkv,T,D]; document d holds
     tokens cu_seqlens[d] .. cu_seqlens[d+1]-1 (a device int32 tensor) and each query sees
-    only its own document's keys.  Returns (o, lse)."""
+    only its own document's keys.  Returns (o, lse).  ``sched`` as for attn_fwd."""
     if out is None:
         out = torch.empty(q.shape, dtype=out_dtype or q.dtype, device=q.device)
     if lse is None:
         lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
     cu, n = _cu_arg(cu_seqlens)
     p = _params(causal, 1, 0, 0, 0, scale)
+    p.sched = _sched_counter(q) if sched and q.is_cuda else None
     _check(lib().ra_attn_fwd_varlen(desc(q), desc(k), desc(v), cu, n, ctypes.byref(p),
                                     desc(out), desc(lse), _stream(q)))
     return out, lse

@@ -2,6 +2,7 @@
 // validation, then dispatch to the kernel launchers.  Validation touches no device
 // state, so the *_validate entry points run on machines without a GPU.
 #include <math.h>
+#include <stddef.h>
 #include <string.h>
 
 #include <algorithm>
@@ -79,9 +80,18 @@ bool same_strides(const ra_tensor *a, const ra_tensor *b) {
     if (rc_ != RA_OK) return rc_; \
   } while (0)
 
+static_assert(offsetof(ra_attn_params, sched) == RA_ATTN_PARAMS_SIZE_V1 &&
+                  sizeof(ra_attn_params) == RA_ATTN_PARAMS_SIZE_V2,
+              "ra_attn_params layout");
+
+// The work counter of a version-2 parameter block, NULL for a version-1 one.
+uint64_t *sched_of(const ra_attn_params *p) {
+  return p->struct_size >= RA_ATTN_PARAMS_SIZE_V2 ? p->sched : nullptr;
+}
+
 int check_params(const ra_attn_params *p, int64_t Skv) {
   if (!p) return RA_ERR_NULL;
-  if (p->struct_size < sizeof(ra_attn_params)) return RA_ERR_RANGE;
+  if (p->struct_size < RA_ATTN_PARAMS_SIZE_V1) return RA_ERR_RANGE;
   if (p->causal != 0 && p->causal != 1) return RA_ERR_RANGE;
   if (p->num_chunks < 1) return RA_ERR_RANGE;
   if (p->start_chunk < 0 || p->start_chunk >= p->num_chunks) return RA_ERR_RANGE;
@@ -89,6 +99,7 @@ int check_params(const ra_attn_params *p, int64_t Skv) {
   if (p->q_offset > ((int64_t)1 << 40) || p->kv_offset > ((int64_t)1 << 40)) return RA_ERR_RANGE;
   if (!isfinite(p->scale)) return RA_ERR_RANGE;
   if (Skv % p->num_chunks) return RA_ERR_SHAPE;
+  if (sched_of(p) && ((uintptr_t)sched_of(p)) % 8) return RA_ERR_ALIGN;
   return RA_OK;
 }
 
@@ -396,6 +407,7 @@ int ra_attn_fwd(const ra_tensor *q, const ra_tensor *k, const ra_tensor *v,
   a.q_offset = p->q_offset; a.kv_offset = p->kv_offset;
   a.scale_log2 = effective_scale(p, q->shape[3]) * kLog2eHost;
   a.o_is_f32 = o->dtype == RA_F32;
+  a.sched = sched_of(p);
   return launch_attn_fwd(a, q->dtype, (int)q->shape[3], p->causal, (hipStream_t)stream);
 }
 
@@ -444,6 +456,7 @@ int ra_attn_fwd_varlen(const ra_tensor *q, const ra_tensor *k, const ra_tensor *
   a.o_is_f32 = o->dtype == RA_F32;
   a.cu = cu_seqlens;
   a.n_docs = n_docs;
+  a.sched = sched_of(p);
   return launch_attn_fwd_varlen(a, (int)q->shape[3], p->causal, (hipStream_t)stream);
 }
 

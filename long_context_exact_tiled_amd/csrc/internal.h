@@ -35,6 +35,8 @@ struct FwdArgs {
   // packed documents (attn_fwd_varlen only): document d holds tokens cu[d] .. cu[d+1]-1
   const int32_t *cu;
   int32_t n_docs;
+  // work counter (bf16 direct kernel, B*Hq not a multiple of 8): NULL = fixed tile order
+  uint64_t *sched;
 };
 
 int launch_attn_fwd(const FwdArgs &a, int dtype, int D, int causal, hipStream_t stream);

@@ -243,3 +243,27 @@ def test_fp8_quantize_validation(ra):
     assert val(_t((1, 3, 37, 8)), as8(torch.zeros(1, 3, 37, 8, dtype=torch.uint8)), desc) == \
         "RA_ERR_ALIGN"
     assert ra.lib().ra_fp8_quantize_workspace_size(ra.desc(x)) >= 3 * 4
+
+
+def test_params_versions_and_work_counter(ra):
+    """ra_attn_params: the version-1 block (no work counter) and the version-2 block are
+    both accepted; a smaller struct_size is out of range; a work counter must be 8-byte
+    aligned (only its address is checked: it is device memory)."""
+    assert ctypes.sizeof(ra.RaAttnParams) == 48
+    assert ra.RaAttnParams.sched.offset == 40
+    q, k, v = _t((1, 7, 64, 128)), _t((1, 1, 64, 128)), _t((1, 1, 64, 128))
+    o, lse = torch.zeros(q.shape, dtype=q.dtype), torch.zeros(q.shape[:3])
+
+    def check(size, sched):
+        p = ra._params(True, 1, 0, 0, 0, None)
+        p.struct_size = size
+        p.sched = sched
+        return ra.STATUS[ra.lib().ra_attn_fwd_validate(
+            ra.desc(q), ra.desc(k), ra.desc(v), ctypes.byref(p), ra.desc(o), ra.desc(lse))]
+
+    assert check(48, None) == "RA_OK"
+    assert check(48, 0x10000) == "RA_OK"
+    assert check(48, 0x10004) == "RA_ERR_ALIGN"
+    assert check(40, None) == "RA_OK"
+    assert check(40, 0x10004) == "RA_OK"  # a version-1 block has no counter field
+    assert check(39, None) == "RA_ERR_RANGE"

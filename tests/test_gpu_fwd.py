@@ -195,3 +195,37 @@ def test_qwen_ulysses_32k_workload():
     torch.cuda.synchronize()
     _sampled_check(w, o, lse, *(si.as_f64(x, "bf16") for x in (q_ref, k_ref, v_ref)), w.name,
                    per_head=12)
+
+
+def _counter(q):
+    ra._sched_counter(q)
+    return ra._SCHED[(q.device.index, torch.cuda.current_stream(q.device).cuda_stream)]
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,S,D", [(1, 7, 1, 1000, 128), (3, 2, 1, 777, 64),
+                                          (1, 28, 4, 700, 128)])
+def test_work_counter_changes_order_not_results(B, Hq, Hkv, S, D):
+    """With the work counter (B*Hq not a multiple of 8) workgroups take query tiles in
+    start order; the outputs are bitwise those of the fixed order, also when the counter
+    holds an arbitrary value (the order rotates), and every call leaves it as it was."""
+    say(f"work counter B={B} Hq={Hq} Hkv={Hkv} S={S} D={D}")
+    q, k, v = si.draw_qkv(11, (B, Hq, S, D), (B, Hkv, S, D), "bf16")
+    qd, kd, vd = to_dev(q, "bf16"), to_dev(k, "bf16"), to_dev(v, "bf16")
+    o0, l0 = ra.attn_fwd(qd, kd, vd, causal=True, sched=False)
+    ctr = _counter(qd)
+    for start in (0, 0, 12345, 2**40 + 3):
+        ctr.fill_(start)
+        o1, l1 = ra.attn_fwd(qd, kd, vd, causal=True)
+        torch.cuda.synchronize()
+        assert torch.equal(o1.view(torch.int16), o0.view(torch.int16)), start
+        assert torch.equal(l1.view(torch.int32), l0.view(torch.int32)), start
+        assert int(ctr.item()) == start
+    ctr.zero_()
+    # packed documents use the same kernel and counter
+    cu = torch.tensor([0, S // 3, S // 3 + 5, S], dtype=torch.int32, device="cuda")
+    o2, l2 = ra.attn_fwd_varlen(qd, kd, vd, cu, causal=True, sched=False)
+    o3, l3 = ra.attn_fwd_varlen(qd, kd, vd, cu, causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o3.view(torch.int16), o2.view(torch.int16))
+    assert torch.equal(l3.view(torch.int32), l2.view(torch.int32))
+    assert int(ctr.item()) == 0
