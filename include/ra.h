@@ -73,8 +73,8 @@ typedef struct {
   float scale;          /* score scale; <= 0 selects 1/sqrt(D) */
   /* Optional (present when struct_size >= RA_ATTN_PARAMS_SIZE_V2): DEVICE pointer to a
    * uint64 work counter, 8-byte aligned and zero before its first use, or NULL.  The
-   * bf16 forward kernels (ra_attn_fwd, ra_attn_fwd_varlen) use it when B * Hq is not a
-   * multiple of 8: each workgroup then takes the next query tile from the counter when
+   * forward kernels (ra_attn_fwd and ra_attn_fwd_varlen on bf16, ra_attn_fwd_fp8) use it
+   * when B * Hq is not a multiple of 8: each workgroup then takes the next query tile from the counter when
    * it starts, heaviest first, so XCDs that run faster take more tiles (the launch
    * places workgroups on XCDs in a fixed round-robin order, and XCD speeds differ).
    * Every call leaves the counter as it found it.  Results never depend on the

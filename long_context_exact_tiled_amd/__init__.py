@@ -239,14 +239,15 @@ def fp8_quantize_validate(x, out, descale, *, transpose=False) -> int:
 def attn_fwd_fp8(q, k, vt, q_descale, k_descale, v_descale, *, causal: bool = False,
                  num_chunks: int = 1, start_chunk: int = 0, q_offset: int = 0,
                  kv_offset: int = 0, scale: Optional[float] = None, out=None, lse=None,
-                 out_dtype: torch.dtype = torch.bfloat16):
+                 out_dtype: torch.dtype = torch.bfloat16, sched: bool = True):
     """attn_fwd over e4m3 codes (q, k [B,H,S,D]; vt [B,Hkv,D,S_pad]) with fp32 descales
-    per (batch, head).  Returns (o, lse)."""
+    per (batch, head).  Returns (o, lse).  ``sched`` as for attn_fwd."""
     if out is None:
         out = torch.empty(q.shape, dtype=out_dtype, device=q.device)
     if lse is None:
         lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
     p = _params(causal, num_chunks, start_chunk, q_offset, kv_offset, scale)
+    p.sched = _sched_counter(q) if sched and q.is_cuda else None
     _check(lib().ra_attn_fwd_fp8(desc(q), desc(k), desc(vt), desc(q_descale), desc(k_descale),
                                  desc(v_descale), ctypes.byref(p), desc(out), desc(lse),
                                  _stream(q)))

@@ -598,6 +598,7 @@ int ra_attn_fwd_fp8(const ra_tensor *q, const ra_tensor *k, const ra_tensor *vt,
   a.kd_sb = k_descale->stride[0]; a.kd_sh = k_descale->stride[1];
   a.vd_sb = v_descale->stride[0]; a.vd_sh = v_descale->stride[1];
   a.vt_cols = (int32_t)vt->shape[3];
+  f.sched = sched_of(p);
   return launch_attn_fwd_fp8(a, (int)q->shape[3], p->causal, (hipStream_t)stream);
 }
 

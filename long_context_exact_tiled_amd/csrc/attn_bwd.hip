@@ -392,11 +392,14 @@ bwd_dq_kernel(BwdArgs a, int num_q_tiles) {
 
   if (qrow < a.Sq) {
     const int64_t orow = b * a.dq_sb + hq * a.dq_sh + (int64_t)qrow * a.dq_ss;
+    // the lane half again, from the lane counter: keeping h alive across the key loop
+    // cost a register spill
+    const int he = (int)(__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)) >> 5);
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const int d = 32 * dt + 8 * g + 4 * h;
+        const int d = 32 * dt + 8 * g + 4 * he;
         if (ACC) {
           f32x4 *acc = (f32x4 *)((float *)a.dq + orow + d);
           const f32x4 prev = *acc;

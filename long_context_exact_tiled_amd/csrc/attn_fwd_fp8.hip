@@ -194,7 +194,22 @@ attn_fwd_fp8_kernel(Fp8Args a) {
   const int h = lane >> 5;
 
   const int HB = f.Hq * f.B;
-  const int bid = blockIdx.x;
+  // Query tile: heaviest first; with a work counter (B*Hq not a multiple of 8) taken in
+  // start order, so that faster XCDs take more tiles (same scheme as the bf16 kernel:
+  // ticket mod grid, the last residue's holder restores the counter).
+  __shared__ int s_job;
+  int bid = blockIdx.x;
+  if (f.sched != nullptr) {
+    if (threadIdx.x == 0) {
+      const unsigned long long g = gridDim.x;
+      const unsigned long long tk = atomicAdd((unsigned long long *)f.sched, 1ull);
+      const int job = (int)(tk % g);
+      if (job == (int)g - 1) atomicAdd((unsigned long long *)f.sched, 0ull - g);
+      s_job = job;
+    }
+    __syncthreads();
+    bid = __builtin_amdgcn_readfirstlane(s_job);
+  }
   const int trank = bid / HB;
   int j = bid - trank * HB;
   if ((HB & 7) == 0) j = (j & 7) * (HB >> 3) + (j >> 3);
@@ -214,9 +229,14 @@ attn_fwd_fp8_kernel(Fp8Args a) {
   const int64_t wpos_first = f.q_offset + q0 + 32 * wave_u;
   const int64_t wpos_last = wpos_first + 31;
   const bool wave_active = (q0 + 32 * wave_u) < f.Sq;
-  const float c = f.scale_log2 * a.q_desc[b * a.qd_sb + hq * a.qd_sh] *
-                  a.k_desc[b * a.kd_sb + hk * a.kd_sh];
-  const float vdesc = a.v_desc[b * a.vd_sb + hk * a.vd_sh];
+  // (wave-uniform values: kept in scalar registers, which the compiler cannot prove for
+  // loads that follow the work counter's atomic)
+  auto uniform = [](float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, x)));
+  };
+  const float c = uniform(f.scale_log2 * a.q_desc[b * a.qd_sb + hq * a.qd_sh] *
+                          a.k_desc[b * a.kd_sb + hk * a.kd_sh]);
+  const float vdesc = uniform(a.v_desc[b * a.vd_sb + hk * a.vd_sh]);
 
   const uint32_t smem0 = lds_offset(smem);
   typename T::Lane L;
@@ -385,6 +405,7 @@ int launch_fp8(const Fp8Args &args, hipStream_t stream) {
   a.f.num_q_tiles = (a.f.Sq + 32 * NW - 1) / (32 * NW);
   const int64_t blocks = (int64_t)a.f.num_q_tiles * a.f.Hq * a.f.B;
   if (blocks <= 0) return RA_OK;
+  if ((a.f.Hq * a.f.B) % 8 == 0) a.f.sched = nullptr;  // fixed XCD head map instead
   hipLaunchKernelGGL((attn_fwd_fp8_kernel<D, CAUSAL, KN, NW, RA_FP8_WPE>), dim3((unsigned)blocks),
                      dim3(64 * NW), 0, stream, a);
   return hipGetLastError() == hipSuccess ? RA_OK : RA_ERR_HIP;

@@ -55,13 +55,29 @@ def test_no_packed_fp32(asm):
         assert not re.search(r"\bv_pk_(fma|mul|add)_f32\b", text), src
 
 
+def _kernel_metadata(text):
+    """(name, private segment bytes, VGPR spills, SGPR spills) of every kernel, from the
+    code object metadata the compiler writes after the code."""
+    meta = text[text.find("amdhsa.kernels:"):]
+    out = []
+    for block in re.split(r"\n  - ", meta)[1:]:
+        name = re.search(r"\.name:\s+(\S+)", block)
+        priv = re.search(r"\.private_segment_fixed_size:\s+(\d+)", block)
+        vsp = re.search(r"\.vgpr_spill_count:\s+(\d+)", block)
+        ssp = re.search(r"\.sgpr_spill_count:\s+(\d+)", block)
+        if name and priv and vsp:
+            out.append((name.group(1), int(priv.group(1)), int(vsp.group(1)),
+                        int(ssp.group(1)) if ssp else 0))
+    return out
+
+
 def test_hot_kernels_do_not_spill(asm):
+    seen = set()
     for src, text in asm.items():
-        for m in re.finditer(r"^(\S+):\s*$", text, re.M):
-            name = m.group(1)
-            if not any(k in name for k in HOT) or name.startswith("."):
+        for name, priv, vspill, _ in _kernel_metadata(text):
+            if not any(k in name for k in HOT):
                 continue
-            body = text[m.end():text.find(".Lfunc_end", m.end())]
-            scratch = re.search(r";\s*ScratchSize:\s*(\d+)", text[m.end():])
-            assert "scratch_store" not in body and "buffer_store_dword v" not in body, (src, name)
-            assert scratch is None or int(scratch.group(1)) == 0, (src, name, scratch.group(1))
+            seen.update(k for k in HOT if k in name)
+            assert vspill == 0 and priv == 0, (src, name, vspill, priv)
+            assert "scratch_store" not in text, src
+    assert seen == set(HOT), set(HOT) - seen

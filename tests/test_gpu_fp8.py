@@ -226,3 +226,22 @@ def test_fp8_ring_chunked_and_fused(causal):
                                   q_offset=q_off).reshape(o_ref.shape)
     for o, l, what in ((o_c, l_c, "chunked"), (o_f, l_f, "fused")):
         _check(to_np64(o), l.cpu().numpy().astype(np.float64), o_ref, l_ref, bound, what)
+
+
+def test_fp8_work_counter_changes_order_not_results():
+    """The FP8 kernel takes query tiles from the stream's work counter when B*Hq is not a
+    multiple of 8: bitwise the outputs of the fixed order, whatever the counter held,
+    and the counter is left as it was."""
+    say("fp8 work counter")
+    (qc, kc, vtc, qd, kd, vd), _ = _fp8_inputs(1, 7, 1, 900, 900, 128, 33)
+    o0, l0 = ra.attn_fwd_fp8(qc, kc, vtc, qd, kd, vd, causal=True, sched=False)
+    ra._sched_counter(qc)
+    ctr = ra._SCHED[(qc.device.index, torch.cuda.current_stream(qc.device).cuda_stream)]
+    for start in (0, 77, 2**33 + 5):
+        ctr.fill_(start)
+        o1, l1 = ra.attn_fwd_fp8(qc, kc, vtc, qd, kd, vd, causal=True)
+        torch.cuda.synchronize()
+        assert torch.equal(o1.view(torch.int16), o0.view(torch.int16)), start
+        assert torch.equal(l1.view(torch.int32), l0.view(torch.int32)), start
+        assert int(ctr.item()) == start
+    ctr.zero_()
