@@ -80,7 +80,9 @@ typedef struct {
    * Every call leaves the counter as it found it.  Results never depend on the
    * counter's value; the tile order does (zero gives heaviest first).  Calls that share
    * a counter must not overlap in time: use one counter per stream.  Other entry points,
-   * and shapes with B * Hq a multiple of 8, ignore it.  NULL: the fixed order. */
+   * and shapes with B * Hq a multiple of 8, do not touch it; every call that takes
+   * ra_attn_params rejects a non-NULL counter that is not 8-byte aligned
+   * (RA_ERR_ALIGN).  NULL: the fixed order. */
   uint64_t *sched;
 } ra_attn_params;
 
