@@ -406,6 +406,35 @@ def main():
         del scratch
         extra["permute_cold_ms_per_step"] = float(np.median(cold))
         extra["permute_cold_GBps"] = moved / (np.median(cold) * 1e-3) / 1e9
+    if args.chunked and not w.backward and not w.fp8:
+        # the merge alone: partials of the visible chunks computed once, then lse_merge
+        # timed by itself (HBM-bound: every partial read once, the result written once)
+        L = w.kv_shape[2] // w.num_chunks
+        chunks = ra.ring_visible_chunks(w.q_shape[2], w.kv_shape[2], num_chunks=w.num_chunks,
+                                        start_chunk=w.start_chunk, causal=w.causal,
+                                        q_offset=w.q_offset, kv_offset=w.kv_offset)
+        parts = [ra.attn_fwd(q, k[:, :, c * L:(c + 1) * L], v[:, :, c * L:(c + 1) * L],
+                             causal=w.causal, q_offset=w.q_offset,
+                             kv_offset=w.kv_offset + c * L, out_dtype=torch.float32)
+                 for c in chunks]
+        mo, ml = ra.lse_merge([x[0] for x in parts], [x[1] for x in parts])
+        torch.cuda.synchronize()
+        mt = []
+        for _ in range(5):  # 20 back-to-back merges per sample
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(20):
+                ra.lse_merge([x[0] for x in parts], [x[1] for x in parts], out=mo, lse=ml)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            mt.append(e0.elapsed_time(e1) / 20)
+        mbytes = sum(x[0].numel() * 4 + x[1].numel() * 4 for x in parts) + \
+            mo.numel() * mo.element_size() + ml.numel() * 4
+        extra["merge_parts"] = len(parts)
+        extra["merge_ms"] = float(np.median(mt))
+        extra["merge_GBps"] = mbytes / (np.median(mt) * 1e-3) / 1e9
+        extra["merge_frac_of_hbm_peak"] = extra["merge_GBps"] / PEAK_HBM_GBPS
+        del parts
     extra["attn_fwd_ms"] = attn_avg
     extra["attn_fwd_ms_median"] = float(np.median(attn_ms))
     extra["attn_fwd_ms_min"] = float(np.min(attn_ms))
