@@ -36,6 +36,7 @@ namespace ra {
 namespace {
 
 constexpr int TN = 64;  // rows per LDS tile of queries in bwd_dkdv
+static_assert(TN <= kMaxTileRows, "tile offsets are 32-bit");
 #ifndef RA_BWD_DQ_UNROLL
 #define RA_BWD_DQ_UNROLL 2  // 32-key halves of a dQ tile unrolled together
 #endif
@@ -51,12 +52,6 @@ constexpr int TN = 64;  // rows per LDS tile of queries in bwd_dkdv
 #ifndef RA_BWD_DQ_KT
 #define RA_BWD_DQ_KT 64  // keys per LDS tile in bwd_dq (128 measured equal)
 #endif
-#ifndef RA_BWD_DKDV_PIPE
-#define RA_BWD_DKDV_PIPE 1  // software-pipelined dK/dV tile
-#endif
-#ifndef RA_BWD_SCORE_ASM
-#define RA_BWD_SCORE_ASM 1  // dK/dV kernel: register placement by inline-asm MFMAs
-#endif
 
 // Register placement in the dK/dV kernel (one wave per SIMD, ~370 live registers).  The
 // compiler's choice -- every MFMA accumulator in VGPRs, other values spilled to AGPRs --
@@ -70,39 +65,23 @@ constexpr int TN = 64;  // rows per LDS tile of queries in bwd_dkdv
 // accumulators overlap exactly, and the epilogue waits explicitly.
 // dK or dV += A B (accumulator in AGPRs, A and B in VGPRs)
 __device__ __forceinline__ void mfma_grad(f32x16 &acc, const bf16x8 &a, const bf16x8 &b) {
-#if RA_BWD_SCORE_ASM
   asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
-#else
-  acc = mfma_bf16(a, b, acc);
-#endif
 }
 // S or dP: first step of a chain (C = 0) and further steps; the B operand (the key/value
 // rows kept for the whole workgroup) is read straight from AGPRs, the result is a VGPR.
 __device__ __forceinline__ f32x16 mfma_score0_ab(const bf16x8 &a, const bf16x8 &b) {
-#if RA_BWD_SCORE_ASM
   f32x16 d;
   asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "a"(b));
   return d;
-#else
-  return mfma_bf16(a, b, f32x16{});
-#endif
 }
 __device__ __forceinline__ f32x16 mfma_score_c_ab(const bf16x8 &a, const bf16x8 &b,
                                                    const f32x16 &c) {
-#if RA_BWD_SCORE_ASM
   f32x16 d;
   asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %3" : "=&v"(d) : "v"(a), "a"(b), "v"(c));
   return d;
-#else
-  return mfma_bf16(a, b, c);
-#endif
 }
 __device__ __forceinline__ void mfma_score_ab(f32x16 &acc, const bf16x8 &a, const bf16x8 &b) {
-#if RA_BWD_SCORE_ASM
   asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "a"(b));
-#else
-  acc = mfma_bf16(a, b, acc);
-#endif
 }
 
 // 16-byte-chunk swizzle of a tile row: for 16 consecutive rows at one chunk the physical
@@ -234,6 +213,7 @@ __global__ void __launch_bounds__(64 * RA_BWD_DQ_NW) __attribute__((amdgpu_waves
 bwd_dq_kernel(BwdArgs a, int num_q_tiles) {
   constexpr int NW = RA_BWD_DQ_NW, BM = 32 * NW;
   constexpr int KT = RA_BWD_DQ_KT;  // keys per LDS tile
+  static_assert(KT <= kMaxTileRows, "tile offsets are 32-bit");
   using Tile = STile<D, NW, KT>;
   __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * 2 * Tile::BYTES];
   const uint32_t smem0 = lds_offset(smem);
@@ -460,24 +440,20 @@ bwd_dkdv_kernel(BwdArgs a, int num_kv_tiles) {
     kf[ks] = as_bf16x8(*(const u32x4 *)(kb_ + (int64_t)kr * a.k_ss + 16 * ks + 8 * h));
     vf[ks] = as_bf16x8(*(const u32x4 *)(vb_ + (int64_t)kr * a.v_ss + 16 * ks + 8 * h));
   }
-#if RA_BWD_SCORE_ASM
   // K^T and V^T are only ever MFMA B operands from here on: keep them in AGPRs
 #pragma unroll
   for (int ks = 0; ks < D / 16; ++ks) {
     asm volatile("" : "+a"(kf[ks]));
     asm volatile("" : "+a"(vf[ks]));
   }
-#endif
 
   f32x16 dk[D / 32], dv[D / 32];
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt) {
     dk[dt] = f32x16{};
     dv[dt] = f32x16{};
-#if RA_BWD_SCORE_ASM
     asm volatile("" : "+a"(dk[dt]));  // the accumulators live in AGPRs from the start
     asm volatile("" : "+a"(dv[dt]));
-#endif
   }
 
   // Q/dO tile loads by the last two waves only: issuing them holds those waves back, so
@@ -514,7 +490,6 @@ bwd_dkdv_kernel(BwdArgs a, int num_kv_tiles) {
   // to its last key's document end.
   int ds = 0, de = 0, w_ds_first = 0, w_ds_last = 0, w_de_first = 0, w_de_last = 0;
   if (VARLEN) {
-    static_assert(!VARLEN || RA_BWD_DKDV_PIPE, "packed documents use the pipelined tile");
     doc_bounds(a.cu, a.n_docs, kr, a.Sq, ds, de);
     w_ds_first = __builtin_amdgcn_readlane(ds, 0);
     w_ds_last = __builtin_amdgcn_readlane(ds, 31);
@@ -589,7 +564,6 @@ bwd_dkdv_kernel(BwdArgs a, int num_kv_tiles) {
     qt_c = qt_n;
     hg_c = hg_n;
     const int64_t qpos0 = a.q_offset + q0;
-#if RA_BWD_DKDV_PIPE
     // The two 32-query steps of the tile as one stream of 4*NST MFMAs, operands read
     // kDep MFMAs ahead:  [S,dP of step 0] [S,dP of step 1 | P,dS of step 0]
     // [dV,dK of step 0 | P,dS of step 1] [dV,dK of step 1].  A step with no visible
@@ -747,74 +721,15 @@ bwd_dkdv_kernel(BwdArgs a, int num_kv_tiles) {
         __builtin_amdgcn_sched_barrier(0);
       }
     }
-#else
-#pragma unroll
-    for (int qs = 0; qs < 2; ++qs) {
-      const int64_t sfirst = qpos0 + 32 * qs, slast = sfirst + 31;  // query positions
-      const int qvalid = min(32, a.Sq - (q0 + 32 * qs));
-      if (!wave_active || qvalid <= 0 || (CAUSAL && wk_first > slast)) continue;
-      const bool need_mask = qvalid < 32 || (CAUSAL && wk_last > sfirst);
-      const uint32_t qo = slot + (uint32_t)(32 * qs * Tile::RB);
-      const uint32_t oo = qo + Tile::BYTES;
-      f32x16 s = f32x16{}, dp = f32x16{};
-#pragma unroll
-      for (int ks = 0; ks < D / 16; ++ks) {
-        s = mfma_bf16(as_bf16x8(Tile::row_read(qo, qpart, ks)), kf[ks], s);
-        dp = mfma_bf16(as_bf16x8(Tile::row_read(oo, qpart, ks)), vf[ks], dp);
-      }
-      // lane: key column r32; element i is query row (i/4)*8 + 4h + i%4 of this step
-      const uint32_t st = slot + 2 * Tile::BYTES + (uint32_t)(4 * 32 * qs);
-      u32x4 pf[2], dsf[2];
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const f32x4 l4 = *(const __attribute__((address_space(3))) f32x4 *)(size_t)(
-            st + (uint32_t)(4 * (8 * g + 4 * h)));
-        const f32x4 d4 = *(const __attribute__((address_space(3))) f32x4 *)(size_t)(
-            st + (uint32_t)(4 * TN + 4 * (8 * g + 4 * h)));
-        float pv[4], dv4[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int i = 4 * g + e;
-          const int qi = (i >> 2) * 8 + 4 * h + (i & 3);  // row within the step
-          float p = fast_exp2(fmaf(s[i], c, -l4[e]));
-          if (need_mask && (qi >= qvalid || (CAUSAL && kpos > sfirst + qi))) p = 0.f;
-          pv[e] = p;
-          dv4[e] = p * (dp[i] + d4[e]);
-        }
-        // element i = 4g + e belongs to k-step s2 = g/2, slot w = 2*(g%2) + e/2
-        const int s2 = g >> 1;
-        const bf16x2 p01 = __builtin_convertvector((f32x2){pv[0], pv[1]}, bf16x2);
-        const bf16x2 p23 = __builtin_convertvector((f32x2){pv[2], pv[3]}, bf16x2);
-        const bf16x2 d01 = __builtin_convertvector((f32x2){dv4[0], dv4[1]}, bf16x2);
-        const bf16x2 d23 = __builtin_convertvector((f32x2){dv4[2], dv4[3]}, bf16x2);
-        pf[s2][2 * (g & 1)] = __builtin_bit_cast(uint32_t, p01);
-        pf[s2][2 * (g & 1) + 1] = __builtin_bit_cast(uint32_t, p23);
-        dsf[s2][2 * (g & 1)] = __builtin_bit_cast(uint32_t, d01);
-        dsf[s2][2 * (g & 1) + 1] = __builtin_bit_cast(uint32_t, d23);
-      }
-      // dV^T[D x 32 keys] += dO^T[D x 32 q] P[32 q x 32 keys];  dK^T += Q^T dS
-#pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2)
-#pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt) {
-          const u32x4 of = Tile::tr_read(oo, tp0, tp1, 16 * s2, dt);
-          dv[dt] = mfma_bf16(as_bf16x8(of), as_bf16x8(pf[s2]), dv[dt]);
-          const u32x4 qf2 = Tile::tr_read(qo, tp0, tp1, 16 * s2, dt);
-          dk[dt] = mfma_bf16(as_bf16x8(qf2), as_bf16x8(dsf[s2]), dk[dt]);
-        }
-    }
-#endif
     if (has_next) stats_store(sv, smem0 + (cur ^ 1) * SLOT);
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): next tile landed
     __syncthreads();
     cur ^= 1;
   }
 
-#if RA_BWD_SCORE_ASM
   // the compiler does not see the asm MFMAs: give their results time to land before
   // the epilogue reads the accumulators
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
-#endif
   if (krow < a.Skv) {
     const int64_t krow_dk = b * a.dk_sb + hk * a.dk_sh + (int64_t)krow * a.dk_ss;
     const int64_t krow_dv = b * a.dv_sb + hk * a.dv_sh + (int64_t)krow * a.dv_ss;

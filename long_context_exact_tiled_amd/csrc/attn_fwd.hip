@@ -15,19 +15,19 @@
 //
 // Design on gfx950 (CDNA4), from measured rates (MFMA 32x32x16 bf16 ~37 clk/SIMD;
 // v_exp_f32 ~4-5x a plain VALU op; ds_read_b128 ~190 B/clk/CU vs ~120 for b64):
-//   * one workgroup = 8 wavefronts = 256 query rows (32 per wave) of one (batch, head);
-//     two waves per SIMD, so one wave's softmax (VALU) runs under the other's MFMAs;
-//     all 8 waves share each K/V tile in LDS (one global read of K/V per 256 rows);
-//   * K/V tiles of 64 keys, double-buffered in LDS: the next tile's global loads are
-//     issued before the current tile's math and stored to the other buffer after it;
-//     waves 0-3 fetch V, waves 4-7 fetch K; loads are unconditional (rows past the end
-//     are clamped and masked), so the compiler's memory counters stay exact;
+//   * bf16 (attn_fwd_direct_kernel): one workgroup = 8 wavefronts = 256 query rows (32
+//     per wave) of one (batch, head), two waves per SIMD, so one wave's softmax (VALU)
+//     runs under the other's MFMAs; all 8 waves share each K/V tile in LDS;
+//   * K/V tiles of 128 keys go straight from global memory into LDS
+//     (global_load_lds_dwordx4), double-buffered, XOR-swizzled so every operand read is
+//     bank-conflict free; the next tile's loads are in flight under the current tile's
+//     math and are issued by one wave per SIMD only, which staggers the two waves of a
+//     SIMD;
 //   * scores are computed transposed, S^T = K Q^T (Q stays in registers as the B
 //     operand): each lane owns ONE query row and 16 of each 32 keys, so the row max is
 //     in-register v_max3 plus one v_permlane32_swap and the row sum needs no shuffle;
-//   * P^T feeds O^T += V^T P^T straight from registers.  V is transposed on its way into
-//     LDS with its keys permuted so that the 8 keys a lane needs for one MFMA are
-//     contiguous: every MFMA operand is a single conflict-free ds_read_b128;
+//   * P^T feeds O^T += V^T P^T straight from registers; the V^T operand comes from the
+//     row-major V tile through the transposing LDS read (ds_read_b64_tr_b16);
 //   * exp2 with scale*log2(e) folded into one FMA per score; P rounded to bf16 with one
 //     v_cvt_pk per pair for the PV MFMA, while the row sum adds the fp32 values;
 //   * lazy rescale: the running max only moves (and O, l are only rescaled) when a
@@ -37,9 +37,11 @@
 //   * the ring walk skips chunks (and tiles) that lie entirely after the block's last
 //     query position under the causal mask; only tiles that straddle the diagonal or a
 //     chunk end pay for the element mask; waves whose rows all precede a tile skip it;
-//   * heaviest query tiles are dispatched first (causal work grows with the tile
-//     index), and heads are grouped so that consecutive workgroups -- which the
-//     dispatcher spreads over the 8 XCDs -- land on XCDs that share key/value heads.
+//   * heaviest query tiles first (causal work grows with the tile index); with 8 | B*Hq
+//     the heads are grouped so that each XCD sees a fixed subset of them, otherwise the
+//     workgroups take their tiles from a work counter in start order;
+//   * fp32 (attn_fwd_kernel<F32Path>): the same walk and softmax with 32x32x2 fp32 MFMAs,
+//     64-key tiles staged through registers into LDS.
 #include <math.h>
 
 #include <type_traits>
@@ -50,241 +52,12 @@
 namespace ra {
 namespace {
 
-constexpr int BN = 64;           // keys per tile
+constexpr int BN = 64;           // keys per tile of the fp32 path
 constexpr float kLazyRescale = 8.0f;  // log2 units
-#ifndef RA_FWD_BF16_WAVES
-#define RA_FWD_BF16_WAVES 8
-#endif
-constexpr int kBf16Waves = RA_FWD_BF16_WAVES;  // 8 measured faster than 2 x 4
-#ifndef RA_FWD_DIRECT
-#define RA_FWD_DIRECT 1
-#endif
-#ifndef RA_FWD_DMA_ASM
-#define RA_FWD_DMA_ASM 1
-#endif
-#ifndef RA_FWD_KN
-#define RA_FWD_KN 128  // keys per tile on the bf16 direct path (measured: 3.6 % faster than 64)
-#endif
-#ifndef RA_FWD_DIRECT_WAVES
-#define RA_FWD_DIRECT_WAVES 8  // waves per workgroup on the bf16 direct path
-#endif
-#ifndef RA_FWD_LOADER_MAP
-#define RA_FWD_LOADER_MAP 1  // bf16 direct kernel: 0 every wave loads, 1 waves NW/2.., 2 odd waves
-#endif
-#ifndef RA_FWD_DMA_LATE
-#define RA_FWD_DMA_LATE 0
-#endif
-#ifndef RA_FWD_PIPELINE
-#define RA_FWD_PIPELINE 0
-#endif
+constexpr int kDirectWaves = 8;  // waves per workgroup on the bf16 path (32 query rows each)
+constexpr int kDirectKN = 128;   // keys per tile on the bf16 path (measured 3.6 % faster than 64)
+static_assert(kDirectKN <= kMaxTileRows && BN <= kMaxTileRows, "tile offsets are 32-bit");
 
-
-// ---------------------------------------------------------------------------------
-// bf16 path: 32x32x16 bf16 MFMA; K row-major in LDS, V transposed + key-permuted in LDS.
-// ---------------------------------------------------------------------------------
-template <int D, int NW>
-struct Bf16Path {
-  using elem_t = uint16_t;
-  static constexpr int kWaves = NW;           // 32 query rows per wave
-  static constexpr int kThreads = 64 * NW;
-  static constexpr int KSTR = D + 8;    // K row stride (elements): 68 dwords for D=128
-  static constexpr int VSTR = BN + 8;   // V^T row stride: 36 dwords -> b128 reads conflict-free
-  static constexpr int K_ELEMS = BN * KSTR;
-  static constexpr int V_ELEMS = D * VSTR;
-  static constexpr int BUF_BYTES = (K_ELEMS + V_ELEMS) * 2;
-  // With 8 waves, threads 0..255 fetch V and 256..511 fetch K; with 4 waves every
-  // thread fetches one V block and its share of K.
-  static constexpr int KT = NW == 8 ? 256 : 64 * NW;  // threads fetching K
-  static constexpr int KCH = BN * D / 8 / KT;          // 16-byte K chunks per such thread
-  static constexpr int VBC = D / 8;                    // 8-wide column groups of V
-  static constexpr int VOFF = NW == 8 ? 0 : 4;         // first staging slot of K
-  static constexpr int NST = NW == 8 ? (KCH > 4 ? KCH : 4) : 4 + KCH;
-
-  struct QFrag { bf16x8 x[D / 16]; };
-  struct Stage { u32x4 x[NST]; };
-  struct PFrag { u32x4 x[4]; };
-  static constexpr bool kPipelined = RA_FWD_PIPELINE;  // three LDS tiles fit (105 KiB)
-
-  // One pipelined step: S^T of the NEXT tile (QK MFMAs, K from slot bn) interleaved by
-  // hand with the softmax of the CURRENT tile (sc -> bf16 P), then O^T += V^T P^T with V
-  // from slot bc.  Each QK MFMA is paired with one pair of exponentials and the K read
-  // kDepth steps ahead; the fences keep the scheduler from regrouping them.  Returns
-  // this lane's share of the current tile's exp-sum.
-  __device__ static float fused_step(f32x16 (&sn)[2], const QFrag &qf, const elem_t *bn,
-                                     const f32x16 (&sc)[2], float c, float mneg,
-                                     f32x16 (&o)[D / 32], const elem_t *bc, int lane) {
-    const int r = lane & 31, h = lane >> 5;
-    constexpr int NQK = 2 * (D / 16), NPV = 4 * (D / 32);
-    constexpr int PPS = 16 / NQK;  // softmax pairs per QK MFMA (16 pairs per tile)
-    u32x4 kf[kDepth];
-    VPre vp;
-#pragma unroll
-    for (int i = 0; i < kDepth; ++i) kf[i] = k_frag(bn, i, r, h);
-#pragma unroll
-    for (int i = 0; i < kDepth; ++i) vp.x[i] = v_frag(bc, i, r, h);
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt) sn[mt] = f32x16{};
-    PFrag pf;
-    float acc0 = 0.f, acc1 = 0.f;
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int step = 0; step < NQK; ++step) {
-      const int ks = step >> 1, mt = step & 1;
-      sn[mt] = mfma_bf16(as_bf16x8(kf[step % kDepth]), qf.x[ks], sn[mt]);
-      if (step + kDepth < NQK) kf[step % kDepth] = k_frag(bn, step + kDepth, r, h);
-#pragma unroll
-      for (int j = 0; j < PPS; ++j) {
-        const int pair = step * PPS + j;
-        const int kstep = pair >> 2, w = pair & 3;
-        const int m2 = kstep >> 1, s2 = kstep & 1;
-        const float p0 = fast_exp2(fmaf(sc[m2][8 * s2 + 2 * w], c, mneg));
-        const float p1 = fast_exp2(fmaf(sc[m2][8 * s2 + 2 * w + 1], c, mneg));
-        const bf16x2 pk = __builtin_convertvector((f32x2){p0, p1}, bf16x2);
-        pf.x[kstep][w] = __builtin_bit_cast(uint32_t, pk);
-        acc0 += p0;
-        acc1 += p1;
-      }
-      __builtin_amdgcn_sched_barrier(0);
-    }
-#pragma unroll
-    for (int step = 0; step < NPV; ++step) {
-      const int kstep = step / (D / 32), dt = step % (D / 32);
-      o[dt] = mfma_bf16(as_bf16x8(vp.x[step % kDepth]), as_bf16x8(pf.x[kstep]), o[dt]);
-      if (step + kDepth < NPV) vp.x[step % kDepth] = v_frag(bc, step + kDepth, r, h);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    return acc0 + acc1;
-  }
-
-  __device__ static void load_q(QFrag &qf, const FwdArgs &a, const elem_t *qbase, int qrow, int h) {
-    const int row = min(qrow, a.Sq - 1);
-#pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks)
-      qf.x[ks] = as_bf16x8(*(const u32x4 *)(qbase + (int64_t)row * a.q_ss + ks * 16 + 8 * h));
-  }
-
-  // V is fetched as 4-key x 8-dim blocks (key fastest across lanes), K as 16-byte row
-  // chunks.  Rows >= Skv are clamped (and masked later).
-  __device__ static void load_tile(Stage &st, const FwdArgs &a, const elem_t *kbase,
-                                   const elem_t *vbase, int kb, int tid) {
-    const bool v_role = NW == 8 ? tid < 256 : true;
-    const bool k_role = NW == 8 ? tid >= 256 : true;
-    if (v_role && tid < 16 * VBC) {
-      const int r = tid & 15, c = tid >> 4;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int kv = min(kb + 4 * r + i, a.Skv - 1);
-        st.x[i] = *(const u32x4 *)(vbase + (int64_t)kv * a.v_ss + c * 8);
-      }
-    }
-    if (k_role) {
-      const int t = NW == 8 ? tid - 256 : tid;
-#pragma unroll
-      for (int i = 0; i < KCH; ++i) {
-        const int id = t + KT * i;
-        const int row = id / (D / 8), c8 = id % (D / 8);
-        const int kv = min(kb + row, a.Skv - 1);
-        st.x[VOFF + i] = *(const u32x4 *)(kbase + (int64_t)kv * a.k_ss + c8 * 8);
-      }
-    }
-  }
-
-  __device__ static void store_tile(const Stage &st, elem_t *buf, int tid) {
-    const bool v_role = NW == 8 ? tid < 256 : true;
-    const bool k_role = NW == 8 ? tid >= 256 : true;
-    if (v_role && tid < 16 * VBC) {
-      elem_t *Vt = buf + K_ELEMS;
-      const int r = tid & 15, c = tid >> 4;
-      // keys 4r..4r+3 = 16*ks + 8*a + 4*hh + (0..3) go to positions 16*ks + 8*hh + 4*a
-      const int pos = 16 * (r >> 2) + 8 * (r & 1) + 4 * ((r >> 1) & 1);
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;
-        const int w = j >> 1;
-        const uint32_t lo = perm_b32(st.x[1][w], st.x[0][w], sel);
-        const uint32_t hi = perm_b32(st.x[3][w], st.x[2][w], sel);
-        *(u32x2 *)(Vt + (c * 8 + j) * VSTR + pos) = u32x2{lo, hi};
-      }
-    }
-    if (k_role) {
-      const int t = NW == 8 ? tid - 256 : tid;
-#pragma unroll
-      for (int i = 0; i < KCH; ++i) {
-        const int id = t + KT * i;
-        const int row = id / (D / 8), c8 = id % (D / 8);
-        *(u32x4 *)(buf + row * KSTR + c8 * 8) = st.x[VOFF + i];
-      }
-    }
-  }
-
-  // S^T[32 keys x 32 queries] for the two 32-key halves of the tile.  K fragments are
-  // read from LDS kDepth MFMAs ahead of their use (an LDS round trip is several MFMAs).
-  static constexpr int kDepth = 2;
-  __device__ static u32x4 k_frag(const elem_t *buf, int step, int r, int h) {
-    const int ks = step >> 1, mt = step & 1;
-    return *(const u32x4 *)(buf + (32 * mt + r) * KSTR + ks * 16 + 8 * h);
-  }
-  __device__ static void qk(f32x16 (&s)[2], const QFrag &qf, const elem_t *buf, int lane) {
-    const int r = lane & 31, h = lane >> 5;
-    constexpr int NSTEP = 2 * (D / 16);
-    u32x4 kf[kDepth];
-#pragma unroll
-    for (int i = 0; i < kDepth; ++i) kf[i] = k_frag(buf, i, r, h);
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt) s[mt] = f32x16{};
-#pragma unroll
-    for (int step = 0; step < NSTEP; ++step) {
-      const int ks = step >> 1, mt = step & 1;
-      s[mt] = mfma_bf16(as_bf16x8(kf[step % kDepth]), qf.x[ks], s[mt]);
-      if (step + kDepth < NSTEP) kf[step % kDepth] = k_frag(buf, step + kDepth, r, h);
-    }
-  }
-
-  // p = exp2(s*c - m) -> bf16 pairs (the B operand of PV); returns this lane's sum of
-  // the fp32 values (the sum must not carry the bf16 rounding of single terms: rows
-  // with few visible keys would show it directly in lse).
-  __device__ static float exp_pack(const f32x16 (&s)[2], float c, float mneg, PFrag &pf) {
-    float acc0 = 0.f, acc1 = 0.f;
-#pragma unroll
-    for (int kstep = 0; kstep < 4; ++kstep) {
-      const int mt = kstep >> 1, s2 = kstep & 1;
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const float p0 = fast_exp2(fmaf(s[mt][8 * s2 + 2 * w], c, mneg));
-        const float p1 = fast_exp2(fmaf(s[mt][8 * s2 + 2 * w + 1], c, mneg));
-        const bf16x2 pk = __builtin_convertvector((f32x2){p0, p1}, bf16x2);
-        pf.x[kstep][w] = __builtin_bit_cast(uint32_t, pk);
-        acc0 += p0;
-        acc1 += p1;
-      }
-    }
-    return acc0 + acc1;
-  }
-
-  // O^T[D x 32 queries] += V^T P^T.  V^T fragments run kDepth MFMAs ahead; the first
-  // kDepth are read by pv_prefetch before the softmax so its VALU work hides them.
-  struct VPre { u32x4 x[kDepth]; };
-  __device__ static u32x4 v_frag(const elem_t *buf, int step, int r, int h) {
-    const int kstep = step / (D / 32), dt = step % (D / 32);
-    return *(const u32x4 *)(buf + K_ELEMS + (32 * dt + r) * VSTR + 16 * kstep + 8 * h);
-  }
-  __device__ static void pv_prefetch(VPre &vp, const elem_t *buf, int lane) {
-    const int r = lane & 31, h = lane >> 5;
-#pragma unroll
-    for (int i = 0; i < kDepth; ++i) vp.x[i] = v_frag(buf, i, r, h);
-  }
-  __device__ static void pv(f32x16 (&o)[D / 32], const PFrag &pf, VPre &vp, const elem_t *buf,
-                            int lane) {
-    const int r = lane & 31, h = lane >> 5;
-    constexpr int NSTEP = 4 * (D / 32);
-#pragma unroll
-    for (int step = 0; step < NSTEP; ++step) {
-      const int kstep = step / (D / 32), dt = step % (D / 32);
-      o[dt] = mfma_bf16(as_bf16x8(vp.x[step % kDepth]), as_bf16x8(pf.x[kstep]), o[dt]);
-      if (step + kDepth < NSTEP) vp.x[step % kDepth] = v_frag(buf, step + kDepth, r, h);
-    }
-  }
-};
 
 // ---------------------------------------------------------------------------------
 // bf16 direct path: K and V go straight from global memory into LDS
@@ -391,16 +164,8 @@ struct Bf16DirectPath {
         koff = (int)(r * a.k_ss * 2) + 16 * L.k_chunk;
         voff = (int)(r * a.v_ss * 2) + 16 * L.v_chunk;
       }
-#if RA_FWD_DMA_ASM
       dma_b128(kt, koff, slot + blk * 1024);
       dma_b128(vt, voff, slot + TILE_BYTES + blk * 1024);
-#else
-      __builtin_amdgcn_global_load_lds((const void *)((const char *)kt + koff),
-                                       (lds_u8 *)(size_t)(slot + blk * 1024), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds((const void *)((const char *)vt + voff),
-                                       (lds_u8 *)(size_t)(slot + TILE_BYTES + blk * 1024), 16, 0,
-                                       0);
-#endif
     }
   }
 
@@ -488,12 +253,6 @@ struct F32Path {
   struct QFrag { f32x2 x[D / 4]; };
   struct Stage { u32x4 k[CH]; u32x4 v[CH]; };
   struct PFrag { f32x16 x[2]; };
-  static constexpr bool kPipelined = false;  // three fp32 tiles would not fit in LDS
-  __device__ static float fused_step(f32x16 (&)[2], const QFrag &, const elem_t *,
-                                     const f32x16 (&)[2], float, float, f32x16 (&)[D / 32],
-                                     const elem_t *, int) {
-    return 0.f;  // never called: the fp32 path uses the double-buffered loop
-  }
 
   // MFMA step 2j+e of half h uses head dim 4j + 2h + e (A and B agree).
   __device__ static void load_q(QFrag &qf, const FwdArgs &a, const elem_t *qbase, int qrow, int h) {
@@ -599,7 +358,7 @@ __global__ void __launch_bounds__(Path::kThreads) __attribute__((amdgpu_waves_pe
 attn_fwd_kernel(FwdArgs a) {
   using elem_t = typename Path::elem_t;
   constexpr int BM = 32 * Path::kWaves;  // query rows per workgroup
-  constexpr int NBUF = Path::kPipelined ? 3 : 2;
+  constexpr int NBUF = 2;
   __shared__ __attribute__((aligned(16))) unsigned char smem[NBUF * Path::BUF_BYTES];
 
   const int tid = threadIdx.x;
@@ -693,101 +452,37 @@ attn_fwd_kernel(FwdArgs a) {
   ring_next(a, CAUSAL, vis_lim, t, kb, kend, cend);
   typename Path::Stage st;
 
-  if constexpr (!Path::kPipelined) {
-    // ---- double-buffered loop: load next tile | QK, softmax, PV of this tile | store.
-    if (t < a.num_chunks) {
-      Path::load_tile(st, a, kbase, vbase, kb, tid);
-      Path::store_tile(st, tile_buf(0), tid);
-    }
-    // All prologue loads (Q included) have landed: without this the compiler keeps Q's
-    // loads "pending" on the no-tile path and the loop's first MFMAs would wait on the
-    // freshly issued prefetch as well (vmcnt counts in order).
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-    __syncthreads();
-    int cur = 0;
-    while (t < a.num_chunks) {
-      const int kb_cur = kb, cend_cur = cend;
-      ring_next(a, CAUSAL, vis_lim, t, kb, kend, cend);
-      const bool has_next = t < a.num_chunks;
-      if (has_next) Path::load_tile(st, a, kbase, vbase, kb, tid);
-      const elem_t *buf = tile_buf(cur);
-      if (!skips(kb_cur)) {
-        f32x16 s[2];
-        Path::qk(s, qf, buf, lane);
-        typename Path::VPre vp;
-        Path::pv_prefetch(vp, buf, lane);
-        mask_max_rescale(s, kb_cur, cend_cur);
-        const float mneg = m_run == -INFINITY ? 0.f : -m_run;
-        typename Path::PFrag pf;
-        l_run += Path::exp_pack(s, c, mneg, pf);
-        Path::pv(o, pf, vp, buf, lane);
-      }
-      if (has_next) Path::store_tile(st, tile_buf(cur ^ 1), tid);
-      __syncthreads();
-      cur ^= 1;
-    }
-  } else {
-    // ---- software-pipelined loop over a ring of three LDS tiles.  Iteration i holds
-    // tile i (scores already masked, max applied) and tile i+1 (resident in LDS):
-    //   issue global loads of tile i+2
-    //   QK(i+1) MFMAs  interleaved with  softmax(i) VALU;  then PV(i) MFMAs
-    //   store tile i+2 to LDS; barrier; mask + max + lazy rescale of tile i+1
-    const bool v0 = t < a.num_chunks;
-    const int kb0 = kb, ce0 = cend;
-    if (v0) {
-      Path::load_tile(st, a, kbase, vbase, kb0, tid);
-      Path::store_tile(st, tile_buf(0), tid);
-    }
+  // ---- double-buffered loop: load next tile | QK, softmax, PV of this tile | store.
+  if (t < a.num_chunks) {
+    Path::load_tile(st, a, kbase, vbase, kb, tid);
+    Path::store_tile(st, tile_buf(0), tid);
+  }
+  // All prologue loads (Q included) have landed: without this the compiler keeps Q's
+  // loads "pending" on the no-tile path and the loop's first MFMAs would wait on the
+  // freshly issued prefetch as well (vmcnt counts in order).
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+  __syncthreads();
+  int cur = 0;
+  while (t < a.num_chunks) {
+    const int kb_cur = kb, cend_cur = cend;
     ring_next(a, CAUSAL, vis_lim, t, kb, kend, cend);
-    bool vn = t < a.num_chunks;
-    int kbn = kb, cen = cend;
-    if (vn) {
-      Path::load_tile(st, a, kbase, vbase, kbn, tid);
-      Path::store_tile(st, tile_buf(1), tid);
+    const bool has_next = t < a.num_chunks;
+    if (has_next) Path::load_tile(st, a, kbase, vbase, kb, tid);
+    const elem_t *buf = tile_buf(cur);
+    if (!skips(kb_cur)) {
+      f32x16 s[2];
+      Path::qk(s, qf, buf, lane);
+      typename Path::VPre vp;
+      Path::pv_prefetch(vp, buf, lane);
+      mask_max_rescale(s, kb_cur, cend_cur);
+      const float mneg = m_run == -INFINITY ? 0.f : -m_run;
+      typename Path::PFrag pf;
+      l_run += Path::exp_pack(s, c, mneg, pf);
+      Path::pv(o, pf, vp, buf, lane);
     }
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): Q and both tiles have landed
+    if (has_next) Path::store_tile(st, tile_buf(cur ^ 1), tid);
     __syncthreads();
-
-    f32x16 sn[2];  // scores of the next tile to be exponentiated
-    if (v0 && !skips(kb0)) {
-      Path::qk(sn, qf, tile_buf(0), lane);
-      mask_max_rescale(sn, kb0, ce0);
-    }
-    float mneg = m_run == -INFINITY ? 0.f : -m_run;
-    bool vc = v0;
-    int kbc = kb0;
-    int bi = 0;  // LDS slot of the current tile
-    while (vc) {
-      ring_next(a, CAUSAL, vis_lim, t, kb, kend, cend);
-      const bool v2 = t < a.num_chunks;
-      if (v2) Path::load_tile(st, a, kbase, vbase, kb, tid);
-      const int bn_i = bi == 2 ? 0 : bi + 1;
-      const int b2_i = bn_i == 2 ? 0 : bn_i + 1;
-      const elem_t *bc = tile_buf(bi);
-      const elem_t *bnx = tile_buf(bn_i);
-      const bool skip_c = skips(kbc);
-      const bool skip_n = !vn || skips(kbn);
-      f32x16 sc[2] = {sn[0], sn[1]};
-      if (!skip_c) {
-        // One straight-line block (QK of the next slot runs even when that tile is
-        // skipped or absent: the slot holds in-bounds data and the scores are unused).
-        l_run += Path::fused_step(sn, qf, bnx, sc, c, mneg, o, bc, lane);
-      } else if (!skip_n) {
-        Path::qk(sn, qf, bnx, lane);
-      }
-      if (v2) Path::store_tile(st, tile_buf(b2_i), tid);
-      __syncthreads();
-      if (!skip_n) {
-        mask_max_rescale(sn, kbn, cen);
-        mneg = m_run == -INFINITY ? 0.f : -m_run;
-      }
-      vc = vn;
-      kbc = kbn;
-      vn = v2;
-      kbn = kb;
-      cen = cend;
-      bi = bn_i;
-    }
+    cur ^= 1;
   }
 
   // Epilogue: o = O / l, lse = ln(sum) = (m + log2 l) * ln 2.
@@ -889,10 +584,8 @@ attn_fwd_direct_kernel(FwdArgs a) {
   // than the other: the two waves then alternate MFMA and softmax phases instead of
   // running them together (4.5 % on the 32K causal GQA workload).  Odd waves as loaders
   // (both on the same two SIMDs) measured no gain.
-  using LoadPath = Bf16DirectPath<D, (RA_FWD_LOADER_MAP ? NW / 2 : NW), KN>;
-  const int lw = RA_FWD_LOADER_MAP == 0 ? wave_u
-                 : RA_FWD_LOADER_MAP == 1 ? wave_u - NW / 2
-                                          : ((wave_u & 1) ? (wave_u >> 1) : -1);
+  using LoadPath = Bf16DirectPath<D, NW / 2, KN>;
+  const int lw = wave_u - NW / 2;
   typename LoadPath::Lane LL;
   if (lw >= 0) LoadPath::setup(LL, a, 64 * lw + lane, lds_offset(smem));
   auto load_tile = [&](int kbx, uint32_t slot) {
@@ -941,10 +634,7 @@ attn_fwd_direct_kernel(FwdArgs a) {
     const int kb_cur = kb, cend_cur = cend;
     ring_next<KN>(a, CAUSAL, vis_lim, t, kb, kend, cend);
     const bool has_next = t < a.num_chunks;
-#if !RA_FWD_DMA_LATE
-    if (has_next)
-      load_tile(kb, smem0 + (cur ^ 1) * Path::BUF_BYTES);
-#endif
+    if (has_next) load_tile(kb, smem0 + (cur ^ 1) * Path::BUF_BYTES);
 
     const int64_t kpos0 = a.kv_offset + kb_cur;
     const bool doc_skip =
@@ -999,10 +689,6 @@ attn_fwd_direct_kernel(FwdArgs a) {
       l_run += Path::exp_pack(s, c, mneg, pf);
       Path::pv(o, pf, L, cur);
     }
-#if RA_FWD_DMA_LATE
-    if (has_next)
-      load_tile(kb, smem0 + (cur ^ 1) * Path::BUF_BYTES);
-#endif
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the next tile's direct loads landed
     __syncthreads();
     return has_next;
@@ -1042,14 +728,14 @@ attn_fwd_direct_kernel(FwdArgs a) {
 template <int D, bool CAUSAL, bool VARLEN = false>
 int launch_direct(const FwdArgs &args, hipStream_t stream) {
   FwdArgs a = args;
-  constexpr int NW = RA_FWD_DIRECT_WAVES;
+  constexpr int NW = kDirectWaves;
   a.num_q_tiles = (a.Sq + 32 * NW - 1) / (32 * NW);
   const int64_t blocks = (int64_t)a.num_q_tiles * a.Hq * a.B;
   if (blocks <= 0) return RA_OK;
   // the work counter serves the shapes the fixed XCD head map cannot (B*Hq % 8 != 0):
   // with it the 32-head layers measured 1.8 % slower (their K/V leave the XCD's L2)
   if ((a.Hq * a.B) % 8 == 0) a.sched = nullptr;
-  constexpr int KN = RA_FWD_KN;
+  constexpr int KN = kDirectKN;
   hipLaunchKernelGGL((attn_fwd_direct_kernel<D, CAUSAL, NW, KN, VARLEN>), dim3((unsigned)blocks),
                      dim3(64 * NW), 0, stream, a);
   return hipGetLastError() == hipSuccess ? RA_OK : RA_ERR_HIP;
@@ -1069,15 +755,9 @@ int launch_one(const FwdArgs &args, hipStream_t stream) {
 }  // namespace
 
 int launch_attn_fwd(const FwdArgs &a, int dtype, int D, int causal, hipStream_t stream) {
-  if (dtype == RA_BF16 && RA_FWD_DIRECT) {
+  if (dtype == RA_BF16) {
     if (D == 128) return causal ? launch_direct<128, true>(a, stream) : launch_direct<128, false>(a, stream);
     if (D == 64) return causal ? launch_direct<64, true>(a, stream) : launch_direct<64, false>(a, stream);
-  }
-  if (dtype == RA_BF16) {
-    if (D == 128) return causal ? launch_one<Bf16Path<128, kBf16Waves>, 128, true>(a, stream)
-                                : launch_one<Bf16Path<128, kBf16Waves>, 128, false>(a, stream);
-    if (D == 64) return causal ? launch_one<Bf16Path<64, kBf16Waves>, 64, true>(a, stream)
-                               : launch_one<Bf16Path<64, kBf16Waves>, 64, false>(a, stream);
   } else if (dtype == RA_F32) {
     if (D == 128) return causal ? launch_one<F32Path<128>, 128, true>(a, stream)
                                 : launch_one<F32Path<128>, 128, false>(a, stream);

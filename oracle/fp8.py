@@ -36,7 +36,8 @@ least 2^6.  Hence, element-wise,
     |o - o_exact| <= 2^-4 * sum_j p_j |v_j|  +  2^-16 * n_sub * max_j |v_j|
 
 with p the exact softmax weights and n_sub the number of visible keys with
-exp(s - m) < 2^-12.  ``p_rounding_bound`` computes the right-hand side.
+exp(s - m) < 2^-12.  ``p_rounding_bound`` computes the right-hand side for listed rows,
+``p_rounding_bound_head`` for every row of one head.
 """
 from __future__ import annotations
 
@@ -173,6 +174,42 @@ def p_rounding_bound(q, k, v, rows: Iterable[Tuple[int, int, int]], *, causal: b
     return np.stack(out)
 
 
+def p_rounding_bound_head(q, k, v, b: int, h: int, *, causal: bool = False,
+                          scale: Optional[float] = None, q_offset: int = 0, kv_offset: int = 0,
+                          row_block: int = 256) -> np.ndarray:
+    """``p_rounding_bound`` for every row of head (b, h) at once -> [Sq, D].
+
+    The same right-hand side, row block by row block: the visible keys of a row are a
+    prefix of the key axis (all keys without the mask, those at or before the row's
+    position with it), so max_j |v_j| over them is a running maximum along the keys.
+    """
+    q, k, v = _as64(q), _as64(k), _as64(v)
+    Hq, Hkv, Sq, D = q.shape[1], k.shape[1], q.shape[2], q.shape[3]
+    Skv = k.shape[2]
+    scale = _default_scale(scale, D)
+    g = h // (Hq // Hkv)
+    kpos = kv_offset + np.arange(Skv)
+    va = np.abs(v[b, g])
+    va_prefix_max = np.maximum.accumulate(va, axis=0) if Skv else va
+    out = np.zeros((Sq, D))
+    for r0 in range(0, Sq, row_block):
+        r1 = min(Sq, r0 + row_block)
+        qpos = q_offset + np.arange(r0, r1)
+        s = _masked_scores(q[b, h, r0:r1], k[b, g], scale, qpos, kpos, causal)
+        vis = np.isfinite(s)
+        n_vis = vis.sum(axis=1)
+        m = np.where(n_vis > 0, s.max(axis=1, initial=-np.inf), 0.0)
+        pt = np.where(vis, np.exp(s - m[:, None]), 0.0)
+        tot = pt.sum(axis=1)
+        p = pt / np.where(tot > 0, tot, 1.0)[:, None]
+        n_sub = np.count_nonzero(vis & (pt < 2.0 ** -12), axis=1)
+        last = np.clip(n_vis - 1, 0, max(Skv - 1, 0))
+        vmax = va_prefix_max[last] if Skv else np.zeros((r1 - r0, D))
+        blk = 2.0 ** -4 * (p @ va) + 2.0 ** -16 * n_sub[:, None] * vmax
+        out[r0:r1] = np.where((n_vis > 0)[:, None], blk, 0.0)
+    return out
+
+
 def simulate_p_rounding(q, k, v, *, causal: bool = False, scale: Optional[float] = None,
                         delta: float = 0.0):
     """o with P' = 2^(6 + delta) exp(s - m) rounded to e4m3 in the numerator only
@@ -200,4 +237,5 @@ def simulate_p_rounding(q, k, v, *, causal: bool = False, scale: Optional[float]
 
 
 __all__ = ["E4M3_MAX", "e4m3_decode", "e4m3_encode", "quantize_heads", "transpose_codes",
-           "dequantize", "fp8_attention", "p_rounding_bound", "simulate_p_rounding"]
+           "dequantize", "fp8_attention", "p_rounding_bound", "p_rounding_bound_head",
+           "simulate_p_rounding"]

@@ -81,8 +81,9 @@ def gather_lse(t: np.ndarray, idx):
 
 
 # Gradient tolerance (derived in test_gpu_bwd.py's header): element-wise
-# 2e-2 + 2^-8 |ref|, mean abs 2e-3, L2 within 1e-2 |ref| + 2e-3 sqrt(n) (the relative
-# L2 bound with the mean bound's floor, for gradients that vanish exactly).
+# 2e-2 + 2^-8 |ref|, mean abs 2e-3, L2 within max(1e-2 |ref|, 2e-3 sqrt(n)): the relative
+# L2 bound, with the mean bound's floor only where the reference itself is below it
+# (gradients that vanish exactly, such as dK of a row that sees a single key).
 GRAD_TOL = dict(o_max=2e-2, o_mean=2e-3)
 
 
@@ -96,5 +97,5 @@ def check_grad(got, ref, what):
     excess = float((err - (GRAD_TOL["o_max"] + 2.0 ** -8 * np.abs(ref))).max(initial=-1.0))
     assert excess <= 0.0, f"{what}: element error over 2e-2 + 2^-8|ref| by {excess}"
     assert mean <= GRAD_TOL["o_mean"], f"{what}: mean abs err {mean}"
-    l2_bound = 1e-2 * float(np.linalg.norm(ref)) + GRAD_TOL["o_mean"] * np.sqrt(err.size)
+    l2_bound = max(1e-2 * float(np.linalg.norm(ref)), GRAD_TOL["o_mean"] * np.sqrt(err.size))
     assert float(np.linalg.norm(got - ref)) <= l2_bound, f"{what}: relative L2 {rel}"

@@ -7,7 +7,7 @@ Tolerance for bf16 gradients (none is stated for gradients, so it is derived fro
 arithmetic): each output is rounded to bf16 once (<= 2^-9 |g|) and P and dS are rounded
 to bf16 before their matrix products (aggregate <= 2^-9 |g| more), so element-wise
 |err| <= 2e-2 + 2^-8 |ref|; besides, mean abs err <= 2e-3 and L2 error <= 1e-2 of the
-reference's L2 norm, plus the mean bound's floor (2e-3 RMS) for a gradient that vanishes
+reference's L2 norm, or the mean bound's floor (2e-3 RMS) where that is larger: for a gradient that vanishes
 exactly: a row that sees a single key has P = 1 and dP = D, so its dS is 0.  With
 grouped heads dK and dV sum over the group and reach |g| of several units, where the
 output rounding alone exceeds a flat 2e-2.

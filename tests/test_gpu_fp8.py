@@ -173,17 +173,17 @@ def test_fp8_deterministic():
     assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
 
 
-def test_qwen7b_gqa_32k_fp8_workload_sampled_rows():
+@pytest.fixture(scope="module")
+def qwen32k_fp8():
     """The headline attention shape (q [1, 7, 32768, 128], k, v [1, 1, 32768, 128],
-    causal) in fp8: sampled rows of every head against the oracle, and the quantizer's
-    codes for the same tensors bit-exact."""
+    causal) in fp8, run once: the quantizer's codes for the bf16 tensors (bit-exact), then
+    the attention on the oracle's codes."""
     w = si.WORKLOADS["qwen7b_gqa_32k_fp8"]
     say(f"workload {w.name}")
     q, k, v = si.draw_qkv(w.seed, w.q_shape, w.kv_shape, "bf16")
     qx, kx, vx = (si.bf16_bits_to_f32(t) for t in (q, k, v))
     (qc, qd), (kc, kd), (vc, vd) = (ofp8.quantize_heads(t) for t in (qx, kx, vx))
     vtc = ofp8.transpose_codes(vc)
-    # the GPU quantizer on the same bf16 tensors
     gq, gqd = ra.fp8_quantize(_bf16_dev(q))
     gk, gkd = ra.fp8_quantize(_bf16_dev(k))
     gv, gvd = ra.fp8_quantize(_bf16_dev(v), transpose=True)
@@ -192,19 +192,32 @@ def test_qwen7b_gqa_32k_fp8_workload_sampled_rows():
         assert np.array_equal(_codes_np(got), ref), f"{name} codes differ"
     for got, ref in ((gqd, qd), (gkd, kd), (gvd, vd)):
         assert np.array_equal(got.cpu().numpy(), ref)
-    # attention on the oracle's codes
+    del gq, gk, gv
     o, lse = ra.attn_fwd_fp8(_codes_dev(qc), _codes_dev(kc), _codes_dev(vtc),
                              *(torch.from_numpy(d).cuda() for d in (qd, kd, vd)), causal=True)
     torch.cuda.synchronize()
+    deq = (ofp8.dequantize(qc, qd), ofp8.dequantize(kc, kd), ofp8.dequantize(vc, vd))
+    return w, to_np64(o), lse.cpu().numpy().astype(np.float64), deq
+
+
+def test_qwen7b_gqa_32k_fp8_workload_sampled_rows(qwen32k_fp8):
+    w, o_n, l_n, (q64, k64, v64) = qwen32k_fp8
     B, Hq, Sq, D = w.q_shape
     idx = sample_rows(B, Hq, Sq, per_head=4, seed=w.seed)
-    q64, k64, v64 = ofp8.dequantize(qc, qd), ofp8.dequantize(kc, kd), ofp8.dequantize(vc, vd)
     o_ref, l_ref = oracle.attention_rows(q64, k64, v64, idx, causal=True)
     bound = ofp8.p_rounding_bound(q64, k64, v64, idx, causal=True)
-    o_n, l_n = to_np64(o), lse.cpu().numpy().astype(np.float64)
     got_o = np.stack([o_n[b, h, i] for (b, h, i) in idx])
     got_l = np.array([l_n[b, h, i] for (b, h, i) in idx])
     _check(got_o, got_l, o_ref, l_ref, bound, "o sampled")
+
+
+@pytest.mark.parametrize("h", [0, 3, 6])
+def test_qwen7b_gqa_32k_fp8_workload_whole_head(qwen32k_fp8, h):
+    """Every row of query head h within the derived bound."""
+    w, o_n, l_n, (q64, k64, v64) = qwen32k_fp8
+    o_ref, l_ref = oracle.full_attention(q64[:, h:h + 1], k64, v64, causal=True)
+    bound = ofp8.p_rounding_bound_head(q64, k64, v64, 0, h, causal=True)
+    _check(o_n[0, h], l_n[0, h], o_ref[0, 0], l_ref[0, 0], bound, f"o head {h} (all rows)")
 
 
 @pytest.mark.parametrize("causal", [True, False])

@@ -1,7 +1,8 @@
 """GPU parity of ra_attn_fwd (and the chunk-by-chunk ring share) against the CPU oracle.
 
-Small cases compare every element; the full-size workloads compare sampled rows that
-the oracle computes one by one.  Inputs come from ``seeded_inputs`` (N(0,1), bf16
+Small cases compare every element; the full-size workloads compare every row of whole
+heads (all 7 query heads of the 32K GQA headline, three heads of each 32-head workload)
+plus sampled rows of every head.  Inputs come from ``seeded_inputs`` (N(0,1), bf16
 rounded by RNE for bf16 cases); the oracle reads the rounded values exactly.
 """
 import numpy as np
@@ -135,49 +136,98 @@ def test_ring_tiny_f32_workload():
     check_lse(to_np64(lse), l_full, "f32", "lse vs full attention")
 
 
-def _sampled_check(w, o, lse, q64, k64, v64, what, per_head=6):
+def _sampled_check(w, o_np, l_np, q64, k64, v64, what, per_head=6):
     B, H, S, _ = w.q_shape
     idx = sample_rows(B, H, S, per_head=per_head, seed=w.seed)
     o_ref, l_ref = oracle.attention_rows(q64, k64, v64, idx, causal=w.causal,
                                          q_offset=w.q_offset, kv_offset=w.kv_offset)
-    o_np = o.float().cpu().numpy()
-    l_np = lse.cpu().numpy()
     check_o(gather_rows(o_np, idx).astype(np.float64), o_ref, w.dtype, f"{what} o (sampled)")
     check_lse(gather_lse(l_np, idx).astype(np.float64), l_ref, w.dtype, f"{what} lse (sampled)")
     assert np.isfinite(o_np).all() and np.isfinite(l_np).all()
 
 
-def test_llama_causal_8k_workload():
+def _whole_head_check(w, o_np, l_np, q64, k64, v64, h, what):
+    """Every row of query head h against the oracle (its key/value head by the grouping)."""
+    group = w.q_shape[1] // w.kv_shape[1]
+    g = h // group
+    o_ref, l_ref = oracle.full_attention(q64[:, h:h + 1], k64[:, g:g + 1], v64[:, g:g + 1],
+                                         causal=w.causal, q_offset=w.q_offset,
+                                         kv_offset=w.kv_offset)
+    check_o(o_np[:, h:h + 1].astype(np.float64), o_ref, w.dtype, f"{what} o head {h} (all rows)")
+    check_lse(l_np[:, h:h + 1].astype(np.float64), l_ref, w.dtype,
+              f"{what} lse head {h} (all rows)")
+
+
+# Full-size workloads.  Each runs once on the GPU, in the launch configuration bench.py
+# times (module-scoped fixtures); every row of whole heads is then compared with the
+# oracle, one head per test so that each test stays short, and sampled rows (tile
+# edges, both ends, random rows) of every head.
+
+@pytest.fixture(scope="module")
+def llama8k():
     w = si.WORKLOADS["llama7b_causal_8k"]
     say(f"workload {w.name}")
     q, k, v = si.draw_qkv(w.seed, w.q_shape, w.kv_shape, w.dtype)
     qd, kd, vd = to_dev(q, "bf16"), to_dev(k, "bf16"), to_dev(v, "bf16")
-    o, lse = ra.attn_fwd(qd, kd, vd, causal=True)
+    o = torch.full(qd.shape, float("nan"), dtype=torch.bfloat16, device="cuda")
+    lse = torch.full(qd.shape[:3], float("nan"), dtype=torch.float32, device="cuda")
+    ra.attn_fwd(qd, kd, vd, causal=True, out=o, lse=lse)
     torch.cuda.synchronize()
-    _sampled_check(w, o, lse, *(si.as_f64(x, "bf16") for x in (q, k, v)), w.name)
+    res = (w, o.float().cpu().numpy(), lse.cpu().numpy(),
+           *(si.as_f64(x, "bf16") for x in (q, k, v)))
+    del qd, kd, vd, o, lse
+    return res
 
 
-def test_ring8_rank3_32k_workload_fused_and_chunked():
+def test_llama_causal_8k_workload_sampled(llama8k):
+    w, o_np, l_np, q64, k64, v64 = llama8k
+    _sampled_check(w, o_np, l_np, q64, k64, v64, w.name)
+
+
+@pytest.mark.parametrize("h", [0, 13, 31])
+def test_llama_causal_8k_workload_whole_head(llama8k, h):
+    w, o_np, l_np, q64, k64, v64 = llama8k
+    _whole_head_check(w, o_np, l_np, q64, k64, v64, h, w.name)
+
+
+@pytest.fixture(scope="module")
+def ring32k():
     w = si.WORKLOADS["ring8_rank3_32k"]
-    say(f"workload {w.name} fused")
     q, k, v = si.draw_qkv(w.seed, w.q_shape, w.kv_shape, w.dtype)
     qd, kd, vd = to_dev(q, "bf16"), to_dev(k, "bf16"), to_dev(v, "bf16")
+    say(f"workload {w.name} fused")
     o, lse = ra.attn_fwd(qd, kd, vd, causal=True, num_chunks=w.num_chunks,
                          start_chunk=w.start_chunk, q_offset=w.q_offset)
     torch.cuda.synchronize()
-    q64, k64, v64 = (si.as_f64(x, "bf16") for x in (q, k, v))
-    _sampled_check(w, o, lse, q64, k64, v64, "fused")
     say(f"workload {w.name} chunk-by-chunk + merge")
     assert ra.ring_visible_chunks(4096, 32768, num_chunks=8, start_chunk=3, causal=True,
                                   q_offset=w.q_offset) == [3, 0, 1, 2]
     o2, lse2 = ra.ring_attn_chunked(qd, kd, vd, causal=True, num_chunks=w.num_chunks,
                                     start_chunk=w.start_chunk, q_offset=w.q_offset)
     torch.cuda.synchronize()
-    _sampled_check(w, o2, lse2, q64, k64, v64, "chunked")
+    res = {"fused": (o.float().cpu().numpy(), lse.cpu().numpy()),
+           "chunked": (o2.float().cpu().numpy(), lse2.cpu().numpy())}
+    del qd, kd, vd, o, lse, o2, lse2
+    return w, res, tuple(si.as_f64(x, "bf16") for x in (q, k, v))
 
 
-def test_qwen_ulysses_32k_workload():
-    """Permute the sequence-sharded sources of rank 0, then causal GQA attention at 32K."""
+@pytest.mark.parametrize("form", ["fused", "chunked"])
+def test_ring8_rank3_32k_workload_sampled(ring32k, form):
+    w, res, (q64, k64, v64) = ring32k
+    _sampled_check(w, *res[form], q64, k64, v64, form)
+
+
+@pytest.mark.parametrize("form", ["fused", "chunked"])
+@pytest.mark.parametrize("h", [0, 18, 31])
+def test_ring8_rank3_32k_workload_whole_head(ring32k, form, h):
+    w, res, (q64, k64, v64) = ring32k
+    _whole_head_check(w, *res[form], q64, k64, v64, h, form)
+
+
+@pytest.fixture(scope="module")
+def qwen32k():
+    """Permute the sequence-sharded sources of rank 0 (bit-exact), then causal GQA
+    attention over the whole 32K head shard."""
     w = si.WORKLOADS["qwen7b_ulysses4_rank0_32k"]
     say(f"workload {w.name}")
     qs, ks, vs = si.draw_ulysses_sources(w.seed)
@@ -191,10 +241,27 @@ def test_qwen_ulysses_32k_workload():
         heads.append((d.unsqueeze(0), ref[None]))
     (qd, q_ref), (kd, k_ref), (vd, v_ref) = heads
     assert tuple(qd.shape) == w.q_shape and tuple(kd.shape) == w.kv_shape
-    o, lse = ra.attn_fwd(qd, kd, vd, causal=True)
+    o = torch.full(qd.shape, float("nan"), dtype=torch.bfloat16, device="cuda")
+    lse = torch.full(qd.shape[:3], float("nan"), dtype=torch.float32, device="cuda")
+    ra.attn_fwd(qd, kd, vd, causal=True, out=o, lse=lse)
     torch.cuda.synchronize()
-    _sampled_check(w, o, lse, *(si.as_f64(x, "bf16") for x in (q_ref, k_ref, v_ref)), w.name,
-                   per_head=12)
+    res = (w, o.float().cpu().numpy(), lse.cpu().numpy(),
+           *(si.as_f64(x, "bf16") for x in (q_ref, k_ref, v_ref)))
+    del qd, kd, vd, o, lse, heads
+    return res
+
+
+def test_qwen_ulysses_32k_workload_sampled(qwen32k):
+    w, o_np, l_np, q64, k64, v64 = qwen32k
+    _sampled_check(w, o_np, l_np, q64, k64, v64, w.name, per_head=12)
+
+
+@pytest.mark.parametrize("h", range(7))
+def test_qwen_ulysses_32k_workload_whole_head(qwen32k, h):
+    """All 7 query heads of the headline, every row (each one query tile set of the
+    work-counter launch)."""
+    w, o_np, l_np, q64, k64, v64 = qwen32k
+    _whole_head_check(w, o_np, l_np, q64, k64, v64, h, w.name)
 
 
 def _counter(q):

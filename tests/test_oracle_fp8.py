@@ -139,3 +139,26 @@ def test_bound_constant_is_tight():
     assert err > 2.0 ** -5 * A
     bound = fp8.p_rounding_bound(q, k, v, [(0, 0, 0)], scale=1.0)[0, 0]
     assert err <= bound
+
+
+@pytest.mark.parametrize("causal,q_off,kv_off", [(False, 0, 0), (True, 0, 0), (True, 30, 0),
+                                                 (True, 0, 20), (True, 5, 70)])
+def test_head_bound_matches_row_bound_and_holds(causal, q_off, kv_off):
+    """The whole-head form of the bound is the per-row bound for every row (including
+    rows with no visible key), with several row blocks and a ragged last block, and the
+    simulated e4m3 rounding of P' stays within it."""
+    rng = np.random.default_rng(7 + q_off + kv_off)
+    q = rng.standard_normal((1, 4, 70, 8)) * 4.0
+    k = rng.standard_normal((1, 2, 64, 8))
+    v = rng.standard_normal((1, 2, 64, 8))
+    kw = dict(causal=causal, q_offset=q_off, kv_offset=kv_off)
+    for h in range(4):
+        head = fp8.p_rounding_bound_head(q, k, v, 0, h, row_block=32, **kw)
+        rows = fp8.p_rounding_bound(q, k, v, [(0, h, i) for i in range(70)], **kw)
+        np.testing.assert_allclose(head, rows, rtol=1e-12, atol=1e-300)
+    if q_off == 0 and kv_off == 0:
+        o_ref, _ = oracle.full_attention(q, k, v, causal=causal)
+        o_sim = fp8.simulate_p_rounding(q, k, v, causal=causal, delta=1.0)
+        for h in range(4):
+            bound = fp8.p_rounding_bound_head(q, k, v, 0, h, causal=causal)
+            assert (np.abs(o_sim[0, h] - o_ref[0, h]) <= bound * (1 + 1e-9) + 1e-15).all()
