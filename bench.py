@@ -4,15 +4,19 @@ One step = one pass of the whole forward hot path over one batch of synthetic in
 For the headline workload (a Qwen2.5-7B-shaped GQA layer, 28 query / 4 key-value heads
 x 128, one rank's share of a 4-way Ulysses split at 32K tokens):
 
-    ulysses_permute(q), (k), (v)   sequence shards -> rank 0's head shard
+    ulysses_permute(q, k, v)       sequence shards -> rank 0's head shard (one launch)
     attn_fwd                       causal, GQA 7:1, S = 32768, bf16 in, fp32 accumulate
     ulysses_permute(o)             head shard -> sequence shards
 
 Prints ONE JSON line.  ``value`` is the algorithmic attention TFLOP/s of the whole step
 (inputs resident in HBM; flops use the causal S^2/2 convention, 2 flops per MAC);
 ``roofline`` reports the attention kernel alone, timed with HIP events on the stream it
-runs on; ``cpu_baseline`` times the fp64 CPU oracle on a bounded sample of the same
-workload.  Other workloads can be selected with --workload.
+runs on; ``cpu_baseline`` times the fp64 CPU oracle on whole heads of the same workload's
+own seeded inputs, for a bounded time.  The default run also times the other workloads
+of the same hot path (the 8K Llama-7B-shaped causal layer, one rank's share of an 8-way
+ring at 32K -- fused and chunk by chunk with the merge -- and the 16K causal backward)
+and reports each as extra keys.  ``--workload`` selects another workload as the
+headline of the line instead.
 """
 from __future__ import annotations
 
@@ -30,6 +34,7 @@ PEAK_BF16_TFLOPS = 2516.6     # 256 CU x 2.4 GHz x 4096 flop/clk/CU (dense bf16 
 PEAK_F32_TFLOPS = 157.3
 PEAK_FP8_TFLOPS = 5033.2      # 256 CU x 2.4 GHz x 8192 flop/clk/CU (dense fp8 MFMA)
 PEAK_HBM_GBPS = 8000.0
+HEADLINE = "qwen7b_ulysses4_rank0_32k"
 
 
 def visible_pairs(Sq, Skv, num_chunks, causal, q_offset, kv_offset):
@@ -94,119 +99,141 @@ def blas_threads() -> int:
     return len(os.sched_getaffinity(0))
 
 
-def cpu_baseline(w, budget_s: float = 15.0):
-    """Time the fp64 oracle on blocks of query rows spread over the sequence."""
+def blas_vendor() -> str:
+    try:
+        cfg = np.show_config(mode="dicts")["Build Dependencies"]["blas"]
+        return f"{cfg.get('name', '?')} {cfg.get('version', '')}".strip()
+    except Exception:
+        return "unknown"
+
+
+# ------------------------------------------------------------------ CPU oracle baseline
+
+def _workload_inputs_f64(w):
+    """The workload's own seeded inputs as the oracle reads them (fp64 of the bf16
+    values): q, k, v (and dO for a backward), plus cu_seqlens for packed documents."""
     import oracle
     import seeded_inputs as si
+    if w.ulysses_P:  # the head shard of rank r, moved by the oracle's own permute
+        srcs = si.draw_ulysses_sources(w.seed)
+        q, k, v = (oracle.seq_to_head(s, w.ulysses_P, w.ulysses_rank)[None] for s in srcs)
+        return [si.as_f64(x, "bf16") for x in (q, k, v)], None
+    xs = si.draw_qkv(w.seed, w.q_shape, w.kv_shape, w.dtype, with_dout=w.backward)
+    cu = si.draw_doc_offsets(w.seed, w.q_shape[2]) if w.packed_docs else None
+    return [si.as_f64(x, w.dtype) for x in xs], cu
 
+
+def cpu_baseline(w, budget_s: float = 20.0):
+    """Time the fp64 oracle on whole query heads (every row) of the workload's own seeded
+    inputs, head after head until the time budget is spent (at least one head).
+
+    ``value`` credits the algorithmic work of the heads done with the same convention as
+    the GPU line (causal S^2/2, 2 flops per MAC; 2.5x the forward for a backward);
+    ``value_full_matrix`` credits what the oracle actually computes (every masked score of
+    the full matrix)."""
+    import oracle
+    xs, cu = _workload_inputs_f64(w)
     B, Hq, Sq, D = w.q_shape
-    Skv = w.kv_shape[2]
-    rng = np.random.Generator(np.random.PCG64(w.seed + 7))
-    k = rng.standard_normal((1, 1, Skv, D), dtype=np.float32)
-    v = rng.standard_normal((1, 1, Skv, D), dtype=np.float32)
-    k64 = si.bf16_bits_to_f32(si.bf16_bits(k)).astype(np.float64)
-    v64 = si.bf16_bits_to_f32(si.bf16_bits(v)).astype(np.float64)
-    blk = 128
-    # Passes over the sequence (a fresh random order of its 128-row blocks each, one pass
-    # per query head at most) until the time budget is spent.
-    starts = []
-    for _ in range(B * Hq):
-        order = list(range(0, Sq, blk))
-        rng.shuffle(order)
-        starts += order
-    if w.fp8:  # the context's codes are set up once, like the inputs, before timing
+    Hkv, Skv = w.kv_shape[1], w.kv_shape[2]
+    group = Hq // Hkv
+    fp8_codes = None
+    if w.fp8:  # the inputs' codes are set up once, like the GPU side's inputs
         from oracle import fp8 as ofp8
-        kc, kdd = ofp8.quantize_heads(k64.astype(np.float32))
-        vc, vdd = ofp8.quantize_heads(v64.astype(np.float32))
-    done_flops, rows, t0 = 0.0, 0, time.perf_counter()
-    cu = si.draw_doc_offsets(w.seed, Sq) if w.packed_docs else None
-    for a in starts:
-        qb = si.bf16_bits_to_f32(si.bf16_bits(
-            rng.standard_normal((1, 1, blk, D), dtype=np.float32))).astype(np.float64)
-        if cu is not None:  # rows of one document against that document's keys
-            d = max(i for i in range(len(cu) - 1) if cu[i] <= a)
-            lo, hi = cu[d], cu[d + 1]
-            n = min(blk, hi - a)
-            kk, vv = k64[:, :, lo:hi], v64[:, :, lo:hi]
-            if w.backward:
-                nk = min(hi - lo, a - lo + n) if w.causal else hi - lo
-                oracle.attention_bwd(qb[:, :, :n], kk[:, :, :nk], vv[:, :, :nk], qb[:, :, :n],
-                                     causal=w.causal, q_offset=a - lo)
-                done_flops += 2.5 * attn_flops(1, 1, n, hi - lo, D, 1, w.causal, a - lo, 0)
+        fp8_codes = [ofp8.quantize_heads(x.astype(np.float32)) for x in xs[:3]]
+    fwd_mult = 2.5 if w.backward else 1.0
+    done, done_full, units, t0 = 0.0, 0.0, 0, time.perf_counter()
+    if w.backward:  # one key/value head (with its group of query heads) per unit
+        q64, k64, v64, do64 = xs
+        unit_list = list(range(Hkv))
+    else:
+        q64, k64, v64 = xs[:3]
+        unit_list = list(range(Hq))
+    for u in unit_list:
+        if w.backward:
+            if cu is not None:
+                hs = slice(u * group, (u + 1) * group)
+                oracle.varlen_attention_bwd(q64[:, hs], k64[:, u:u + 1], v64[:, u:u + 1],
+                                            do64[:, hs], cu, causal=w.causal)
+                pairs = sum(visible_pairs(b - a, b - a, 1, w.causal, 0, 0)
+                            for a, b in zip(cu, cu[1:]))
+                full = sum(float(b - a) ** 2 for a, b in zip(cu, cu[1:]))
             else:
-                oracle.full_attention(qb[:, :, :n], kk, vv, causal=w.causal, q_offset=a - lo)
-                done_flops += attn_flops(1, 1, n, hi - lo, D, 1, w.causal, a - lo, 0)
-        elif w.fp8:  # the fp8 oracle: quantize the block (per-head rule), then exact
-            # attention of the dequantized values over the context quantized up front
-            qc, qdd = ofp8.quantize_heads(qb.astype(np.float32))
-            ofp8.fp8_attention(qc, kc, vc, qdd, kdd, vdd, causal=w.causal,
-                               q_offset=w.q_offset + a, kv_offset=w.kv_offset)
-            done_flops += attn_flops(1, 1, blk, Skv, D, 1, w.causal, w.q_offset + a,
-                                     w.kv_offset)
-        elif w.backward:  # all five products for the block's (query, key) pairs
-            nk = min(Skv, w.q_offset + a + blk - w.kv_offset) if w.causal else Skv
-            oracle.attention_bwd(qb, k64[:, :, :nk], v64[:, :, :nk], qb, causal=w.causal,
-                                 q_offset=w.q_offset + a, kv_offset=w.kv_offset)
-            done_flops += 2.5 * attn_flops(1, 1, blk, Skv, D, 1, w.causal, w.q_offset + a,
-                                           w.kv_offset)
+                oracle.attention_bwd_heads(q64, k64, v64, do64, [(0, u)], causal=w.causal,
+                                           q_offset=w.q_offset, kv_offset=w.kv_offset)
+                pairs = visible_pairs(Sq, Skv, w.num_chunks, w.causal, w.q_offset,
+                                      w.kv_offset)
+                full = float(Sq) * Skv
+            done += fwd_mult * 4.0 * D * pairs * group
+            done_full += fwd_mult * 4.0 * D * full * group
         else:
-            oracle.full_attention(qb, k64, v64, causal=w.causal, q_offset=w.q_offset + a,
-                                  kv_offset=w.kv_offset)
-            done_flops += attn_flops(1, 1, blk, Skv, D, 1, w.causal, w.q_offset + a,
-                                     w.kv_offset)
-        rows += blk
+            g = u // group
+            if fp8_codes is not None:
+                from oracle import fp8 as ofp8
+                (qc, qd), (kc, kd), (vc, vd) = fp8_codes
+                ofp8.fp8_attention(qc[:, u:u + 1], kc[:, g:g + 1], vc[:, g:g + 1],
+                                   qd[:, u:u + 1], kd[:, g:g + 1], vd[:, g:g + 1],
+                                   causal=w.causal, q_offset=w.q_offset, kv_offset=w.kv_offset)
+            elif cu is not None:
+                oracle.varlen_attention(q64[:, u:u + 1], k64[:, g:g + 1], v64[:, g:g + 1], cu,
+                                        causal=w.causal)
+            else:
+                oracle.full_attention(q64[:, u:u + 1], k64[:, g:g + 1], v64[:, g:g + 1],
+                                      causal=w.causal, q_offset=w.q_offset,
+                                      kv_offset=w.kv_offset)
+            if cu is not None:
+                pairs = sum(visible_pairs(b - a, b - a, 1, w.causal, 0, 0)
+                            for a, b in zip(cu, cu[1:]))
+                full = sum(float(b - a) ** 2 for a, b in zip(cu, cu[1:]))
+            else:
+                pairs = visible_pairs(Sq, Skv, w.num_chunks, w.causal, w.q_offset, w.kv_offset)
+                full = float(Sq) * Skv
+            done += 4.0 * D * pairs
+            done_full += 4.0 * D * full
+        units += 1
         if time.perf_counter() - t0 > budget_s:
             break
     dt = time.perf_counter() - t0
+    what = ("key/value head(s) with their query-head group" if w.backward else "query head(s)")
+    kind = "backward" if w.backward else ("fp8 forward" if w.fp8 else "forward")
     return {
-        "value": done_flops / dt / 1e12, "unit": "TFLOP/s", "cores": blas_threads(),
+        "value": done / dt / 1e12, "unit": "TFLOP/s", "cores": blas_threads(),
         "kind": "oracle",
-        "sample": f"{rows} query rows ({rows // blk} blocks of {blk} at random positions, "
-                  f"{math.ceil(rows / Sq)} pass(es) over the sequence) of one head against its "
-                  f"{'causal ' if w.causal else ''}"
-                  f"{'own document' if cu is not None else str(Skv) + '-key context'}, "
-                  f"{'backward' if w.backward else ('fp8 forward' if w.fp8 else 'forward')} "
-                  f"oracle{' (context quantized before timing)' if w.fp8 else ''}, fp64 "
-                  f"NumPy, {dt:.1f} s",
+        "value_full_matrix": done_full / dt / 1e12,
+        "blas": blas_vendor(),
+        "sample": f"{units} of {len(unit_list)} {what}, every row, of workload {w.name}'s own "
+                  f"seeded inputs (q {list(w.q_shape)}, k/v {list(w.kv_shape)}"
+                  f"{', causal' if w.causal else ''}"
+                  f"{', rank 0 head shard via the oracle permute' if w.ulysses_P else ''}"
+                  f"{', packed documents' if cu is not None else ''}); {kind} oracle, fp64 "
+                  f"NumPy on {blas_vendor()}; it computes every masked score of the full "
+                  f"matrix: value credits the causal S^2/2 work like the GPU line, "
+                  f"value_full_matrix the S^2 it computes; {dt:.1f} s",
     }
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    # untimed steps: the GPU's clocks take tens of milliseconds of load to settle (five
-    # warm-up steps of the headline measured 2 % slower than a hundred)
-    ap.add_argument("--warmup", type=int, default=100)
-    ap.add_argument("--workload", default="qwen7b_ulysses4_rank0_32k")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-budget", type=float, default=15.0)
-    ap.add_argument("--chunked", action="store_true",
-                    help="ring workloads: one attn_fwd per visible chunk + lse_merge "
-                         "(backward: one attn_bwd_accum per visible chunk)")
-    args = ap.parse_args()
-    if args.gpus != 1:
-        print("bench.py measures one GPU: every box here has a single MI355X, and the multi-GPU "
-              "ring/Ulysses exchange is not part of this build (run with --gpus 1).",
-              file=sys.stderr)
-        sys.exit(2)
+# ------------------------------------------------------------------ GPU workloads
 
+def setup_workload(w, chunked, dev):
+    """Device inputs and the step's three parts for workload w: pre() (layout / quantize),
+    attn() (the timed attention kernel(s)), post(); plus flops, bytes moved by pre/post,
+    the roofline peak and extra report keys."""
     import torch
     import long_context_exact_tiled_amd as ra
     import seeded_inputs as si
 
-    w = si.WORKLOADS[args.workload]
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
     B, Hq, Sq, D = w.q_shape
     Skv = w.kv_shape[2]
 
     def to_dev(x):
-        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).to(dev) \
-            if w.dtype == "bf16" else torch.from_numpy(x).to(dev)
+        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16) \
+            .to(dev) if w.dtype == "bf16" else torch.from_numpy(x).to(dev)
 
     flops = attn_flops(B, Hq, Sq, Skv, D, w.num_chunks, w.causal, w.q_offset, w.kv_offset)
-    extra = {}
+    extra, moved = {}, 0
+    peak = PEAK_FP8_TFLOPS if w.fp8 else (PEAK_BF16_TFLOPS if w.dtype == "bf16"
+                                          else PEAK_F32_TFLOPS)
+    noop = lambda: None  # noqa: E731
+    pre = post = noop
     if w.ulysses_P:
         qs, ks, vs = (to_dev(x) for x in si.draw_ulysses_sources(w.seed))
         P, r = w.ulysses_P, w.ulysses_rank
@@ -219,9 +246,7 @@ def main():
         moved = 2 * (qh.numel() + 2 * kh.numel() + o.numel()) * qh.element_size()
 
         def pre():
-            ra.ulysses_permute(qs, P, r, 0, out=qh)
-            ra.ulysses_permute(ks, P, r, 0, out=kh)
-            ra.ulysses_permute(vs, P, r, 0, out=vh)
+            ra.ulysses_permute_multi([qs, ks, vs], P, r, 0, outs=[qh, kh, vh])
 
         def attn():
             ra.attn_fwd(qh.unsqueeze(0), kh.unsqueeze(0), vh.unsqueeze(0), causal=True,
@@ -243,7 +268,6 @@ def main():
         ws = torch.empty(1 << 20, dtype=torch.uint8, device=dev)
         o = torch.empty(q.shape, dtype=torch.bfloat16, device=dev)
         lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
-        moved = 0
         # quantizer traffic: two reads of the bf16 inputs (max pass, convert pass) and
         # one write of the codes
         extra["quantize_bytes"] = int(2 * (q.numel() + k.numel() + v.numel()) * 2
@@ -257,9 +281,6 @@ def main():
 
         def attn():
             ra.attn_fwd_fp8(qc, kc, vtc, qd, kd, vd, causal=w.causal, out=o, lse=lse)
-
-        def post():
-            pass
     elif w.packed_docs:
         q, k, v = (to_dev(x) for x in si.draw_qkv(w.seed, w.q_shape, w.kv_shape, w.dtype))
         cu = si.draw_doc_offsets(w.seed, Sq)
@@ -267,7 +288,6 @@ def main():
         o = torch.empty_like(q)
         lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
         flops = sum(attn_flops(B, Hq, b - a, b - a, D, 1, w.causal) for a, b in zip(cu, cu[1:]))
-        moved = 0
         extra["documents"] = len(cu) - 1
         if w.backward:
             ra.attn_fwd_varlen(q, k, v, cud, causal=w.causal, out=o, lse=lse)
@@ -286,12 +306,6 @@ def main():
 
             def attn():
                 ra.attn_fwd_varlen(q, k, v, cud, causal=w.causal, out=o, lse=lse)
-
-        def pre():
-            pass
-
-        def post():
-            pass
     elif w.backward:
         q, k, v, do = (to_dev(x) for x in si.draw_qkv(w.seed, w.q_shape, w.kv_shape, w.dtype,
                                                       with_dout=True))
@@ -301,8 +315,7 @@ def main():
         ws = torch.empty(max(ra.attn_bwd_workspace_size(q, k, **kw), 256),
                          dtype=torch.uint8, device=dev)
         flops *= 2.5  # five matrix products per (query, key) pair against the forward's two
-        moved = 0
-        if args.chunked:
+        if chunked:
             # one ring rank's backward as the ring delivers the chunks: one accumulating
             # step per visible chunk into fp32 accumulators (zeroed before each pass)
             dq = torch.zeros(q.shape, dtype=torch.float32, device=dev)
@@ -322,71 +335,175 @@ def main():
             dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
             extra["kernel"] = "attn_bwd (delta + dkdv + dq)"
 
-            def pre():
-                pass
-
             def attn():
                 ra.attn_bwd(q, k, v, o, do, lse, dq=dq, dk=dk, dv=dv, workspace=ws, **kw)
-
-        def post():
-            pass
     else:
         q, k, v = (to_dev(x) for x in si.draw_qkv(w.seed, w.q_shape, w.kv_shape, w.dtype))
         o = torch.empty_like(q)
         lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
-        moved = 0
         kw = dict(causal=w.causal, num_chunks=w.num_chunks, start_chunk=w.start_chunk,
                   q_offset=w.q_offset, kv_offset=w.kv_offset)
-
-        def pre():
-            pass
-
-        if args.chunked:
+        if chunked:
             extra["kernel"] = "attn_fwd per visible chunk (fp32 partials) + lse_merge"
 
             def attn():
                 ra.ring_attn_chunked(q, k, v, **kw)
+
+            # the merge alone: partials of the visible chunks computed once, then
+            # lse_merge timed by itself (HBM-bound: every partial read once, the result
+            # written once)
+            L = Skv // w.num_chunks
+            chunks = ra.ring_visible_chunks(Sq, Skv, num_chunks=w.num_chunks,
+                                            start_chunk=w.start_chunk, causal=w.causal,
+                                            q_offset=w.q_offset, kv_offset=w.kv_offset)
+            parts = [ra.attn_fwd(q, k[:, :, c * L:(c + 1) * L], v[:, :, c * L:(c + 1) * L],
+                                 causal=w.causal, q_offset=w.q_offset,
+                                 kv_offset=w.kv_offset + c * L, out_dtype=torch.float32)
+                     for c in chunks]
+            mo, ml = ra.lse_merge([x[0] for x in parts], [x[1] for x in parts])
+            mbytes = sum(x[0].numel() * 4 + x[1].numel() * 4 for x in parts) + \
+                mo.numel() * mo.element_size() + ml.numel() * 4
+
+            def merge():
+                ra.lse_merge([x[0] for x in parts], [x[1] for x in parts], out=mo, lse=ml)
+            extra["_merge"] = (merge, mbytes, len(parts))
         else:
             def attn():
                 ra.attn_fwd(q, k, v, out=o, lse=lse, **kw)
+    return dict(pre=pre, attn=attn, post=post, flops=flops, moved=moved, peak=peak, extra=extra)
 
-        def post():
-            pass
 
-    stream = torch.cuda.current_stream(dev)
-    for _ in range(args.warmup):
-        pre(); attn(); post()
+def time_step(s, warmup, steps, stream):
+    """W untimed steps, then K timed ones with HIP events on the stream around each part.
+    Returns (total ms per step, attention ms per step list, pre+post ms list)."""
+    import torch
+    for _ in range(warmup):
+        s["pre"](); s["attn"](); s["post"]()
     torch.cuda.synchronize()
-
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     t_start.record(stream)
-    for s in range(args.steps):
-        ev[s][0].record(stream)
-        pre()
-        ev[s][1].record(stream)
-        attn()
-        ev[s][2].record(stream)
-        post()
-        ev[s][3].record(stream)
+    for e in ev:
+        e[0].record(stream)
+        s["pre"]()
+        e[1].record(stream)
+        s["attn"]()
+        e[2].record(stream)
+        s["post"]()
+        e[3].record(stream)
     t_end.record(stream)
     torch.cuda.synchronize()
     total_ms = t_start.elapsed_time(t_end)
-    ms_step = total_ms / args.steps
     attn_ms = [e[1].elapsed_time(e[2]) for e in ev]
-    perm_ms = [e[0].elapsed_time(e[1]) + e[2].elapsed_time(e[3]) for e in ev]
+    side_ms = [e[0].elapsed_time(e[1]) + e[2].elapsed_time(e[3]) for e in ev]
+    return total_ms / steps, attn_ms, side_ms
+
+
+def time_calls(fn, stream, reps=5, inner=20):
+    """Median per-call ms of `inner` back-to-back calls, over `reps` samples."""
+    import torch
+    fn()
+    torch.cuda.synchronize()
+    mt = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(inner):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        mt.append(e0.elapsed_time(e1) / inner)
+    return float(np.median(mt))
+
+
+# The other workloads of the hot path, reported beside the headline in the default run:
+# (report key, workload, chunk by chunk)
+SECONDARY = [
+    ("llama7b_8k_fwd", "llama7b_causal_8k", False),
+    ("ring8_rank3_32k_fused_fwd", "ring8_rank3_32k", False),
+    ("ring8_rank3_32k_chunked_fwd", "ring8_rank3_32k", True),
+    ("llama7b_16k_bwd", "llama7b_causal_bwd_16k", False),
+]
+
+
+def secondary_lines(dev, stream, min_warmup_ms=150.0, steps=20):
+    """Attention TFLOP/s and fraction of peak of each secondary workload (warm clocks:
+    untimed calls for at least min_warmup_ms first), the merge's GB/s for the chunked
+    ring share."""
+    import torch
+    import seeded_inputs as si
+    out = {}
+    for key, name, chunked in SECONDARY:
+        w = si.WORKLOADS[name]
+        s = setup_workload(w, chunked, dev)
+        s["attn"]()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        s["attn"]()
+        torch.cuda.synchronize()
+        est_ms = max((time.perf_counter() - t0) * 1e3, 0.05)
+        warm = int(min(400, max(5, math.ceil(min_warmup_ms / est_ms))))
+        _, attn_ms, _ = time_step(s, warm, steps, stream)
+        ms = float(np.median(attn_ms))
+        tf = s["flops"] / (ms * 1e-3) / 1e12
+        out[f"{key}_ms"] = ms
+        out[f"{key}_tflops"] = tf
+        out[f"{key}_frac"] = tf / s["peak"]
+        if "_merge" in s["extra"]:
+            merge, mbytes, nparts = s["extra"]["_merge"]
+            mms = time_calls(merge, stream)
+            out["ring8_rank3_32k_merge_parts"] = nparts
+            out["ring8_rank3_32k_merge_ms"] = mms
+            out["ring8_rank3_32k_merge_GBps"] = mbytes / (mms * 1e-3) / 1e9
+            out["ring8_rank3_32k_merge_frac_of_hbm_peak"] = \
+                out["ring8_rank3_32k_merge_GBps"] / PEAK_HBM_GBPS
+        del s
+        torch.cuda.empty_cache()
+    return out
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    # untimed steps: the GPU's clocks take tens of milliseconds of load to settle (five
+    # warm-up steps of the headline measured 2 % slower than a hundred)
+    ap.add_argument("--warmup", type=int, default=100)
+    ap.add_argument("--workload", default=HEADLINE)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=20.0)
+    ap.add_argument("--no-secondary", action="store_true",
+                    help="skip the other workloads reported beside the headline")
+    ap.add_argument("--chunked", action="store_true",
+                    help="ring workloads: one attn_fwd per visible chunk + lse_merge "
+                         "(backward: one attn_bwd_accum per visible chunk)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: every box here has a single MI355X, and the multi-GPU "
+              "ring/Ulysses exchange is not part of this build (run with --gpus 1).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import seeded_inputs as si
+
+    w = si.WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+    s = setup_workload(w, args.chunked, dev)
+    flops, moved, peak, extra = s["flops"], s["moved"], s["peak"], s["extra"]
+
+    ms_step, attn_ms, side_ms = time_step(s, args.warmup, args.steps, stream)
     attn_avg = float(np.mean(attn_ms))
     achieved = flops / (attn_avg * 1e-3) / 1e12
-    peak = PEAK_FP8_TFLOPS if w.fp8 else (PEAK_BF16_TFLOPS if w.dtype == "bf16"
-                                          else PEAK_F32_TFLOPS)
     if w.fp8:
-        extra["quantize_ms_per_step"] = float(np.mean(perm_ms))
-        extra["quantize_GBps"] = extra["quantize_bytes"] / (np.mean(perm_ms) * 1e-3) / 1e9
+        extra["quantize_ms_per_step"] = float(np.mean(side_ms))
+        extra["quantize_GBps"] = extra["quantize_bytes"] / (np.mean(side_ms) * 1e-3) / 1e9
     if moved:
-        extra["permute_ms_per_step"] = float(np.mean(perm_ms))
-        extra["permute_GBps"] = moved / (np.mean(perm_ms) * 1e-3) / 1e9
+        extra["permute_ms_per_step"] = float(np.mean(side_ms))
+        extra["permute_GBps"] = moved / (np.mean(side_ms) * 1e-3) / 1e9
         # cold-cache rate: a 1 GiB write evicts the 256 MB Infinity Cache before each pass
         scratch = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
         cold = []
@@ -394,51 +511,35 @@ def main():
             scratch.zero_()
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record(stream)
-            pre()
+            s["pre"]()
             e1.record(stream)
             scratch.zero_()
             e2, e3 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e2.record(stream)
-            post()
+            s["post"]()
             e3.record(stream)
             torch.cuda.synchronize()
             cold.append(e0.elapsed_time(e1) + e2.elapsed_time(e3))
         del scratch
         extra["permute_cold_ms_per_step"] = float(np.median(cold))
         extra["permute_cold_GBps"] = moved / (np.median(cold) * 1e-3) / 1e9
-    if args.chunked and not w.backward and not w.fp8:
-        # the merge alone: partials of the visible chunks computed once, then lse_merge
-        # timed by itself (HBM-bound: every partial read once, the result written once)
-        L = w.kv_shape[2] // w.num_chunks
-        chunks = ra.ring_visible_chunks(w.q_shape[2], w.kv_shape[2], num_chunks=w.num_chunks,
-                                        start_chunk=w.start_chunk, causal=w.causal,
-                                        q_offset=w.q_offset, kv_offset=w.kv_offset)
-        parts = [ra.attn_fwd(q, k[:, :, c * L:(c + 1) * L], v[:, :, c * L:(c + 1) * L],
-                             causal=w.causal, q_offset=w.q_offset,
-                             kv_offset=w.kv_offset + c * L, out_dtype=torch.float32)
-                 for c in chunks]
-        mo, ml = ra.lse_merge([x[0] for x in parts], [x[1] for x in parts])
-        torch.cuda.synchronize()
-        mt = []
-        for _ in range(5):  # 20 back-to-back merges per sample
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            for _ in range(20):
-                ra.lse_merge([x[0] for x in parts], [x[1] for x in parts], out=mo, lse=ml)
-            e1.record(stream)
-            torch.cuda.synchronize()
-            mt.append(e0.elapsed_time(e1) / 20)
-        mbytes = sum(x[0].numel() * 4 + x[1].numel() * 4 for x in parts) + \
-            mo.numel() * mo.element_size() + ml.numel() * 4
-        extra["merge_parts"] = len(parts)
-        extra["merge_ms"] = float(np.median(mt))
-        extra["merge_GBps"] = mbytes / (np.median(mt) * 1e-3) / 1e9
+    merge = extra.pop("_merge", None)
+    if merge is not None:
+        fn, mbytes, nparts = merge
+        mms = time_calls(fn, stream)
+        extra["merge_parts"] = nparts
+        extra["merge_ms"] = mms
+        extra["merge_GBps"] = mbytes / (mms * 1e-3) / 1e9
         extra["merge_frac_of_hbm_peak"] = extra["merge_GBps"] / PEAK_HBM_GBPS
-        del parts
     extra["attn_fwd_ms"] = attn_avg
     extra["attn_fwd_ms_median"] = float(np.median(attn_ms))
     extra["attn_fwd_ms_min"] = float(np.min(attn_ms))
     extra["attn_flops"] = flops
+    kernel = extra.pop("kernel", "attn_fwd")
+    del s
+    torch.cuda.empty_cache()
+    if w.name == HEADLINE and not args.chunked and not args.no_secondary:
+        extra.update(secondary_lines(dev, stream))
 
     line = {
         "metric": METRIC,
@@ -458,12 +559,11 @@ def main():
                    "q_offset": w.q_offset, "ulysses_P": w.ulysses_P,
                    "ulysses_rank": w.ulysses_rank, "parallelism": "1 GPU (one rank's share)"},
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
-                     "frac": achieved / peak, "traffic": None,
-                     "kernel": extra.pop("kernel", "attn_fwd")},
+                     "frac": achieved / peak, "traffic": None, "kernel": kernel},
         "cpu_baseline": None,
         **extra,
     }
-    if w.name == "qwen7b_ulysses4_rank0_32k" and not args.chunked:
+    if w.name == HEADLINE and not args.chunked:
         line["roofline"]["traffic"] = measured_traffic()
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)

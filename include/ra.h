@@ -13,6 +13,11 @@
  *   per-axis shape and stride counted in ELEMENTS.  The innermost stride must be 1.
  *   Every data pointer must be 16-byte aligned and every outer stride must be a
  *   whole number of 16-byte units (rows are moved with 16-byte vector accesses).
+ * - Token strides of attention operands ([B, H, S, D] tensors of the attention entry
+ *   points): the kernels move tiles of up to 128 tokens and form a byte offset within
+ *   a tile in 32 bits, so (min(128, S) - 1) * stride[2] + D, in bytes, must stay below
+ *   2^31 (about 8.4 M bf16 elements of token stride); otherwise RA_ERR_SHAPE.  Batch
+ *   and head strides are not limited.
  * - The caller owns and allocates every buffer (inputs, outputs, workspace).  The
  *   library allocates nothing, keeps no global state and never synchronises.
  * - Work is enqueued on `stream` (a hipStream_t; NULL is the null stream).  Outputs
@@ -37,6 +42,7 @@ extern "C" {
 
 #define RA_VERSION 100 /* 0.1.0 */
 #define RA_MAX_MERGE_PARTS 64
+#define RA_MAX_PERMUTE_TENSORS 4
 #define RA_MAX_DOCS (1 << 24)
 
 typedef enum {
@@ -197,6 +203,23 @@ int ra_ulysses_permute(const ra_tensor *src, ra_tensor *dst, int32_t P, int32_t 
                        ra_stream stream);
 int ra_ulysses_permute_validate(const ra_tensor *src, const ra_tensor *dst, int32_t P, int32_t rank,
                                 int32_t dir);
+
+/*
+ * ra_ulysses_permute_n -- ra_ulysses_permute of n (src, dst) pairs in one launch, e.g. the
+ * q, k and v of one layer before attention (the same section of [P4]: one all-to-all
+ * carries all of a layer's inputs; here one kernel packs them).
+ *
+ * srcs, dsts: arrays of n descriptors; pair i is exactly ra_ulysses_permute(&srcs[i],
+ * &dsts[i], P, rank, dir) and is validated as such (pairs may differ in head count, e.g.
+ * 28 query and 4 key/value heads, in dtype and in head dim).  No destination may overlap
+ * any source or another destination.  1 <= n <= RA_MAX_PERMUTE_TENSORS (else
+ * RA_ERR_RANGE).  Pairs whose rows (D * element size) are all 128, 256 or 512 bytes of
+ * one size move in a single launch; otherwise pair by pair.  Bit-exact.
+ */
+int ra_ulysses_permute_n(int32_t n, const ra_tensor *srcs, ra_tensor *dsts, int32_t P, int32_t rank,
+                         int32_t dir, ra_stream stream);
+int ra_ulysses_permute_n_validate(int32_t n, const ra_tensor *srcs, const ra_tensor *dsts,
+                                  int32_t P, int32_t rank, int32_t dir);
 
 /*
  * ra_attn_bwd -- gradients dq, dk, dv of L = sum(dout * o) for the attention of

@@ -29,7 +29,7 @@ __all__ = [
     "attn_fwd_varlen", "attn_fwd_varlen_validate", "attn_bwd_varlen", "attn_bwd_varlen_validate",
     "attn_bwd_accum", "attn_bwd_accum_validate", "ring_attn_bwd_chunked",
     "fp8_quantize", "fp8_quantize_validate", "attn_fwd_fp8", "attn_fwd_fp8_validate",
-    "ring_attn_fp8_chunked",
+    "ring_attn_fp8_chunked", "ulysses_permute_multi", "ulysses_permute_multi_validate",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libra.so")
@@ -102,6 +102,8 @@ def lib() -> ctypes.CDLL:
             "ra_lse_merge_validate": [i32, T, T, T, T],
             "ra_ulysses_permute": [T, T, i32, i32, i32, vp],
             "ra_ulysses_permute_validate": [T, T, i32, i32, i32],
+            "ra_ulysses_permute_n": [i32, T, T, i32, i32, i32, vp],
+            "ra_ulysses_permute_n_validate": [i32, T, T, i32, i32, i32],
             "ra_attn_bwd": [T, T, T, T, T, T, PP, T, T, T, vp, sz, vp],
             "ra_attn_bwd_validate": [T, T, T, T, T, T, PP, T, T, T],
             "ra_attn_bwd_varlen": [T, T, T, T, T, T, vp, i32, PP, T, T, T, vp, sz, vp],
@@ -345,6 +347,31 @@ def ulysses_permute(src: torch.Tensor, P: int, rank: int, dir: int = 0, *,
     _check(lib().ra_ulysses_permute(desc(src), desc(out), int(P), int(rank), int(dir),
                                     _stream(src)))
     return out
+
+
+def ulysses_permute_multi(srcs: Sequence[torch.Tensor], P: int, rank: int, dir: int = 0, *,
+                          outs: Optional[Sequence[torch.Tensor]] = None):
+    """ulysses_permute of several tensors (e.g. q, k, v of a layer) in one launch.
+    Returns the list of destinations."""
+    srcs = list(srcs)
+    if outs is None:
+        outs = [torch.empty(_permute_out_shape(s, P, rank, dir), dtype=s.dtype, device=s.device)
+                for s in srcs]
+    outs = list(outs)
+    if len(outs) != len(srcs) or not srcs:
+        raise RaError(-6, "RA_ERR_RANGE: srcs and outs must be non-empty and of equal length")
+    sa = (RaTensor * len(srcs))(*[desc(t) for t in srcs])
+    oa = (RaTensor * len(outs))(*[desc(t) for t in outs])
+    _check(lib().ra_ulysses_permute_n(len(srcs), sa, oa, int(P), int(rank), int(dir),
+                                      _stream(srcs[0])))
+    return outs
+
+
+def ulysses_permute_multi_validate(srcs, outs, P, rank, dir) -> int:
+    sa = (RaTensor * max(len(srcs), 1))(*[desc(t) for t in srcs])
+    oa = (RaTensor * max(len(outs), 1))(*[desc(t) for t in outs])
+    return int(lib().ra_ulysses_permute_n_validate(len(srcs), sa, oa, int(P), int(rank),
+                                                   int(dir)))
 
 
 def ulysses_permute_validate(src, out, P, rank, dir) -> int:

@@ -131,6 +131,17 @@ int check_lse(const ra_tensor *lse, const ra_tensor *q, bool is_output) {
   return RA_OK;
 }
 
+// A [B, H, S, D] operand read in tiles of up to kMaxTileRows tokens: a lane's byte offset
+// within a tile, (rows - 1) * token stride + row bytes, must fit in 31 bits.
+int check_tile_span(const ra_tensor *t) {
+  if (!t || t->ndim != 4) return RA_OK;
+  const int64_t rows = std::min<int64_t>(kMaxTileRows, t->shape[2]);
+  if (rows <= 1 || t->shape[3] == 0) return RA_OK;
+  const int64_t es = esize(t->dtype);
+  if ((rows - 1) * t->stride[2] * es + t->shape[3] * es > (int64_t)INT32_MAX) return RA_ERR_SHAPE;
+  return RA_OK;
+}
+
 int check_grid(const ra_tensor *q) {
   const int64_t tiles = (q->shape[2] + 127) / 128;
   if (tiles * q->shape[1] * q->shape[0] > (int64_t)INT32_MAX) return RA_ERR_SHAPE;
@@ -147,6 +158,7 @@ int fwd_validate(const ra_tensor *q, const ra_tensor *k, const ra_tensor *v,
   if (!same_shape(o, q)) return RA_ERR_SHAPE;
   RA_TRY(check_lse(lse, q, true));
   RA_TRY(check_grid(q));
+  for (const ra_tensor *t : {q, k, v, o}) RA_TRY(check_tile_span(t));
   const int64_t D = q->shape[3];
   if (D != 64 && D != 128) return RA_ERR_UNSUPPORTED;
   return RA_OK;
@@ -223,6 +235,7 @@ int bwd_validate(const ra_tensor *q, const ra_tensor *k, const ra_tensor *v, con
   RA_TRY(check_lse(lse, q, false));
   RA_TRY(check_grid(q));
   RA_TRY(check_grid(k));
+  for (const ra_tensor *t : {q, k, v, o, dout, dq, dk, dv}) RA_TRY(check_tile_span(t));
   const int64_t D = q->shape[3];
   if (q->dtype != RA_BF16) return RA_ERR_UNSUPPORTED;
   if (D != 64 && D != 128) return RA_ERR_UNSUPPORTED;
@@ -486,15 +499,9 @@ int ra_lse_merge(int32_t n, const ra_tensor *o_parts, const ra_tensor *lse_parts
   return launch_lse_merge(a, (hipStream_t)stream);
 }
 
-int ra_ulysses_permute_validate(const ra_tensor *src, const ra_tensor *dst, int32_t P,
-                                int32_t rank, int32_t dir) {
-  return permute_validate(src, dst, P, rank, dir);
-}
-
-int ra_ulysses_permute(const ra_tensor *src, ra_tensor *dst, int32_t P, int32_t rank, int32_t dir,
-                       ra_stream stream) {
-  RA_TRY(permute_validate(src, dst, P, rank, dir));
-  if (numel(src) == 0) return RA_OK;
+namespace {
+PermuteArgs permute_args(const ra_tensor *src, const ra_tensor *dst, int32_t P, int32_t rank,
+                         int32_t dir) {
   const ra_tensor *seq = dir == 0 ? src : dst;
   const ra_tensor *head = dir == 0 ? dst : src;
   PermuteArgs a{};
@@ -509,7 +516,67 @@ int ra_ulysses_permute(const ra_tensor *src, ra_tensor *dst, int32_t P, int32_t 
   a.rank0 = rank == -1 ? 0 : rank;
   a.nranks = rank == -1 ? P : 1;
   a.dir = dir;
+  return a;
+}
+
+// byte range [lo, hi) a tensor's elements can touch (a conservative extent)
+void byte_span(const ra_tensor *t, uintptr_t &lo, uintptr_t &hi) {
+  int64_t last = 0;
+  for (int i = 0; i < t->ndim; ++i)
+    if (t->shape[i] > 0) last += (t->shape[i] - 1) * t->stride[i];
+  lo = (uintptr_t)t->data;
+  hi = lo + (uintptr_t)((last + 1) * esize(t->dtype));
+}
+
+bool overlaps(const ra_tensor *a, const ra_tensor *b) {
+  if (numel(a) == 0 || numel(b) == 0) return false;
+  uintptr_t a0, a1, b0, b1;
+  byte_span(a, a0, a1);
+  byte_span(b, b0, b1);
+  return a0 < b1 && b0 < a1;
+}
+
+int permute_n_validate(int32_t n, const ra_tensor *srcs, const ra_tensor *dsts, int32_t P,
+                       int32_t rank, int32_t dir) {
+  if (!srcs || !dsts) return RA_ERR_NULL;
+  if (n < 1 || n > RA_MAX_PERMUTE_TENSORS) return RA_ERR_RANGE;
+  for (int i = 0; i < n; ++i) RA_TRY(permute_validate(&srcs[i], &dsts[i], P, rank, dir));
+  for (int i = 0; i < n; ++i)
+    for (int j = 0; j < n; ++j)
+      if (overlaps(&dsts[i], &srcs[j]) || (i != j && overlaps(&dsts[i], &dsts[j])))
+        return RA_ERR_STRIDE;
+  return RA_OK;
+}
+}  // namespace
+
+int ra_ulysses_permute_validate(const ra_tensor *src, const ra_tensor *dst, int32_t P,
+                                int32_t rank, int32_t dir) {
+  return permute_validate(src, dst, P, rank, dir);
+}
+
+int ra_ulysses_permute(const ra_tensor *src, ra_tensor *dst, int32_t P, int32_t rank, int32_t dir,
+                       ra_stream stream) {
+  RA_TRY(permute_validate(src, dst, P, rank, dir));
+  if (numel(src) == 0) return RA_OK;
+  const PermuteArgs a = permute_args(src, dst, P, rank, dir);
   return launch_ulysses_permute(a, (hipStream_t)stream);
+}
+
+
+int ra_ulysses_permute_n_validate(int32_t n, const ra_tensor *srcs, const ra_tensor *dsts,
+                                  int32_t P, int32_t rank, int32_t dir) {
+  return permute_n_validate(n, srcs, dsts, P, rank, dir);
+}
+
+int ra_ulysses_permute_n(int32_t n, const ra_tensor *srcs, ra_tensor *dsts, int32_t P,
+                         int32_t rank, int32_t dir, ra_stream stream) {
+  RA_TRY(permute_n_validate(n, srcs, dsts, P, rank, dir));
+  PermuteArgs a[RA_MAX_PERMUTE_TENSORS];
+  int k = 0;
+  for (int i = 0; i < n; ++i)
+    if (numel(&srcs[i]) > 0) a[k++] = permute_args(&srcs[i], &dsts[i], P, rank, dir);
+  if (k == 0) return RA_OK;
+  return launch_ulysses_permute_n(a, k, (hipStream_t)stream);
 }
 
 int ra_attn_bwd_validate(const ra_tensor *q, const ra_tensor *k, const ra_tensor *v,

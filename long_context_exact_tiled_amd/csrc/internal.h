@@ -11,6 +11,12 @@ namespace ra {
 
 constexpr float kLog2eHost = 1.4426950408889634f;
 
+// Kernels that move [rows, D] tiles straight from global memory into LDS form each
+// lane's byte offset within a tile in 32 bits.  No tile has more rows than this, so the
+// host accepts a token stride only if (min(kMaxTileRows, S) - 1) * stride + D elements
+// stay below 2^31 bytes.
+constexpr int kMaxTileRows = 128;
+
 // Forward attention problem after validation: raw pointers and element strides.
 struct FwdArgs {
   const void *q;
@@ -69,6 +75,8 @@ struct PermuteArgs {
 };
 
 int launch_ulysses_permute(const PermuteArgs &a, hipStream_t stream);
+// Several (src, dst) pairs with the same P, rank and direction in one launch.
+int launch_ulysses_permute_n(const PermuteArgs *a, int n, hipStream_t stream);
 
 struct BwdArgs {
   const void *q, *k, *v, *o, *dout;

@@ -13,6 +13,8 @@
 // tile) from the grid and (row, 16-byte column) from the thread index, so no thread
 // divides; every wavefront reads and writes whole rows.  Row sizes other than 128, 256
 // or 512 bytes use a flat kernel that decodes each 16-byte chunk's position by division.
+// Several tensors (q, k and v of a layer) can move in one launch: the grid's z axis
+// runs over the (rank, head) ranges of every pair in turn.
 #include "common.h"
 #include "internal.h"
 
@@ -71,14 +73,27 @@ __global__ void __launch_bounds__(kThreads) permute_kernel(PermuteArgs a, int64_
   }
 }
 
-// grid (token tiles, shard s, rank-and-head rr * Hl + hh); CPR 16-byte chunks per row
+// Up to this many (src, dst) pairs share one launch; the z extent of the grid is the
+// concatenation of their (rank, head) ranges.
+constexpr int kMaxPairs = RA_MAX_PERMUTE_TENSORS;
+struct PairArgs {
+  PermuteArgs t[kMaxPairs];
+  int32_t zbase[kMaxPairs + 1];  // pair i owns grid z in [zbase[i], zbase[i+1])
+  int32_t n;
+};
+
+// grid (token tiles, shard s, rank-and-head rr * Hl + hh of pair i, pairs concatenated);
+// CPR 16-byte chunks per row
 constexpr int kRowUnroll = 4;
 template <int CPR>
-__global__ void __launch_bounds__(kThreads) permute_rows_kernel(PermuteArgs a) {
+__global__ void __launch_bounds__(kThreads) permute_rows_kernel(PairArgs m) {
   constexpr int RPB = kThreads / CPR;  // rows per pass of the block
+  int i = 0;  // the pair of this block (wave-uniform)
+  while (i + 1 < m.n && (int)blockIdx.z >= m.zbase[i + 1]) ++i;
+  const PermuteArgs &a = m.t[i];
   const int rl = threadIdx.x / CPR, c = threadIdx.x % CPR;
   const int s = blockIdx.y;
-  const int rh = blockIdx.z;
+  const int rh = blockIdx.z - m.zbase[i];
   const int hh = rh % a.Hl, rr = rh / a.Hl;  // wave-uniform
   const int64_t rank = a.rank0 + rr;
   const int64_t seq_base = s * a.seq_s0 + (rank * a.Hl + hh) * a.seq_s2;
@@ -105,28 +120,68 @@ __global__ void __launch_bounds__(kThreads) permute_rows_kernel(PermuteArgs a) {
 
 }  // namespace
 
-int launch_ulysses_permute(const PermuteArgs &a, hipStream_t stream) {
+namespace {
+
+int launch_flat(const PermuteArgs &a, hipStream_t stream) {
   const int64_t rows = (int64_t)a.nranks * a.Hl * a.P * a.Sl;
   const int64_t nchunks = rows * (a.row_bytes / 16);
   if (nchunks <= 0) return RA_OK;
-  const int cpr = a.row_bytes / 16;
-  const int64_t rh = (int64_t)a.nranks * a.Hl;
-  if ((cpr == 8 || cpr == 16 || cpr == 32) && a.P <= 65535 && rh <= 65535) {
-    const int64_t rows_per_block = (int64_t)(kThreads / cpr) * kRowUnroll;
-    const dim3 grid((unsigned)((a.Sl + rows_per_block - 1) / rows_per_block), (unsigned)a.P,
-                    (unsigned)rh);
-    if (cpr == 8)
-      hipLaunchKernelGGL(permute_rows_kernel<8>, grid, dim3(kThreads), 0, stream, a);
-    else if (cpr == 16)
-      hipLaunchKernelGGL(permute_rows_kernel<16>, grid, dim3(kThreads), 0, stream, a);
-    else
-      hipLaunchKernelGGL(permute_rows_kernel<32>, grid, dim3(kThreads), 0, stream, a);
-    return hipGetLastError() == hipSuccess ? RA_OK : RA_ERR_HIP;
-  }
   int64_t blocks = (nchunks + (int64_t)kThreads * kUnroll - 1) / ((int64_t)kThreads * kUnroll);
   if (blocks > 65536) blocks = 65536;
   hipLaunchKernelGGL(permute_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, stream, a, nchunks);
   return hipGetLastError() == hipSuccess ? RA_OK : RA_ERR_HIP;
+}
+
+// The row kernel serves pairs whose rows are 128, 256 or 512 bytes, all the same size.
+bool rows_kernel_fits(const PermuteArgs *a, int n) {
+  const int cpr = a[0].row_bytes / 16;
+  if (cpr != 8 && cpr != 16 && cpr != 32) return false;
+  int64_t z = 0;
+  for (int i = 0; i < n; ++i) {
+    if (a[i].row_bytes != a[0].row_bytes || a[i].P != a[0].P || a[i].P > 65535) return false;
+    z += (int64_t)a[i].nranks * a[i].Hl;
+  }
+  return z <= 65535;
+}
+
+}  // namespace
+
+int launch_ulysses_permute_n(const PermuteArgs *a, int n, hipStream_t stream) {
+  // pairs with nothing to move drop out
+  PairArgs m{};
+  int k = 0;
+  for (int i = 0; i < n; ++i)
+    if ((int64_t)a[i].nranks * a[i].Hl * a[i].P * a[i].Sl > 0) m.t[k++] = a[i];
+  if (k == 0) return RA_OK;
+  if (!rows_kernel_fits(m.t, k)) {
+    for (int i = 0; i < k; ++i) {
+      const int rc = launch_flat(m.t[i], stream);
+      if (rc != RA_OK) return rc;
+    }
+    return RA_OK;
+  }
+  m.n = k;
+  int32_t max_sl = 0;
+  m.zbase[0] = 0;
+  for (int i = 0; i < k; ++i) {
+    m.zbase[i + 1] = m.zbase[i] + m.t[i].nranks * m.t[i].Hl;
+    max_sl = m.t[i].Sl > max_sl ? m.t[i].Sl : max_sl;
+  }
+  const int cpr = m.t[0].row_bytes / 16;
+  const int64_t rows_per_block = (int64_t)(kThreads / cpr) * kRowUnroll;
+  const dim3 grid((unsigned)((max_sl + rows_per_block - 1) / rows_per_block), (unsigned)m.t[0].P,
+                  (unsigned)m.zbase[k]);
+  if (cpr == 8)
+    hipLaunchKernelGGL(permute_rows_kernel<8>, grid, dim3(kThreads), 0, stream, m);
+  else if (cpr == 16)
+    hipLaunchKernelGGL(permute_rows_kernel<16>, grid, dim3(kThreads), 0, stream, m);
+  else
+    hipLaunchKernelGGL(permute_rows_kernel<32>, grid, dim3(kThreads), 0, stream, m);
+  return hipGetLastError() == hipSuccess ? RA_OK : RA_ERR_HIP;
+}
+
+int launch_ulysses_permute(const PermuteArgs &a, hipStream_t stream) {
+  return launch_ulysses_permute_n(&a, 1, stream);
 }
 
 }  // namespace ra

@@ -169,6 +169,23 @@ def test_permute_validation(ra):
     assert v(_t((4, 16, 28, 4)), _t((7, 64, 4)), 4, 0, 0) == "RA_ERR_ALIGN"  # 8-byte rows
 
 
+def test_permute_n_validation(ra):
+    q, k, v = _t((4, 16, 28, 128)), _t((4, 16, 4, 128)), _t((4, 16, 4, 128))
+    qh, kh, vh = _t((7, 64, 128)), _t((1, 64, 128)), _t((1, 64, 128))
+    v_ = lambda s, d, P=4, r=0, dr=0: ra.STATUS[ra.ulysses_permute_multi_validate(s, d, P, r, dr)]
+    assert v_([q, k, v], [qh, kh, vh]) == "RA_OK"
+    assert v_([qh, kh, vh], [q, k, v], dr=1) == "RA_OK"
+    assert v_([q, k, v], [qh, kh, _t((2, 64, 128))]) == "RA_ERR_SHAPE"  # third pair invalid
+    assert v_([q] * 5, [qh] * 5) == "RA_ERR_RANGE"                      # more than 4 pairs
+    assert v_([], []) == "RA_ERR_RANGE"
+    # destinations overlapping each other or a source
+    buf = _t((2 * 64 * 128,))
+    a, b = buf[:64 * 128].view(1, 64, 128), buf[32 * 128:96 * 128].view(1, 64, 128)
+    assert v_([k, v], [a, b]) == "RA_ERR_STRIDE"
+    kflat = k.view(-1)
+    assert v_([k, v], [kh, kflat[:64 * 128].view(1, 64, 128)]) == "RA_ERR_STRIDE"  # dst on a src
+
+
 def test_bwd_validation(ra):
     q, k, v = _t((1, 4, 64, 128)), _t((1, 2, 64, 128)), _t((1, 2, 64, 128))
     o, do, lse = _t(q.shape), _t(q.shape), torch.zeros(1, 4, 64)
@@ -267,3 +284,54 @@ def test_params_versions_and_work_counter(ra):
     assert check(40, None) == "RA_OK"
     assert check(40, 0x10004) == "RA_OK"  # a version-1 block has no counter field
     assert check(39, None) == "RA_ERR_RANGE"
+
+
+def _raw(ra, shape, stride, dtype, ptr=1 << 20):
+    """A descriptor with a fake device address: the *_validate entry points never
+    dereference it, so huge strides need no memory."""
+    d = ra.RaTensor()
+    d.data = ptr
+    d.dtype = dtype
+    d.ndim = len(shape)
+    for i, (n, s) in enumerate(zip(shape, stride)):
+        d.shape[i] = n
+        d.stride[i] = s
+    return d
+
+
+def _contig(shape):
+    st, acc = [], 1
+    for n in reversed(shape):
+        st.insert(0, acc)
+        acc *= n
+    return st
+
+
+@pytest.mark.parametrize("S,token_stride,want", [
+    (256, 8_000_000, "RA_OK"),            # 127 * 8.0M * 2 + 256 B < 2^31
+    (256, 8_455_000, "RA_ERR_SHAPE"),     # 127 * 8.455M * 2 B > 2^31
+    (2, 8_455_000, "RA_OK"),              # a 2-token tile spans one stride only
+    (128, 8_455_000, "RA_ERR_SHAPE"),
+    (200, 1 << 30, "RA_ERR_SHAPE"),
+])
+def test_tile_offset_bound(ra, S, token_stride, want):
+    """Token strides whose in-tile byte offsets would pass 2^31 are rejected on the host
+    (checked only through the validate entry points; such views never reach a GPU)."""
+    L = ra.lib()
+    BF16 = ra.RA_BF16
+    D = 128
+    big = [2 * token_stride * S, token_stride * S, token_stride, 1]
+    okq = lambda: _raw(ra, (1, 2, S, D), _contig((1, 2, S, D)), BF16)
+    lse = _raw(ra, (1, 2, S), _contig((1, 2, S)), ra.RA_F32)
+    p = ra._params(True, 1, 0, 0, 0, None)
+    for which in range(4):  # q, k, v, o in turn carry the large token stride
+        ts = [okq() for _ in range(4)]
+        ts[which] = _raw(ra, (1, 2, S, D), big, BF16)
+        rc = L.ra_attn_fwd_validate(ts[0], ts[1], ts[2], ctypes.byref(p), ts[3], lse)
+        assert ra.STATUS[rc] == want, (which, ra.STATUS[rc])
+    for which in range(8):  # q, k, v, o, dout, dq, dk, dv
+        ts = [okq() for _ in range(8)]
+        ts[which] = _raw(ra, (1, 2, S, D), big, BF16)
+        rc = L.ra_attn_bwd_validate(ts[0], ts[1], ts[2], ts[3], ts[4], lse,
+                                    ctypes.byref(p), ts[5], ts[6], ts[7])
+        assert ra.STATUS[rc] == want, (which, ra.STATUS[rc])

@@ -65,3 +65,50 @@ def test_head_to_seq_writes_only_its_slice():
                              np.full((P, Sl, H, D), _bits(torch.tensor(7.0).bfloat16())[()],
                                      dtype=np.uint16))
     assert np.array_equal(_bits(dst), ref)
+
+
+@pytest.mark.parametrize("rank", [0, 3, -1])
+def test_permute_multi_qkv_one_launch(rank):
+    """q, k and v of the 32K GQA layer (28 and 4 heads, 4 shards of 8192 tokens) moved by
+    one ra_ulysses_permute_n call: each bit-exact, then back (dir 1) in one call."""
+    say(f"permute multi q/k/v rank={rank}")
+    qs, ks, vs = si.draw_ulysses_sources(1004)
+    P = 4
+    srcs = [to_dev(x, "bf16") for x in (qs, ks, vs)]
+    outs = ra.ulysses_permute_multi(srcs, P, rank, 0)
+    torch.cuda.synchronize()
+    for got, src in zip(outs, (qs, ks, vs)):
+        assert np.array_equal(_bits(got), oracle.seq_to_head(src, P, rank))
+    backs = [torch.zeros_like(s) for s in srcs]
+    if rank >= 0:  # dir 1 writes only the rank's head slice: compare that against the oracle
+        ra.ulysses_permute_multi(outs, P, rank, 1, outs=backs)
+        torch.cuda.synchronize()
+        for got, src, o in zip(backs, (qs, ks, vs), outs):
+            zero = np.zeros(src.shape, dtype=np.uint16)
+            assert np.array_equal(_bits(got), oracle.head_to_seq(_bits(o), P, rank, zero))
+    else:
+        ra.ulysses_permute_multi(outs, P, -1, 1, outs=backs)
+        torch.cuda.synchronize()
+        for got, src in zip(backs, (qs, ks, vs)):
+            assert np.array_equal(_bits(got), src)
+
+
+def test_permute_multi_mixed_rows_and_dtypes():
+    """Pairs with different row sizes or dtypes (pair by pair) and a pair with no tokens."""
+    say("permute multi mixed")
+    rng = np.random.Generator(np.random.PCG64(78))
+    a = si.draw(rng, (2, 37, 6, 64), "bf16")     # 128-byte rows
+    b = si.draw(rng, (2, 37, 4, 96), "bf16")     # 192-byte rows
+    c = si.draw(rng, (2, 37, 2, 32), "f32")      # 128-byte rows, fp32
+    e = np.zeros((2, 0, 4, 64), dtype=np.uint16)
+    srcs = [to_dev(a, "bf16"), to_dev(b, "bf16"), to_dev(c, "f32"), to_dev(e, "bf16")]
+    outs = ra.ulysses_permute_multi(srcs, 2, 1, 0)
+    torch.cuda.synchronize()
+    for got, src in zip(outs[:3], (a, b, c.view(np.uint32))):
+        assert np.array_equal(_bits(got), oracle.seq_to_head(src, 2, 1))
+    assert outs[3].numel() == 0
+    # bf16 and fp32 pairs with 128-byte rows share one launch
+    outs = ra.ulysses_permute_multi([srcs[0], srcs[2]], 2, 0, 0)
+    torch.cuda.synchronize()
+    for got, src in zip(outs, (a, c.view(np.uint32))):
+        assert np.array_equal(_bits(got), oracle.seq_to_head(src, 2, 0))
