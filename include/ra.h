@@ -19,7 +19,9 @@
  *   2^31 (about 8.4 M bf16 elements of token stride); otherwise RA_ERR_SHAPE.  Batch
  *   and head strides are not limited.
  * - The caller owns and allocates every buffer (inputs, outputs, workspace).  The
- *   library allocates nothing, keeps no global state and never synchronises.
+ *   library allocates nothing, keeps no global state and never synchronises; the one
+ *   exception is ra_attn_bwd_noalloc, whose workspace is a fixed array of the loaded
+ *   module (see there).
  * - Work is enqueued on `stream` (a hipStream_t; NULL is the null stream).  Outputs
  *   are valid once the stream's work has completed.  Inputs must stay alive and
  *   unmodified until then.  Calls are thread-safe.
@@ -55,7 +57,8 @@ typedef enum {
   RA_ERR_RANGE = -6,       /* a scalar parameter out of range */
   RA_ERR_UNSUPPORTED = -7, /* valid request this build does not implement */
   RA_ERR_HIP = -8,         /* kernel launch failed */
-  RA_ERR_WORKSPACE = -9    /* workspace missing or smaller than required */
+  RA_ERR_WORKSPACE = -9,   /* workspace missing or smaller than required */
+  RA_ERR_SCRATCH = -10     /* needs more than ra_attn_bwd_noalloc's fixed scratch */
 } ra_status;
 
 typedef enum { RA_F32 = 0, RA_BF16 = 1, RA_FP8_E4M3 = 2 /* OCP e4m3, 1 byte */ } ra_dtype;
@@ -247,6 +250,29 @@ int ra_attn_bwd_validate(const ra_tensor *q, const ra_tensor *k, const ra_tensor
                          const ra_tensor *dv);
 /* Bytes of workspace ra_attn_bwd needs for these shapes (0 if the shapes are invalid). */
 size_t ra_attn_bwd_workspace_size(const ra_tensor *q, const ra_tensor *k, const ra_attn_params *p);
+
+/*
+ * ra_attn_bwd_noalloc -- ra_attn_bwd without a workspace argument and without any
+ * allocation, for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving or training loops, harnesses that forbid hipMalloc).
+ *
+ * Same arguments (minus workspace), checks, results and errors as ra_attn_bwd; it runs
+ * on the CURRENT device (the stream must belong to it).  Its workspace is a fixed
+ * device array inside the library, RA_NOALLOC_SCRATCH_BYTES per GPU, held from library
+ * load until the process ends; a problem whose workspace (ra_attn_bwd_workspace_size)
+ * exceeds it returns RA_ERR_SCRATCH with nothing enqueued.  Every call on one GPU
+ * shares that GPU's array: calls that overlap in time on one GPU (other streams, other
+ * threads) race and give undefined gradients; calls in one stream's order are safe.
+ * No hipMalloc, hipFree or allocating library routine is called (the first call on a
+ * device looks up the array's device address once).
+ */
+#define RA_NOALLOC_SCRATCH_BYTES (32u << 20) /* 32 MiB: B * Hq * Sq up to 8 M query rows */
+int ra_attn_bwd_noalloc(const ra_tensor *q, const ra_tensor *k, const ra_tensor *v,
+                        const ra_tensor *o, const ra_tensor *dout, const ra_tensor *lse,
+                        const ra_attn_params *p, ra_tensor *dq, ra_tensor *dk, ra_tensor *dv,
+                        ra_stream stream);
+/* RA_NOALLOC_SCRATCH_BYTES of the loaded library. */
+size_t ra_noalloc_scratch_bytes(void);
 
 /*
  * ra_attn_bwd_varlen -- ra_attn_bwd over packed documents (the gradients of

@@ -30,6 +30,7 @@ __all__ = [
     "attn_bwd_accum", "attn_bwd_accum_validate", "ring_attn_bwd_chunked",
     "fp8_quantize", "fp8_quantize_validate", "attn_fwd_fp8", "attn_fwd_fp8_validate",
     "ring_attn_fp8_chunked", "ulysses_permute_multi", "ulysses_permute_multi_validate",
+    "attn_bwd_noalloc", "noalloc_scratch_bytes",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libra.so")
@@ -37,7 +38,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libra.so")
 STATUS = {
     0: "RA_OK", -1: "RA_ERR_NULL", -2: "RA_ERR_DTYPE", -3: "RA_ERR_SHAPE", -4: "RA_ERR_STRIDE",
     -5: "RA_ERR_ALIGN", -6: "RA_ERR_RANGE", -7: "RA_ERR_UNSUPPORTED", -8: "RA_ERR_HIP",
-    -9: "RA_ERR_WORKSPACE",
+    -9: "RA_ERR_WORKSPACE", -10: "RA_ERR_SCRATCH",
 }
 RA_F32, RA_BF16, RA_FP8_E4M3 = 0, 1, 2
 MAX_MERGE_PARTS = 64
@@ -106,6 +107,8 @@ def lib() -> ctypes.CDLL:
             "ra_ulysses_permute_n_validate": [i32, T, T, i32, i32, i32],
             "ra_attn_bwd": [T, T, T, T, T, T, PP, T, T, T, vp, sz, vp],
             "ra_attn_bwd_validate": [T, T, T, T, T, T, PP, T, T, T],
+            "ra_attn_bwd_noalloc": [T, T, T, T, T, T, PP, T, T, T, vp],
+            "ra_noalloc_scratch_bytes": [],
             "ra_attn_bwd_varlen": [T, T, T, T, T, T, vp, i32, PP, T, T, T, vp, sz, vp],
             "ra_attn_bwd_varlen_validate": [T, T, T, T, T, T, vp, i32, PP, T, T, T],
             "ra_attn_bwd_workspace_size": [T, T, PP],
@@ -125,6 +128,7 @@ def lib() -> ctypes.CDLL:
             fn.restype = ctypes.c_int
         L.ra_attn_bwd_workspace_size.restype = ctypes.c_size_t
         L.ra_fp8_quantize_workspace_size.restype = ctypes.c_size_t
+        L.ra_noalloc_scratch_bytes.restype = ctypes.c_size_t
         L.ra_status_string.restype = ctypes.c_char_p
         _LIB = L
     return _LIB
@@ -400,6 +404,25 @@ def attn_bwd(q, k, v, o, dout, lse, *, causal=False, num_chunks=1, start_chunk=0
                              ctypes.byref(p), desc(dq), desc(dk), desc(dv),
                              workspace.data_ptr(), workspace.numel(), _stream(q)))
     return dq, dk, dv
+
+
+def attn_bwd_noalloc(q, k, v, o, dout, lse, *, causal=False, num_chunks=1, start_chunk=0,
+                     q_offset=0, kv_offset=0, scale=None, dq=None, dk=None, dv=None):
+    """attn_bwd whose workspace is the library's fixed per-GPU scratch (no allocation by
+    the library; calls that overlap on one GPU race).  Runs on q's device."""
+    p = _params(causal, num_chunks, start_chunk, q_offset, kv_offset, scale)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    with torch.cuda.device(q.device):
+        _check(lib().ra_attn_bwd_noalloc(desc(q), desc(k), desc(v), desc(o), desc(dout),
+                                         desc(lse), ctypes.byref(p), desc(dq), desc(dk),
+                                         desc(dv), _stream(q)))
+    return dq, dk, dv
+
+
+def noalloc_scratch_bytes() -> int:
+    return int(lib().ra_noalloc_scratch_bytes())
 
 
 def attn_bwd_varlen(q, k, v, o, dout, lse, cu_seqlens, *, causal=False, scale=None, dq=None,

@@ -6,6 +6,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "internal.h"
 
@@ -392,6 +393,7 @@ const char *ra_status_string(int status) {
     case RA_ERR_UNSUPPORTED: return "RA_ERR_UNSUPPORTED: valid request not implemented (head dim or dtype)";
     case RA_ERR_HIP: return "RA_ERR_HIP: kernel launch failed";
     case RA_ERR_WORKSPACE: return "RA_ERR_WORKSPACE: workspace missing, misaligned or too small";
+    case RA_ERR_SCRATCH: return "RA_ERR_SCRATCH: the problem needs more workspace than the no-allocation entry point's fixed scratch holds (use ra_attn_bwd with a workspace)";
     default: return "unknown ra_status";
   }
 }
@@ -725,3 +727,51 @@ int ra_attn_bwd_accum(const ra_tensor *q, const ra_tensor *k, const ra_tensor *v
 }
 
 }  // extern "C"
+
+// ---------------------------------------------------------------------------------
+// ra_attn_bwd_noalloc: ra_attn_bwd with its workspace in a fixed device array of this
+// library, for callers that cannot allocate.  The array is a file-scope __device__
+// object, so every GPU the library runs on holds its own copy (RA_NOALLOC_SCRATCH_BYTES)
+// from module load until the process ends.  Host code never passes the array's name to a
+// kernel (on the host it only names a stand-in): the device address of the current GPU's
+// copy is looked up once per device with hipGetSymbolAddress and kept.
+// ---------------------------------------------------------------------------------
+namespace {
+
+__device__ __align__(256) unsigned char scratch[RA_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];  // device address of `scratch` per device, or null
+
+// The current device's copy of `scratch` (looked up on the first call on that device).
+int scratch_of_current_device(void **out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return RA_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void *ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return RA_ERR_HIP;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return RA_OK;
+}
+
+}  // namespace
+
+extern "C" int ra_attn_bwd_noalloc(const ra_tensor *q, const ra_tensor *k, const ra_tensor *v,
+                                   const ra_tensor *o, const ra_tensor *dout,
+                                   const ra_tensor *lse, const ra_attn_params *p, ra_tensor *dq,
+                                   ra_tensor *dk, ra_tensor *dv, ra_stream stream) {
+  RA_TRY(bwd_validate(q, k, v, o, dout, lse, p, dq, dk, dv));
+  const size_t need = bwd_workspace_bytes(q->shape[0], q->shape[1], q->shape[2]);
+  if (need > (size_t)RA_NOALLOC_SCRATCH_BYTES) return RA_ERR_SCRATCH;
+  if (numel(q) == 0 && numel(k) == 0) return RA_OK;
+  void *ws = nullptr;
+  RA_TRY(scratch_of_current_device(&ws));
+  BwdArgs a = bwd_args(q, k, v, o, dout, lse, p, dq, dk, dv, ws);
+  return launch_attn_bwd(a, (int)q->shape[3], p->causal, (hipStream_t)stream);
+}
+
+extern "C" size_t ra_noalloc_scratch_bytes(void) { return (size_t)RA_NOALLOC_SCRATCH_BYTES; }
