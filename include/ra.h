@@ -233,9 +233,9 @@ int ra_ulysses_permute_n_validate(int32_t n, const ra_tensor *srcs, const ra_ten
  * dv = P^T dout, dS = P * (dout v^T - D), dq = scale dS k, dk = scale dS^T q; with
  * grouped heads dk, dv sum over the query heads of a group.
  *
- * q, o, dout [B, Hq, Sq, D]; k, v [B, Hkv, Skv, D]; all RA_BF16 (RA_F32 returns
- * RA_ERR_UNSUPPORTED in this build); lse [B, Hq, Sq] RA_F32 from ra_attn_fwd with
- * the same p.  dq like q, dk and dv like k, same dtype as q.  The ring parameters
+ * q, o, dout [B, Hq, Sq, D]; k, v [B, Hkv, Skv, D]; all RA_BF16 or all RA_F32 (fp32
+ * inputs run fp32 MFMAs throughout); D 64 or 128; lse [B, Hq, Sq] RA_F32 from
+ * ra_attn_fwd with the same p.  dq like q, dk and dv like k, same dtype as q.  The ring parameters
  * fix the order in which dq accumulates over chunks.  Outputs must not overlap the
  * inputs.  workspace: device memory of at least ra_attn_bwd_workspace_size bytes,
  * 256-byte aligned, overwritten.  Deterministic.
@@ -282,7 +282,7 @@ size_t ra_noalloc_scratch_bytes(void);
  * Same sources and reading as ra_attn_fwd_varlen ([P3] section "5. 实战案例", [P4]
  * section "工程实践中的真实收益"; the backward formulas are the textbook softmax
  * gradient, recomputing P from lse).  Tensors, dtypes, workspace and errors as for
- * ra_attn_bwd (bf16, D 64 or 128, workspace from ra_attn_bwd_workspace_size with
+ * ra_attn_bwd (bf16 only, like the packed forward; D 64 or 128, workspace from ra_attn_bwd_workspace_size with
  * num_chunks = 1); q, k, v, o, dout hold the same T tokens; cu_seqlens, n_docs and the
  * params restrictions as for ra_attn_fwd_varlen; o and lse must come from
  * ra_attn_fwd_varlen with the same cu_seqlens.
@@ -310,8 +310,8 @@ int ra_attn_bwd_varlen_validate(const ra_tensor *q, const ra_tensor *k, const ra
  * sums over the chunks; the chunk's dk/dv accumulators travel with the chunk and sum
  * over the devices.  Formulas as for ra_attn_bwd, restricted to the chunk.
  *
- * q, o, dout [B, Hq, Sq, D] RA_BF16; k, v [B, Hkv, Skv, D] RA_BF16, the chunk only;
- * lse [B, Hq, Sq] RA_F32, the merged forward lse of this block; D 64 or 128.
+ * q, o, dout [B, Hq, Sq, D]; k, v [B, Hkv, Skv, D], the chunk only; all RA_BF16 or all
+ * RA_F32; lse [B, Hq, Sq] RA_F32, the merged forward lse of this block; D 64 or 128.
  * dq_acc [B, Hq, Sq, D], dk_acc and dv_acc [B, Hkv, Skv, D]: RA_F32, read and
  * updated in place (acc += contribution); the caller zeroes them before the first
  * step.  p: causal, scale and the global positions q_offset (first query) and

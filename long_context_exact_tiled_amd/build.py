@@ -17,8 +17,8 @@ CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libra.so")
 ROOT = os.path.dirname(PKG)
 
-SOURCES = ["api.hip", "attn_fwd.hip", "attn_fwd_fp8.hip", "attn_bwd.hip", "fp8_quant.hip",
-           "lse_merge.hip", "ulysses_permute.hip"]
+SOURCES = ["api.hip", "attn_fwd.hip", "attn_fwd_fp8.hip", "attn_bwd.hip", "attn_bwd_f32.hip",
+           "fp8_quant.hip", "lse_merge.hip", "ulysses_permute.hip"]
 
 # Packed-fp32 VALU forms are disabled: the compiler may otherwise form them from plain
 # float code.  The host pass does not know this device feature and says so (harmless).

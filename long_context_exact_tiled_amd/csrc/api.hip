@@ -238,7 +238,6 @@ int bwd_validate(const ra_tensor *q, const ra_tensor *k, const ra_tensor *v, con
   RA_TRY(check_grid(k));
   for (const ra_tensor *t : {q, k, v, o, dout, dq, dk, dv}) RA_TRY(check_tile_span(t));
   const int64_t D = q->shape[3];
-  if (q->dtype != RA_BF16) return RA_ERR_UNSUPPORTED;
   if (D != 64 && D != 128) return RA_ERR_UNSUPPORTED;
   return RA_OK;
 }
@@ -249,6 +248,7 @@ int bwd_varlen_validate(const ra_tensor *q, const ra_tensor *k, const ra_tensor 
                         const int32_t *cu_seqlens, int32_t n_docs, const ra_attn_params *p,
                         const ra_tensor *dq, const ra_tensor *dk, const ra_tensor *dv) {
   RA_TRY(bwd_validate(q, k, v, o, dout, lse, p, dq, dk, dv));
+  if (q->dtype != RA_BF16) return RA_ERR_UNSUPPORTED;  // the packed forward is bf16 only
   if (q->shape[2] != k->shape[2]) return RA_ERR_SHAPE;
   if (p->num_chunks != 1 || p->start_chunk != 0 || p->q_offset != 0 || p->kv_offset != 0)
     return RA_ERR_RANGE;
@@ -604,6 +604,8 @@ int ra_attn_bwd(const ra_tensor *q, const ra_tensor *k, const ra_tensor *v, cons
     return RA_ERR_WORKSPACE;
   if (numel(q) == 0 && numel(k) == 0) return RA_OK;
   BwdArgs a = bwd_args(q, k, v, o, dout, lse, p, dq, dk, dv, workspace);
+  if (q->dtype == RA_F32)
+    return launch_attn_bwd_f32(a, (int)q->shape[3], p->causal, false, (hipStream_t)stream);
   return launch_attn_bwd(a, (int)q->shape[3], p->causal, (hipStream_t)stream);
 }
 
@@ -723,6 +725,8 @@ int ra_attn_bwd_accum(const ra_tensor *q, const ra_tensor *k, const ra_tensor *v
   // causal chunk skip: a chunk after the block's last query adds nothing
   if (p->causal && p->kv_offset > p->q_offset + q->shape[2] - 1) return RA_OK;
   BwdArgs a = bwd_args(q, k, v, o, dout, lse, p, dq_acc, dk_acc, dv_acc, workspace);
+  if (q->dtype == RA_F32)
+    return launch_attn_bwd_f32(a, (int)q->shape[3], p->causal, true, (hipStream_t)stream);
   return launch_attn_bwd_accum(a, (int)q->shape[3], p->causal, (hipStream_t)stream);
 }
 
@@ -771,6 +775,8 @@ extern "C" int ra_attn_bwd_noalloc(const ra_tensor *q, const ra_tensor *k, const
   void *ws = nullptr;
   RA_TRY(scratch_of_current_device(&ws));
   BwdArgs a = bwd_args(q, k, v, o, dout, lse, p, dq, dk, dv, ws);
+  if (q->dtype == RA_F32)
+    return launch_attn_bwd_f32(a, (int)q->shape[3], p->causal, false, (hipStream_t)stream);
   return launch_attn_bwd(a, (int)q->shape[3], p->causal, (hipStream_t)stream);
 }
 

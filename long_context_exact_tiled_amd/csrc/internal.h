@@ -133,5 +133,7 @@ int launch_attn_bwd(const BwdArgs &a, int D, int causal, hipStream_t stream);
 int launch_attn_bwd_varlen(const BwdArgs &a, int D, int causal, hipStream_t stream);
 // One ring step: dq, dk, dv point at fp32 accumulators that receive += contributions.
 int launch_attn_bwd_accum(const BwdArgs &a, int D, int causal, hipStream_t stream);
+// fp32 inputs: dq, dk, dv are fp32; acc = true adds to them (the ring step).
+int launch_attn_bwd_f32(const BwdArgs &a, int D, int causal, bool acc, hipStream_t stream);
 
 }  // namespace ra

@@ -120,6 +120,10 @@ def test_bwd_varlen_validation(ra):
 
     assert f() == "RA_OK" and f(causal=True) == "RA_OK"
     assert f(k=_t((1, 2, 32, 128)), v=_t((1, 2, 32, 128))) == "RA_ERR_SHAPE"
+    # the packed forward is bf16 only, so is its backward
+    fo = lambda t: t.float()
+    assert ra.STATUS[ra.attn_bwd_varlen_validate(fo(q), fo(k), fo(v), fo(o), fo(do), lse, cu,
+                                                 fo(q), fo(k), fo(v))] == "RA_ERR_UNSUPPORTED"
 
 
 def test_fwd_rejects_before_launch(ra):
@@ -195,7 +199,10 @@ def test_bwd_validation(ra):
     assert val(q, k, v, o, do, lse, dq, dk, dv.float()) == "RA_ERR_DTYPE"
     assert val(q, k, v, o, do, lse, dq, _t((1, 2, 65, 128)), dv) == "RA_ERR_SHAPE"
     f = lambda t: t.float()
-    assert val(f(q), f(k), f(v), f(o), f(do), lse, f(dq), f(dk), f(dv)) == "RA_ERR_UNSUPPORTED"
+    assert val(f(q), f(k), f(v), f(o), f(do), lse, f(dq), f(dk), f(dv)) == "RA_OK"  # fp32
+    assert val(f(q), f(k), f(v), f(o), f(do), lse, dq, f(dk), f(dv)) == "RA_ERR_DTYPE"
+    assert val(f(q)[..., :64], f(k)[..., :64], f(v)[..., :64], f(o)[..., :64], f(do)[..., :64],
+               lse, f(dq)[..., :64], f(dk)[..., :64], f(dv)[..., :64]) == "RA_OK"  # D = 64
     assert ra.attn_bwd_workspace_size(q, k) >= 4 * 64 * 4
     assert ra.attn_bwd_workspace_size(q, _t((1, 3, 64, 128))) == 0
 
