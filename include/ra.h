@@ -336,8 +336,8 @@ int ra_attn_bwd_accum_validate(const ra_tensor *q, const ra_tensor *k, const ra_
  * ra_fp8_quantize -- bf16 -> e4m3 codes with one fp32 scale per (batch, head), the
  * input of ra_attn_fwd_fp8.
  *
- * [P4] section "FlashAttention 如何破局？不只是融合内核": FlashAttention-3 supports the
- * FP8 data type, halving key/value traffic.  The scaling rule is a reading (the pages
+ * [P4] section "那么，FlashAttention-2 和 -3 又改进了什么？": FlashAttention-3 supports
+ * the FP8 data type, halving key/value traffic.  The scaling rule is a reading (the pages
  * give none): with a = max |x| over the head, code = e4m3(clamp(x * (448 / a), -448,
  * 448)), an fp32 multiply and a round-to-nearest-even conversion to OCP e4m3;
  * descale = a / 448 (fp32); an all-zero head gets descale 1 and zero codes.  The value
@@ -363,8 +363,9 @@ size_t ra_fp8_quantize_workspace_size(const ra_tensor *src);
  * dequantized q, k, v (value = decode(code) * descale of its (batch, head)), the same
  * ring walk, causal mask and outputs.
  *
- * [P4] section "FlashAttention 如何破局？不只是融合内核" (FlashAttention-3's FP8 support;
- * tiling and the online softmax); ring and merge sources as ra_attn_fwd.  The attention
+ * [P4] sections "那么，FlashAttention-2 和 -3 又改进了什么？" (FlashAttention-3's FP8
+ * support) and "FlashAttention 如何破局？不只是融合内核" (tiling and the online
+ * softmax); ring and merge sources as ra_attn_fwd.  The attention
  * weights are rounded to e4m3 for the P V product (after scaling by 2^6); the row sums
  * and lse use the unrounded fp32 weights.
  *

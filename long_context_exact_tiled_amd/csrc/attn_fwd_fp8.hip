@@ -3,8 +3,9 @@
 //
 // Sources (page title, host):
 //   [P4] "ms-swift集成FlashAttention 2/3，长文本训练更高效" (maplevalley.com.cn), section
-//        "FlashAttention 如何破局？不只是融合内核": FlashAttention-3 supports the FP8 data
-//        type, halving key/value traffic; tiling and the online softmax as in attn_fwd.
+//        "那么，FlashAttention-2 和 -3 又改进了什么？": FlashAttention-3 supports the FP8
+//        data type, halving key/value traffic; section "FlashAttention 如何破局？不只是
+//        融合内核": tiling and the online softmax, as in attn_fwd.
 //   [P2] "Ulysses与Ring-Attention序列并行技术详解" (cnvsn.com): the ring_attention_forward
 //        listing (chunks visited in turn, log-space accumulation).
 //

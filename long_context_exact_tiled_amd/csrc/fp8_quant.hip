@@ -2,8 +2,8 @@
 // optionally transposed to [B, H, D, S_pad] (the V^T layout the FP8 attention reads).
 //
 // [P4] "ms-swift集成FlashAttention 2/3，长文本训练更高效" (maplevalley.com.cn), section
-// "FlashAttention 如何破局？不只是融合内核": FlashAttention-3 supports the FP8 data type,
-// halving the key/value traffic.  The scaling rule is a reading (the pages give none):
+// "那么，FlashAttention-2 和 -3 又改进了什么？": FlashAttention-3 supports the FP8 data
+// type, halving the key/value traffic.  The scaling rule is a reading (the pages give none):
 // with a = max |x| over the head, codes = e4m3(clamp(x * (448 / a), -448, 448)) with an
 // fp32 multiply and round-to-nearest-even conversion, descale = a / 448 (an all-zero
 // head: 1, 1); the value of a code is decode(code) * descale.

@@ -21,7 +21,9 @@ give, in the order they give them.  Sources (page title, then the section):
   with the step's output).
 * [P4] "ms-swift集成FlashAttention 2/3，长文本训练更高效" (maplevalley.com.cn),
   sections "FlashAttention 如何破局？不只是融合内核" (tiling with an online
-  running max and normaliser; result identical to full attention) and
+  running max and normaliser, only the output written back), "那么，
+  FlashAttention-2 和 -3 又改进了什么？" (the speed-ups keep the results
+  numerically identical to plain attention) and
   "Ulysses：强互联下的高速通路" (sequence shards [B, S_local] x N, an
   all-to-all before attention and one after that restores the order), and
   "工程实践中的真实收益" (packing mixed sequences into one).

@@ -85,8 +85,8 @@ def full_attention(q, k, v, *, causal: bool = False, scale: Optional[float] = No
     """Full softmax(scale * Q K^T) V over every key at once -> (o, lse), fp64.
 
     The definition the method must reproduce exactly: [P2] ``ulysses_attention_forward``
-    (softmax over the whole key axis, then multiply by V); [P4] "FlashAttention 如何破局"
-    states the tiled computation returns this same result.  Rows are processed in
+    (softmax over the whole key axis, then multiply by V); [P4] "那么，FlashAttention-2 和
+    -3 又改进了什么？" states that the tiled kernels keep this same result.  Rows are processed in
     blocks of ``row_block`` only to bound memory; each row still gets its whole softmax.
     """
     q, k, v = _as64(q), _as64(k), _as64(v)

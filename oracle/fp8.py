@@ -4,7 +4,7 @@ See ``oracle/__init__.py`` for who may import it.
 
 The pages say only that FlashAttention-3 supports the FP8 data type, which halves
 the traffic of the key/value cache ([P4] "ms-swift集成FlashAttention 2/3，长文本训练更高效",
-section "FlashAttention 如何破局？不只是融合内核", its FlashAttention-3 list), and that
+section "那么，FlashAttention-2 和 -3 又改进了什么？", its FlashAttention-3 list), and that
 sequence parallelism combines with FP8 training ([P2] "Ulysses与Ring-Attention序列并行技术详解",
 the list of engineering considerations near its end).  Everything else here is a
 reading, stated once:
