@@ -76,6 +76,12 @@ __device__ __forceinline__ int swz(int r) {
   return (r / (256 / RB)) % (RB / 16);
 }
 
+// Lane index, formed afresh where it is used: values derived from it that are only
+// needed before or after the tile loop then hold no register across the loop.
+__device__ __forceinline__ int lane_index() {
+  return (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+}
+
 template <int D, int KN, int NW_>
 struct Fp8Tile {
   static constexpr int NW = NW_;
@@ -86,30 +92,42 @@ struct Fp8Tile {
   static constexpr int VBPW = V_BYTES / 1024 / NW;
   static_assert(K_BYTES % (1024 * NW) == 0 && V_BYTES % (1024 * NW) == 0,
                 "tiles split evenly into 1-KiB direct loads per wave");
+  // rows between one lane's successive K (V^T) direct loads: a multiple of the swizzle's
+  // 16-row period, so every load of a lane has the same swizzled column
+  static constexpr int KRS = NW * 1024 / D;
+  static constexpr int VRS = NW * 1024 / KN;
+  static_assert(KRS % 16 == 0 && VRS % 16 == 0, "direct loads keep their swizzled column");
   static constexpr int KM = D / 64;   // 64-dim slices of a K row
   static constexpr int NG = KN / 64;   // 64-key groups of a V^T row
   struct Lane {
-    int k_row[KBPW], k_col[KBPW];  // tile row and byte column of this lane's 16 bytes
-    int v_row[VBPW], v_col[VBPW];
+    int k_off, v_off;  // byte offsets of this lane's 16 bytes in its first K and V^T
+                       // direct loads from the tile's first key (K row-major, V^T rows
+                       // of keys); its i-th load is KRS i (VRS i) rows further on
     // operand read addresses in slot 0: K chunk 4m + 2h + e of row r, V^T chunk
     // 4g + 2h + e of row r (swizzled); block and slot offsets are immediates
     uint32_t ka[KM][2], va[NG][2];
   };
 
-  __device__ static void setup(Lane &L, int lane, int wave, uint32_t smem0) {
-#pragma unroll
-    for (int i = 0; i < KBPW; ++i) {
-      const int byte = (wave + NW * i) * 1024 + 16 * lane;
-      const int r = byte / D, p = (byte % D) / 16;
-      L.k_row[i] = r;
-      L.k_col[i] = 16 * (p ^ swz<D>(r));
-    }
-#pragma unroll
-    for (int i = 0; i < VBPW; ++i) {
-      const int byte = (wave + NW * i) * 1024 + 16 * lane;
-      const int r = byte / KN, p = (byte % KN) / 16;
-      L.v_row[i] = r;
-      L.v_col[i] = 16 * (p ^ swz<KN>(r));
+  // tile row and (swizzled) byte column of the 16 bytes lane `lane` of wave `wave` moves
+  // in its i-th K or V^T direct load
+  __device__ static void k_piece(int lane, int wave, int i, int &r, int &col) {
+    const int byte = (wave + NW * i) * 1024 + 16 * lane;
+    r = byte / D;
+    col = 16 * (((byte % D) / 16) ^ swz<D>(r));
+  }
+  __device__ static void v_piece(int lane, int wave, int i, int &r, int &col) {
+    const int byte = (wave + NW * i) * 1024 + 16 * lane;
+    r = byte / KN;
+    col = 16 * (((byte % KN) / 16) ^ swz<KN>(r));
+  }
+
+  __device__ static void setup(Lane &L, const FwdArgs &f, int lane, int wave, uint32_t smem0) {
+    {
+      int r, col;
+      k_piece(lane, wave, 0, r, col);
+      L.k_off = (int)(r * f.k_ss) + col;
+      v_piece(lane, wave, 0, r, col);
+      L.v_off = (int)(r * f.v_ss) + col;
     }
     const int r = lane & 31, h = lane >> 5;
 #pragma unroll
@@ -125,21 +143,42 @@ struct Fp8Tile {
 
   // Direct loads of the tile at key kb into the LDS slot at byte offset `slot`.  Rows
   // past the last key read the last key; V^T columns past the stored row read its last
-  // 16 bytes (both are masked: their weights are exactly 0).
+  // 16 bytes (both are masked: their weights are exactly 0).  Away from the end of the
+  // keys the lane offsets are the precomputed ones and only the scalar base moves.
   __device__ static void load(const Lane &L, const Fp8Args &a, const uint8_t *kbase,
                               const uint8_t *vbase, int kb, uint32_t slot, int wave) {
     const FwdArgs &f = a.f;
+    if (kb + KN <= f.Skv && kb + KN <= a.vt_cols) {
+      const uint8_t *kt = kbase + (int64_t)kb * f.k_ss;
+      const uint8_t *vt = vbase + kb;
+#pragma unroll
+      for (int i = 0; i < KBPW; ++i)
+        dma_b128(kt + (int64_t)(KRS * i) * f.k_ss, L.k_off,
+                 slot + (uint32_t)__builtin_amdgcn_readfirstlane(wave + NW * i) * 1024);
+#pragma unroll
+      for (int i = 0; i < VBPW; ++i)
+        dma_b128(vt + (int64_t)(VRS * i) * f.v_ss, L.v_off,
+                 slot + K_BYTES + (uint32_t)__builtin_amdgcn_readfirstlane(wave + NW * i) * 1024);
+      return;
+    }
+    // the last tile: clamp rows and columns.  These offsets are taken from the head's
+    // first key: the load zero-extends its 32-bit lane offset, and a clamped column
+    // can lie before the tile's own first key (a tile that starts in the last 16
+    // columns of a padded V^T row).
+    const int lane = lane_index();
 #pragma unroll
     for (int i = 0; i < KBPW; ++i) {
-      const uint32_t blk = (uint32_t)__builtin_amdgcn_readfirstlane(wave + NW * i);
-      const int row = min(kb + L.k_row[i], f.Skv - 1);
-      dma_b128(kbase, (int)(row * f.k_ss) + L.k_col[i], slot + blk * 1024);
+      int r, col;
+      k_piece(lane, wave, i, r, col);
+      const int off = (int)(min(kb + r, f.Skv - 1) * f.k_ss) + col;
+      dma_b128(kbase, off, slot + (uint32_t)__builtin_amdgcn_readfirstlane(wave + NW * i) * 1024);
     }
 #pragma unroll
     for (int i = 0; i < VBPW; ++i) {
-      const uint32_t blk = (uint32_t)__builtin_amdgcn_readfirstlane(wave + NW * i);
-      const int col = min(kb + L.v_col[i], a.vt_cols - 16);
-      dma_b128(vbase, (int)(L.v_row[i] * f.v_ss) + col, slot + K_BYTES + blk * 1024);
+      int r, col;
+      v_piece(lane, wave, i, r, col);
+      const int off = (int)(r * f.v_ss) + min(kb + col, a.vt_cols - 16);
+      dma_b128(vbase, off, slot + K_BYTES + (uint32_t)__builtin_amdgcn_readfirstlane(wave + NW * i) * 1024);
     }
   }
 
@@ -225,8 +264,6 @@ attn_fwd_fp8_kernel(Fp8Args a) {
   const uint8_t *kbase = (const uint8_t *)f.k + b * f.k_sb + hk * f.k_sh;
   const uint8_t *vbase = (const uint8_t *)f.v + b * f.v_sb + hk * f.v_sh;
 
-  const int qrow = q0 + 32 * wave + r32;
-  const int64_t qpos = f.q_offset + qrow;
   const int64_t wpos_first = f.q_offset + q0 + 32 * wave_u;
   const int64_t wpos_last = wpos_first + 31;
   const bool wave_active = (q0 + 32 * wave_u) < f.Sq;
@@ -241,12 +278,12 @@ attn_fwd_fp8_kernel(Fp8Args a) {
 
   const uint32_t smem0 = lds_offset(smem);
   typename T::Lane L;
-  T::setup(L, lane, wave, smem0);
+  T::setup(L, f, lane, wave, smem0);
 
   // Q as the B operand: head-dim slice m holds bytes 64m + 32h .. +32 of this row.
   i32x8 qf[D / 64];
   {
-    const uint8_t *qr = qbase + (int64_t)min(qrow, f.Sq - 1) * f.q_ss;
+    const uint8_t *qr = qbase + (int64_t)min(q0 + 32 * wave + r32, f.Sq - 1) * f.q_ss;
 #pragma unroll
     for (int m = 0; m < D / 64; ++m)
       qf[m] = cat8(*(const u32x4 *)(qr + 64 * m + 32 * h),
@@ -262,7 +299,7 @@ attn_fwd_fp8_kernel(Fp8Args a) {
   const int64_t vis_lim = f.q_offset + qlast - f.kv_offset + 1;
   int t = -1, kb = 0, kend = 0, cend = 0;
   ring_next_fp8<KN>(f, CAUSAL, vis_lim, t, kb, kend, cend);
-  if (t < f.num_chunks) T::load(L, a, kbase, vbase, kb, smem0, wave);
+  if (t < f.num_chunks) T::load(L, a, kbase, vbase, kb, smem0, wave_u);
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): Q and the first tile have landed
   __syncthreads();
 
@@ -275,7 +312,7 @@ attn_fwd_fp8_kernel(Fp8Args a) {
     const int kb_cur = kb, cend_cur = cend;
     ring_next_fp8<KN>(f, CAUSAL, vis_lim, t, kb, kend, cend);
     const bool has_next = t < f.num_chunks;
-    if (has_next) T::load(L, a, kbase, vbase, kb, smem0 + (CUR ^ 1) * T::BUF, wave);
+    if (has_next) T::load(L, a, kbase, vbase, kb, smem0 + (CUR ^ 1) * T::BUF, wave_u);
 
     const int64_t kpos0 = f.kv_offset + kb_cur;
     if (wave_active && !(CAUSAL && kpos0 > wpos_last)) {
@@ -291,12 +328,17 @@ attn_fwd_fp8_kernel(Fp8Args a) {
       const int kvalid = min(KN, cend_cur - kb_cur);
       const bool need_mask = (kvalid < KN) || (CAUSAL && kpos0 + kvalid - 1 > wpos_first);
       if (need_mask) {
-        int lim = kvalid;  // keys kk < lim are visible to this lane's row
+        // keys kk < lim are visible to this lane's row.  Row 32 wave + r sees
+        // wpos_first + r - kpos0 + 1 keys of the tile; clamping the wave's term to
+        // [-32, KN] changes no row's min(max(., 0), kvalid).
+        const int ln = lane_index();
+        int lim = kvalid;
         if (CAUSAL) {
-          const int64_t vis = qpos - kpos0 + 1;
-          lim = vis < (int64_t)lim ? (vis > 0 ? (int)vis : 0) : lim;
+          const int64_t w0 = wpos_first - kpos0 + 1;
+          const int vis = (int)(w0 < -32 ? -32 : (w0 > KN ? KN : w0)) + (ln & 31);
+          lim = min(lim, max(vis, 0));
         }
-        lim -= 4 * h;
+        lim -= 4 * (ln >> 5);
 #pragma unroll
         for (int mt = 0; mt < NMT; ++mt)
 #pragma unroll
@@ -374,8 +416,11 @@ attn_fwd_fp8_kernel(Fp8Args a) {
 
   const float l_tot = halves_sum(l_run);
   const float inv = l_tot > 0.f ? vdesc / l_tot : 0.f;
+  const int ln = lane_index();
+  const int qrow = q0 + 32 * wave_u + (ln & 31);
   if (qrow < f.Sq) {
-    if (h == 0) {
+    const int he = ln >> 5;
+    if (he == 0) {
       const float lse = l_tot > 0.f ? (m_run - kP8Shift + __log2f(l_tot)) * kLn2 : -INFINITY;
       f.lse[b * f.l_sb + hq * f.l_sh + qrow] = lse;
     }
@@ -384,7 +429,7 @@ attn_fwd_fp8_kernel(Fp8Args a) {
     for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
-        const int d = 32 * dt + 8 * g4 + 4 * h;
+        const int d = 32 * dt + 8 * g4 + 4 * he;
         const float x0 = o[dt][4 * g4 + 0] * inv, x1 = o[dt][4 * g4 + 1] * inv;
         const float x2 = o[dt][4 * g4 + 2] * inv, x3 = o[dt][4 * g4 + 3] * inv;
         if (f.o_is_f32) {
