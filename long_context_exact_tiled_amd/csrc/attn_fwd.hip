@@ -193,7 +193,7 @@ struct Bf16DirectPath {
   }
 
   __device__ static float exp_pack(const f32x16 (&s)[NMT], float c, float mneg, PFrag &pf) {
-    float acc0 = 0.f, acc1 = 0.f;
+    float acc0 = -0.f, acc1 = -0.f;  // x + -0 is x: the first additions fold away
 #pragma unroll
     for (int kstep = 0; kstep < KN / 16; ++kstep) {
       const int mt = kstep >> 1, s2 = kstep & 1;
@@ -300,7 +300,7 @@ struct F32Path {
   }
 
   __device__ static float exp_pack(const f32x16 (&s)[2], float c, float mneg, PFrag &pf) {
-    float acc = 0.f;
+    float acc = -0.f;
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
@@ -429,7 +429,7 @@ attn_fwd_kernel(FwdArgs a) {
           s[mt][i] = kk < lim ? s[mt][i] : -INFINITY;
         }
     }
-    float mx = fmaxf(fmaxf(s[0][0], s[0][1]), s[0][2]);
+    float mx = fmaxf(max_finite(s[0][0], s[0][1]), s[0][2]);
 #pragma unroll
     for (int i = 3; i < 15; i += 2) mx = fmaxf(fmaxf(mx, s[0][i]), s[0][i + 1]);
     mx = fmaxf(mx, s[0][15]);
@@ -667,7 +667,7 @@ attn_fwd_direct_kernel(FwdArgs a) {
             s[mt][i] = (kk < lim && (!VARLEN || kk >= lo)) ? s[mt][i] : -INFINITY;
           }
       }
-      float mx = fmaxf(fmaxf(s[0][0], s[0][1]), s[0][2]);
+      float mx = fmaxf(max_finite(s[0][0], s[0][1]), s[0][2]);
 #pragma unroll
       for (int i = 3; i < 15; i += 2) mx = fmaxf(fmaxf(mx, s[0][i]), s[0][i + 1]);
       mx = fmaxf(mx, s[0][15]);

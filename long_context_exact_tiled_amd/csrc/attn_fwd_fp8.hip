@@ -347,7 +347,7 @@ attn_fwd_fp8_kernel(Fp8Args a) {
             s[mt][i] = kk < lim ? s[mt][i] : -INFINITY;
           }
       }
-      float mx = fmaxf(fmaxf(s[0][0], s[0][1]), s[0][2]);
+      float mx = fmaxf(max_finite(s[0][0], s[0][1]), s[0][2]);
 #pragma unroll
       for (int i = 3; i < 15; i += 2) mx = fmaxf(fmaxf(mx, s[0][i]), s[0][i + 1]);
       mx = fmaxf(mx, s[0][15]);
@@ -372,7 +372,7 @@ attn_fwd_fp8_kernel(Fp8Args a) {
       // Dwords of block mt go straight into the P'^T operand of its 64-key group g = mt/2:
       // element 2 q4 + (mt & 1) holds the keys of registers 4 q4 .. 4 q4 + 3.
       i32x8 pf[NG];
-      float acc0 = 0.f, acc1 = 0.f;
+      float acc0 = -0.f, acc1 = -0.f;  // x + -0 is x: the first additions fold away
 #pragma unroll
       for (int mt = 0; mt < NMT; ++mt)
 #pragma unroll
@@ -381,7 +381,7 @@ attn_fwd_fp8_kernel(Fp8Args a) {
           const float p1 = fast_exp2(fmaf(s[mt][4 * q4 + 1], c, mneg));
           const float p2 = fast_exp2(fmaf(s[mt][4 * q4 + 2], c, mneg));
           const float p3 = fast_exp2(fmaf(s[mt][4 * q4 + 3], c, mneg));
-          int w = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, __float_as_int(s[mt][4 * q4 + 3]),
+          int w = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, pf[mt >> 1][2 * q4 + (mt & 1)],
                                                   false);
           pf[mt >> 1][2 * q4 + (mt & 1)] = __builtin_amdgcn_cvt_pk_fp8_f32(p2, p3, w, true);
           acc0 += p0 + p1;

@@ -39,9 +39,16 @@ __device__ __forceinline__ f32x16 mfma_f32(float a, float b, const f32x16 &c) {
 // with the same register as both operands returns {value of lane l%32, value of lane
 // 32 + l%32} in every lane, so max / sum of the pair is the same in both halves (and the
 // sum is formed in the same order in both halves, so the halves agree bitwise).
+// max(a, b) for a, b below +inf (scores are finite, or -inf where masked): the median of
+// (a, b, FLT_MAX), one instruction that needs no quieting of its inputs (fmaxf of values
+// the compiler cannot prove quiet, such as MFMA results, costs three)
+__device__ __forceinline__ float max_finite(float a, float b) {
+  return __builtin_amdgcn_fmed3f(a, b, 3.40282347e38f);
+}
+
 __device__ __forceinline__ float halves_max(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  return max_finite(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
 __device__ __forceinline__ float halves_sum(float x) {
