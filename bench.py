@@ -504,16 +504,18 @@ def main():
     if moved:
         extra["permute_ms_per_step"] = float(np.mean(side_ms))
         extra["permute_GBps"] = moved / (np.mean(side_ms) * 1e-3) / 1e9
-        # cold-cache rate: a 1 GiB write evicts the 256 MB Infinity Cache before each pass
-        scratch = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        # cold-cache rate: reading 1 GiB evicts the 256 MB Infinity Cache (and the L2s)
+        # before each pass.  The flush reads: a flush by writing would leave the caches
+        # full of dirty lines whose write-back then runs inside the timed pass.
+        scratch = torch.zeros(1 << 27, dtype=torch.int64, device=dev)
         cold = []
         for _ in range(5):
-            scratch.zero_()
+            scratch.sum()
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record(stream)
             s["pre"]()
             e1.record(stream)
-            scratch.zero_()
+            scratch.sum()
             e2, e3 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e2.record(stream)
             s["post"]()
