@@ -29,6 +29,8 @@
 // storing bf16 results.
 #include <math.h>
 
+#include <type_traits>
+
 #include "common.h"
 #include "internal.h"
 
@@ -299,16 +301,28 @@ bwd_dq_kernel(BwdArgs a, int num_q_tiles) {
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
   __syncthreads();
 
-  int cur = 0;
-  while (t < a.num_chunks) {
+  // One key tile from LDS slot CUR (the next tile's loads go to the other slot); the
+  // loop alternates the slots, so that slot, block and K-versus-V offsets are immediates
+  // of the LDS reads and each lane forms its XOR-swizzled read addresses once per tile.
+  auto tile = [&](auto cur_c) -> bool {
+    constexpr uint32_t CUR = decltype(cur_c)::value;
+    constexpr uint32_t SLOT = CUR * 2 * Tile::BYTES;
     const int kb_cur = kb, cend_cur = cend;
     ring_next_bwd<KT>(a, CAUSAL, vis_lim, t, kb, kend, cend);
-    if (t < a.num_chunks) load_kv(kb, smem0 + (cur ^ 1) * 2 * Tile::BYTES);
+    const bool has_next = t < a.num_chunks;
+    if (has_next) load_kv(kb, smem0 + (CUR ^ 1) * 2 * Tile::BYTES);
     const int64_t kpos0 = a.kv_offset + kb_cur;
     const bool doc_skip =
         VARLEN && (kb_cur + KT <= w_ds_first || (!CAUSAL && kb_cur >= w_de_last));
     if (wave_active && !(CAUSAL && kpos0 > wpos_last) && !doc_skip) {
-      const uint32_t kt = smem0 + cur * 2 * Tile::BYTES, vt = kt + Tile::BYTES;
+      // row reads: smem0 + (kpart ^ 32 ks); transposed reads: smem0 + (tp ^ 64 dt).  The
+      // empty asm keeps them per tile (hoisted out of the loop they would hold 16
+      // registers for its whole length).
+      uint32_t kp = kpart, t0 = tp0, t1 = tp1;
+      asm volatile("" : "+v"(kp), "+v"(t0), "+v"(t1));
+      uint32_t ra[D / 16];
+#pragma unroll
+      for (int ks = 0; ks < D / 16; ++ks) ra[ks] = smem0 + (kp ^ (uint32_t)(32 * ks));
       const int kvalid = min(KT, cend_cur - kb_cur);
       const bool need_mask =
           (kvalid < KT) || (CAUSAL && kpos0 + kvalid - 1 > wpos_first) ||
@@ -323,12 +337,11 @@ bwd_dq_kernel(BwdArgs a, int num_q_tiles) {
 #pragma unroll RA_BWD_DQ_UNROLL
       for (int mt = 0; mt < KT / 32; ++mt) {
         f32x16 s = f32x16{}, dp = f32x16{};
-        const uint32_t ko = kt + (uint32_t)(mt * 32 * Tile::RB);
-        const uint32_t vo = vt + (uint32_t)(mt * 32 * Tile::RB);
+        const uint32_t ko = SLOT + (uint32_t)(mt * 32 * Tile::RB);
 #pragma unroll
         for (int ks = 0; ks < D / 16; ++ks) {
-          s = mfma_bf16(as_bf16x8(Tile::row_read(ko, kpart, ks)), qf[ks], s);
-          dp = mfma_bf16(as_bf16x8(Tile::row_read(vo, kpart, ks)), df[ks], dp);
+          s = mfma_bf16(as_bf16x8(lds_read_b128(ra[ks] + ko)), qf[ks], s);
+          dp = mfma_bf16(as_bf16x8(lds_read_b128(ra[ks] + ko + Tile::BYTES)), df[ks], dp);
         }
         // P^T and dS^T (lane: one query row, 16 of the 32 keys of this half); the element
         // mask only where this 32-key half needs it (a wave-uniform branch)
@@ -360,14 +373,24 @@ bwd_dq_kernel(BwdArgs a, int num_q_tiles) {
         for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
           for (int dt = 0; dt < D / 32; ++dt) {
-            const u32x4 kf = Tile::tr_read(kt, tp0, tp1, 32 * mt + 16 * s2, dt);
+            const uint32_t off = SLOT + (uint32_t)((32 * mt + 16 * s2) * Tile::RB);
+            const uint32_t x = (uint32_t)(64 * dt);
+            const s16x4 lo = lds_read_tr16_b64(smem0 + (t0 ^ x) + off);
+            const s16x4 hi = lds_read_tr16_b64(smem0 + (t1 ^ x) + off);
+            const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+            const u32x4 kf = u32x4{l2[0], l2[1], h2[0], h2[1]};
             dq[dt] = mfma_bf16(as_bf16x8(kf), as_bf16x8(dsf[s2]), dq[dt]);
           }
       }
     }
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): next tile landed
     __syncthreads();
-    cur ^= 1;
+    return has_next;
+  };
+  if (t < a.num_chunks) {
+    while (tile(std::integral_constant<uint32_t, 0>{}) &&
+           tile(std::integral_constant<uint32_t, 1>{})) {
+    }
   }
 
   if (qrow < a.Sq) {
