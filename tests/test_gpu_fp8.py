@@ -124,7 +124,10 @@ CASES = [
     (1, 2, 2, 300, 300, 128, True, 1, 0, 0, 0),
     (2, 4, 2, 200, 330, 64, False, 3, 1, 0, 0),
     (1, 4, 1, 256, 256, 128, True, 4, 1, 0, 0),
+    # chunks of 130: the last tile of chunk 2 starts at key 388, inside the last 16
+    # columns of the padded V^T rows (400), so its clamped columns lie before the tile
     (1, 2, 2, 130, 390, 128, True, 3, 2, 260, 0),
+    (1, 2, 1, 70, 390, 64, False, 3, 0, 0, 0),
     (1, 7, 1, 333, 333, 128, True, 1, 0, 0, 0),
     (1, 2, 2, 200, 200, 128, True, 1, 0, 0, 100),   # rows with no visible key
     (1, 2, 2, 1, 1, 64, True, 1, 0, 0, 0),
