@@ -375,6 +375,9 @@ size_t ra_fp8_quantize_workspace_size(const ra_tensor *src);
  *     hold finite codes (ra_fp8_quantize writes 0 there)
  * q_descale [B, Hq], k_descale and v_descale [B, Hkv]: RA_F32, finite and > 0
  * p   as for ra_attn_fwd;  o [B, Hq, Sq, D] RA_BF16 or RA_F32;  lse [B, Hq, Sq] RA_F32
+ *     With num_chunks > 1 the chunk length Skv / num_chunks must be a multiple of 16
+ *     keys (RA_ERR_ALIGN otherwise): key tiles then start on 16-byte boundaries of vt's
+ *     rows, as a chunk-by-chunk call's vt view must (its data pointer is 16-byte aligned).
  * Errors as for ra_attn_fwd; RA_ERR_SHAPE also when one head's byte offsets exceed
  * 2^31.  Outputs must not overlap the inputs.
  */

@@ -297,6 +297,10 @@ int fp8_validate(const ra_tensor *q, const ra_tensor *k, const ra_tensor *vt,
   if (vt->shape[0] != B || vt->shape[1] != Hkv || vt->shape[2] != D || vt->shape[3] != S_pad)
     return RA_ERR_SHAPE;
   RA_TRY(check_params(p, Skv));
+  // key tiles start at chunk starts plus multiples of 64: 16-key chunks keep every V^T
+  // tile load on a 16-byte boundary of its row, so the last tile's clamped columns
+  // never hold a visible key
+  if (p->num_chunks > 1 && (Skv / p->num_chunks) % 16 != 0) return RA_ERR_ALIGN;
   RA_TRY(check_tensor(o, 4, 16, true));
   if (o->dtype != RA_BF16 && o->dtype != RA_F32) return RA_ERR_DTYPE;
   if (!same_shape(o, q)) return RA_ERR_SHAPE;

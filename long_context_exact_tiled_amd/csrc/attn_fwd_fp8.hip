@@ -142,9 +142,11 @@ struct Fp8Tile {
   }
 
   // Direct loads of the tile at key kb into the LDS slot at byte offset `slot`.  Rows
-  // past the last key read the last key; V^T columns past the stored row read its last
-  // 16 bytes (both are masked: their weights are exactly 0).  Away from the end of the
-  // keys the lane offsets are the precomputed ones and only the scalar base moves.
+  // past the last key read the last key; V^T 16-byte columns past the stored row read
+  // its last 16 bytes.  Both are masked (their weights are exactly 0): kb is a multiple
+  // of 16 (chunks of 16 keys, checked on the host), so a column that starts before the
+  // last key lies wholly inside the padded row and is never clamped.  Away from the end
+  // of the keys the lane offsets are the precomputed ones and only the scalar base moves.
   __device__ static void load(const Lane &L, const Fp8Args &a, const uint8_t *kbase,
                               const uint8_t *vbase, int kb, uint32_t slot, int wave) {
     const FwdArgs &f = a.f;

@@ -233,7 +233,16 @@ def test_fp8_validation(ra):
     o, lse = _t((1, 4, 64, 128)), torch.zeros(1, 4, 64)
     val = lambda *a, **kw: ra.STATUS[ra.attn_fwd_fp8_validate(*a, **kw)]
     assert val(q, k, vt, qd, kd, vd, o, lse, causal=True) == "RA_OK"
-    assert val(q, k, vt, qd, kd, vd, o.float(), lse, num_chunks=2, start_chunk=1) == "RA_OK"
+    # fused ring chunks must be whole 16-key units (key tiles on 16-byte vt boundaries)
+    assert val(q, k, vt, qd, kd, vd, o.float(), lse, num_chunks=2, start_chunk=1) == \
+        "RA_ERR_ALIGN"  # chunks of 20 keys
+    k64k, vt64k = f8((1, 2, 64, 128)), f8((1, 2, 128, 64))
+    for P in (2, 4):  # chunks of 32 and 16 keys
+        assert val(q, k64k, vt64k, qd, kd, vd, o.float(), lse, num_chunks=P,
+                   start_chunk=1) == "RA_OK"
+    k48, vt48 = f8((1, 2, 48, 128)), f8((1, 2, 128, 48))
+    assert val(q, k48, vt48, qd, kd, vd, o, lse, num_chunks=2) == "RA_ERR_ALIGN"  # 24 keys
+    assert val(q, k48, vt48, qd, kd, vd, o, lse, num_chunks=3) == "RA_OK"  # 16 keys
     assert val(q, k, f8((1, 2, 128, 40)), qd, kd, vd, o, lse) == "RA_ERR_ALIGN"  # rows of 40 B
     assert val(q, k, f8((1, 2, 128, 64)), qd, kd, vd, o, lse) == "RA_ERR_SHAPE"  # not S_pad
     assert val(q, k, f8((1, 2, 40, 128)), qd, kd, vd, o, lse) == "RA_ERR_SHAPE"  # not transposed

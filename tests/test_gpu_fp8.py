@@ -121,13 +121,13 @@ def _check(o_got, l_got, o_ref, l_ref, bound, what):
 
 CASES = [
     # B, Hq, Hkv, Sq, Skv, D, causal, P, start, q_off, kv_off
+    # (fused ring chunks are whole 16-key units; their last tiles are ragged)
     (1, 2, 2, 300, 300, 128, True, 1, 0, 0, 0),
-    (2, 4, 2, 200, 330, 64, False, 3, 1, 0, 0),
+    (2, 4, 2, 200, 336, 64, False, 3, 1, 0, 0),
     (1, 4, 1, 256, 256, 128, True, 4, 1, 0, 0),
-    # chunks of 130: the last tile of chunk 2 starts at key 388, inside the last 16
-    # columns of the padded V^T rows (400), so its clamped columns lie before the tile
-    (1, 2, 2, 130, 390, 128, True, 3, 2, 260, 0),
-    (1, 2, 1, 70, 390, 64, False, 3, 0, 0, 0),
+    (1, 2, 2, 144, 432, 128, True, 3, 2, 288, 0),
+    (1, 2, 1, 70, 432, 64, False, 3, 0, 0, 0),
+    (1, 3, 1, 100, 5 * 48, 128, True, 5, 3, 96, 0),
     (1, 7, 1, 333, 333, 128, True, 1, 0, 0, 0),
     (1, 2, 2, 200, 200, 128, True, 1, 0, 0, 100),   # rows with no visible key
     (1, 2, 2, 1, 1, 64, True, 1, 0, 0, 0),
