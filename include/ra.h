@@ -238,7 +238,10 @@ int ra_ulysses_permute_n_validate(int32_t n, const ra_tensor *srcs, const ra_ten
  * ra_attn_fwd with the same p.  dq like q, dk and dv like k, same dtype as q.  The ring parameters
  * fix the order in which dq accumulates over chunks.  Outputs must not overlap the
  * inputs.  workspace: device memory of at least ra_attn_bwd_workspace_size bytes,
- * 256-byte aligned, overwritten.  Deterministic.
+ * 256-byte aligned, overwritten: the D_i rows (B * Hq * Sq fp32), and with bf16 grouped
+ * heads (Hq > Hkv) also one fp32 dk and dv partial per query head (2 * B * Hq * Skv * D
+ * fp32), summed over each group in head order after the per-head passes.
+ * Deterministic.
  */
 int ra_attn_bwd(const ra_tensor *q, const ra_tensor *k, const ra_tensor *v, const ra_tensor *o,
                 const ra_tensor *dout, const ra_tensor *lse, const ra_attn_params *p,
@@ -248,7 +251,8 @@ int ra_attn_bwd_validate(const ra_tensor *q, const ra_tensor *k, const ra_tensor
                          const ra_tensor *o, const ra_tensor *dout, const ra_tensor *lse,
                          const ra_attn_params *p, const ra_tensor *dq, const ra_tensor *dk,
                          const ra_tensor *dv);
-/* Bytes of workspace ra_attn_bwd needs for these shapes (0 if the shapes are invalid). */
+/* Bytes of workspace ra_attn_bwd needs for these shapes and dtype (0 if the shapes are
+ * invalid): see ra_attn_bwd's workspace. */
 size_t ra_attn_bwd_workspace_size(const ra_tensor *q, const ra_tensor *k, const ra_attn_params *p);
 
 /*
@@ -256,11 +260,14 @@ size_t ra_attn_bwd_workspace_size(const ra_tensor *q, const ra_tensor *k, const 
  * allocation, for callers that cannot allocate device memory (code under HIP graph
  * capture, tight serving or training loops, harnesses that forbid hipMalloc).
  *
- * Same arguments (minus workspace), checks, results and errors as ra_attn_bwd; it runs
- * on the CURRENT device (the stream must belong to it).  Its workspace is a fixed
- * device array inside the library, RA_NOALLOC_SCRATCH_BYTES per GPU, held from library
- * load until the process ends; a problem whose workspace (ra_attn_bwd_workspace_size)
- * exceeds it returns RA_ERR_SCRATCH with nothing enqueued.  Every call on one GPU
+ * Same arguments (minus workspace), checks and errors as ra_attn_bwd, and the same
+ * results, except that with bf16 grouped heads dk and dv are summed over the group
+ * inside each workgroup (ra_attn_bwd sums per-head partials from its workspace): the
+ * same sums in another fp32 order, not bitwise equal.  It runs on the CURRENT device
+ * (the stream must belong to it).  Its workspace is a fixed device array inside the
+ * library, RA_NOALLOC_SCRATCH_BYTES per GPU, held from library load until the process
+ * ends; a problem whose D_i rows (B * Hq * Sq fp32) exceed it returns RA_ERR_SCRATCH
+ * with nothing enqueued.  Every call on one GPU
  * shares that GPU's array: calls that overlap in time on one GPU (other streams, other
  * threads) race and give undefined gradients; calls in one stream's order are safe.
  * No hipMalloc, hipFree or allocating library routine is called (the first call on a

@@ -376,6 +376,24 @@ BwdArgs bwd_args(const ra_tensor *q, const ra_tensor *k, const ra_tensor *v, con
   return a;
 }
 
+// Workspace of the bf16/fp32 backward: the D_i rows, then (bf16 with grouped heads) the
+// per-query-head dK/dV partials.
+size_t bwd_need_bytes(const ra_tensor *q, const ra_tensor *k) {
+  const size_t delta = bwd_workspace_bytes(q->shape[0], q->shape[1], q->shape[2]);
+  if (q->dtype != RA_BF16) return delta;
+  return delta + bwd_kv_part_bytes(q->shape[0], q->shape[1], k->shape[1], k->shape[2],
+                                   q->shape[3]);
+}
+
+// Points a.kv_part at the partials that follow the D_i rows, when there are any.
+void bwd_set_parts(BwdArgs &a, const ra_tensor *q, const ra_tensor *k, void *workspace) {
+  if (q->dtype != RA_BF16 ||
+      bwd_kv_part_bytes(q->shape[0], q->shape[1], k->shape[1], k->shape[2], q->shape[3]) == 0)
+    return;
+  a.kv_part = (float *)((char *)workspace +
+                        bwd_workspace_bytes(q->shape[0], q->shape[1], q->shape[2]));
+}
+
 }  // namespace
 }  // namespace ra
 
@@ -595,7 +613,7 @@ int ra_attn_bwd_validate(const ra_tensor *q, const ra_tensor *k, const ra_tensor
 size_t ra_attn_bwd_workspace_size(const ra_tensor *q, const ra_tensor *k, const ra_attn_params *p) {
   if (!q || !k || !p) return 0;
   if (check_qkv(q, k, k) != RA_OK || check_params(p, k->shape[2]) != RA_OK) return 0;
-  return bwd_workspace_bytes(q->shape[0], q->shape[1], q->shape[2]);
+  return bwd_need_bytes(q, k);
 }
 
 int ra_attn_bwd(const ra_tensor *q, const ra_tensor *k, const ra_tensor *v, const ra_tensor *o,
@@ -603,11 +621,12 @@ int ra_attn_bwd(const ra_tensor *q, const ra_tensor *k, const ra_tensor *v, cons
                 ra_tensor *dq, ra_tensor *dk, ra_tensor *dv, void *workspace,
                 size_t workspace_bytes, ra_stream stream) {
   RA_TRY(bwd_validate(q, k, v, o, dout, lse, p, dq, dk, dv));
-  const size_t need = bwd_workspace_bytes(q->shape[0], q->shape[1], q->shape[2]);
+  const size_t need = bwd_need_bytes(q, k);
   if (need > 0 && (!workspace || workspace_bytes < need || ((uintptr_t)workspace) % 256))
     return RA_ERR_WORKSPACE;
   if (numel(q) == 0 && numel(k) == 0) return RA_OK;
   BwdArgs a = bwd_args(q, k, v, o, dout, lse, p, dq, dk, dv, workspace);
+  bwd_set_parts(a, q, k, workspace);
   if (q->dtype == RA_F32)
     return launch_attn_bwd_f32(a, (int)q->shape[3], p->causal, false, (hipStream_t)stream);
   return launch_attn_bwd(a, (int)q->shape[3], p->causal, (hipStream_t)stream);
@@ -627,11 +646,12 @@ int ra_attn_bwd_varlen(const ra_tensor *q, const ra_tensor *k, const ra_tensor *
                        ra_tensor *dq, ra_tensor *dk, ra_tensor *dv, void *workspace,
                        size_t workspace_bytes, ra_stream stream) {
   RA_TRY(bwd_varlen_validate(q, k, v, o, dout, lse, cu_seqlens, n_docs, p, dq, dk, dv));
-  const size_t need = bwd_workspace_bytes(q->shape[0], q->shape[1], q->shape[2]);
+  const size_t need = bwd_need_bytes(q, k);
   if (need > 0 && (!workspace || workspace_bytes < need || ((uintptr_t)workspace) % 256))
     return RA_ERR_WORKSPACE;
   if (numel(q) == 0 && numel(k) == 0) return RA_OK;
   BwdArgs a = bwd_args(q, k, v, o, dout, lse, p, dq, dk, dv, workspace);
+  bwd_set_parts(a, q, k, workspace);
   a.cu = cu_seqlens;
   a.n_docs = n_docs;
   return launch_attn_bwd_varlen(a, (int)q->shape[3], p->causal, (hipStream_t)stream);
@@ -722,13 +742,14 @@ int ra_attn_bwd_accum(const ra_tensor *q, const ra_tensor *k, const ra_tensor *v
                       ra_tensor *dv_acc, void *workspace, size_t workspace_bytes,
                       ra_stream stream) {
   RA_TRY(bwd_accum_validate(q, k, v, o, dout, lse, p, dq_acc, dk_acc, dv_acc));
-  const size_t need = bwd_workspace_bytes(q->shape[0], q->shape[1], q->shape[2]);
+  const size_t need = bwd_need_bytes(q, k);
   if (need > 0 && (!workspace || workspace_bytes < need || ((uintptr_t)workspace) % 256))
     return RA_ERR_WORKSPACE;
   if (numel(q) == 0 || numel(k) == 0) return RA_OK;  // nothing to add
   // causal chunk skip: a chunk after the block's last query adds nothing
   if (p->causal && p->kv_offset > p->q_offset + q->shape[2] - 1) return RA_OK;
   BwdArgs a = bwd_args(q, k, v, o, dout, lse, p, dq_acc, dk_acc, dv_acc, workspace);
+  bwd_set_parts(a, q, k, workspace);
   if (q->dtype == RA_F32)
     return launch_attn_bwd_f32(a, (int)q->shape[3], p->causal, true, (hipStream_t)stream);
   return launch_attn_bwd_accum(a, (int)q->shape[3], p->causal, (hipStream_t)stream);

@@ -17,8 +17,10 @@
 //                   stream through LDS in ring order; per tile: S^T = K Q^T and
 //                   dP^T = V dO^T (Q, dO in registers), P and dS in registers, then
 //                   dQ^T += K^T dS^T with K^T read transposed from the same LDS tile;
-//   * bwd_dkdv   -- one workgroup per 128 keys (4 waves x 32) of one key/value head;
-//                   loops over 64-row query tiles of every query head of the group,
+//   * bwd_dkdv   -- one workgroup per 128 keys (4 waves x 32) of one key/value head
+//                   (with grouped heads: of one query head, into fp32 partials that
+//                   bwd_kv_reduce then sums over the group in a fixed order);
+//                   loops over 64-row query tiles of every query head it covers,
 //                   Q and dO tiles in LDS: S = Q K^T, dP = dO V^T (K^T, V^T in registers),
 //                   dV^T += dO^T P and dK^T += Q^T dS with dO^T, Q^T read transposed.
 // Tiles move global -> LDS with direct loads and a swizzle that keeps both row-wise
@@ -439,12 +441,21 @@ bwd_dkdv_kernel(BwdArgs a, int num_kv_tiles) {
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r32 = lane & 31, h = lane >> 5;
-  const int HB = a.Hkv * a.B;
+  // Grouped heads with a partials buffer: one workgroup per (key tile, query head), so
+  // that each sweeps the queries of one head (the workgroups running together on an XCD
+  // then share Q/dO tiles in L2, and the work splits into group-times more pieces);
+  // otherwise one per (key tile, key/value head), looping over the group's heads.
+  const bool split = a.kv_part != nullptr;
+  const int HB = (split ? a.Hq : a.Hkv) * a.B;
   const int bid = blockIdx.x;
   const int kt_i = bid / HB;  // ascending key tiles: lowest keys see the most queries
   int j = bid - kt_i * HB;
   if ((HB & 7) == 0) j = (j & 7) * (HB >> 3) + (j >> 3);
-  const int hk = j % a.Hkv, b = j / a.Hkv;
+  const int hx = split ? a.Hq : a.Hkv;
+  const int b = j / hx;
+  const int hk = split ? (j % hx) / a.group : j % hx;
+  const int hg0 = split ? (j % hx) % a.group : 0;  // first query head within the group
+  const int ngroup = split ? 1 : a.group;         // query heads this workgroup covers
   const int k0 = kt_i * BK;
   const int krow = k0 + 32 * wave + r32;  // this lane's key (column of S)
   const int kr = min(krow, a.Skv - 1);
@@ -526,12 +537,12 @@ bwd_dkdv_kernel(BwdArgs a, int num_kv_tiles) {
     qend = __builtin_amdgcn_readfirstlane(min(max(l_de, l_ds), a.Sq));
   }
   const int nqt = qstart >= qend ? 0 : (qend - qstart + TN - 1) / TN;
-  const int total = nqt * a.group;  // (query head, query tile) pairs
+  const int total = nqt * ngroup;  // (query head, query tile) pairs
 
   // tile `it` is query tile qt of query head hk * group + hg (qt fastest); the pair is
   // advanced by one per tile instead of divided out of it
   auto issue = [&](int hg, int qt, uint32_t slot) {
-    const int hq = hk * a.group + hg;
+    const int hq = hk * a.group + hg0 + hg;
     const int q0 = qstart + qt * TN;
     const uint16_t *qb = (const uint16_t *)a.q + b * a.q_sb + hq * a.q_sh;
     const uint16_t *dob = (const uint16_t *)a.dout + b * a.do_sb + hq * a.do_sh;
@@ -542,7 +553,7 @@ bwd_dkdv_kernel(BwdArgs a, int num_kv_tiles) {
   };
   // lse (as exp2 offsets) and -delta of the tile's 64 rows: threads 0-127
   auto stats = [&](int hg, int qt, float &val) {
-    const int hq = hk * a.group + hg;
+    const int hq = hk * a.group + hg0 + hg;
     const int q0 = qstart + qt * TN;
     const int i = tid & 63;
     const int q = min(q0 + i, a.Sq - 1);
@@ -753,7 +764,23 @@ bwd_dkdv_kernel(BwdArgs a, int num_kv_tiles) {
   // the compiler does not see the asm MFMAs: give their results time to land before
   // the epilogue reads the accumulators
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
-  if (krow < a.Skv) {
+  if (split && krow < a.Skv) {
+    // this query head's unscaled fp32 partials, [2][B, Hq, Skv, D] contiguous
+    const int64_t n_part = (int64_t)a.B * a.Hq * a.Skv * D;
+    const int hq = hk * a.group + hg0;
+    float *pk = a.kv_part + (((int64_t)b * a.Hq + hq) * a.Skv + krow) * D;
+    float *pv = pk + n_part;
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d = 32 * dt + 8 * g + 4 * h;
+        *(f32x4 *)(pk + d) = f32x4{dk[dt][4 * g], dk[dt][4 * g + 1], dk[dt][4 * g + 2],
+                                   dk[dt][4 * g + 3]};
+        *(f32x4 *)(pv + d) = f32x4{dv[dt][4 * g], dv[dt][4 * g + 1], dv[dt][4 * g + 2],
+                                   dv[dt][4 * g + 3]};
+      }
+  } else if (krow < a.Skv) {
     const int64_t krow_dk = b * a.dk_sb + hk * a.dk_sh + (int64_t)krow * a.dk_ss;
     const int64_t krow_dv = b * a.dv_sb + hk * a.dv_sh + (int64_t)krow * a.dv_ss;
 #pragma unroll
@@ -786,6 +813,63 @@ bwd_dkdv_kernel(BwdArgs a, int num_kv_tiles) {
   }
 }
 
+// dK, dV of grouped heads: the sum over the group's query heads of the partials, in head
+// order (deterministic), scaled (dK) and rounded to bf16, or added to the fp32
+// accumulators (ACC).  One thread per 8 head dims of one key; HBM-bound.
+template <int D, bool ACC>
+__global__ void __launch_bounds__(256) bwd_kv_reduce_kernel(BwdArgs a) {
+  constexpr int CPK = D / 8;  // chunks of 8 dims per key
+  const int64_t n_part = (int64_t)a.B * a.Hq * a.Skv * D;
+  const int64_t nchunks = (int64_t)a.B * a.Hkv * a.Skv * CPK;
+  for (int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x; c < nchunks;
+       c += (int64_t)gridDim.x * 256) {
+    const int d = (int)(c % CPK) * 8;
+    const int64_t key_all = c / CPK;  // (b, hk, key)
+    const int key = (int)(key_all % a.Skv);
+    const int64_t bh = key_all / a.Skv;
+    const int hk = (int)(bh % a.Hkv), b = (int)(bh / a.Hkv);
+    float sk[8], sv[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) sk[e] = sv[e] = 0.f;
+    for (int hg = 0; hg < a.group; ++hg) {
+      const float *pk =
+          a.kv_part + (((int64_t)b * a.Hq + hk * a.group + hg) * a.Skv + key) * D + d;
+      const f32x4 k0 = *(const f32x4 *)pk, k1 = *(const f32x4 *)(pk + 4);
+      const f32x4 v0 = *(const f32x4 *)(pk + n_part), v1 = *(const f32x4 *)(pk + n_part + 4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        sk[e] += k0[e]; sk[4 + e] += k1[e];
+        sv[e] += v0[e]; sv[4 + e] += v1[e];
+      }
+    }
+    const int64_t ok = b * a.dk_sb + hk * a.dk_sh + (int64_t)key * a.dk_ss + d;
+    const int64_t ov = b * a.dv_sb + hk * a.dv_sh + (int64_t)key * a.dv_ss + d;
+    if (ACC) {
+      f32x4 *ak = (f32x4 *)((float *)a.dk + ok), *av = (f32x4 *)((float *)a.dv + ov);
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const f32x4 pk = ak[q], pv = av[q];
+        ak[q] = f32x4{pk[0] + sk[4 * q] * a.scale, pk[1] + sk[4 * q + 1] * a.scale,
+                      pk[2] + sk[4 * q + 2] * a.scale, pk[3] + sk[4 * q + 3] * a.scale};
+        av[q] = f32x4{pv[0] + sv[4 * q], pv[1] + sv[4 * q + 1], pv[2] + sv[4 * q + 2],
+                      pv[3] + sv[4 * q + 3]};
+      }
+    } else {
+      u32x4 wk, wv;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const bf16x2 k2 = __builtin_convertvector(
+            (f32x2){sk[2 * q] * a.scale, sk[2 * q + 1] * a.scale}, bf16x2);
+        const bf16x2 v2 = __builtin_convertvector((f32x2){sv[2 * q], sv[2 * q + 1]}, bf16x2);
+        wk[q] = __builtin_bit_cast(uint32_t, k2);
+        wv[q] = __builtin_bit_cast(uint32_t, v2);
+      }
+      *(u32x4 *)((uint16_t *)a.dk + ok) = wk;
+      *(u32x4 *)((uint16_t *)a.dv + ov) = wv;
+    }
+  }
+}
+
 template <int D, bool CAUSAL, bool VARLEN = false, bool ACC = false>
 int launch_bwd(const BwdArgs &a, hipStream_t stream) {
   // 1. D_i
@@ -796,13 +880,21 @@ int launch_bwd(const BwdArgs &a, hipStream_t stream) {
     if (blocks > 0)
       hipLaunchKernelGGL((bwd_delta_kernel<D>), dim3((unsigned)blocks), dim3(256), 0, stream, a);
   }
-  // 2. dK, dV
+  // 2. dK, dV (with grouped heads and a partials buffer: per query head, then summed)
   {
     const int nkt = (a.Skv + 127) / 128;
-    const int64_t blocks = (int64_t)nkt * a.Hkv * a.B;
+    const bool split = a.kv_part != nullptr;
+    const int64_t blocks = (int64_t)nkt * (split ? a.Hq : a.Hkv) * a.B;
     if (blocks > 0)
       hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, VARLEN, ACC>), dim3((unsigned)blocks), dim3(256), 0,
                          stream, a, nkt);
+    const int64_t nchunks = (int64_t)a.B * a.Hkv * a.Skv * (D / 8);
+    if (split && nchunks > 0) {
+      int64_t rblocks = (nchunks + 255) / 256;
+      if (rblocks > (1 << 20)) rblocks = 1 << 20;
+      hipLaunchKernelGGL((bwd_kv_reduce_kernel<D, ACC>), dim3((unsigned)rblocks), dim3(256), 0,
+                         stream, a);
+    }
   }
   // 3. dQ
   {
@@ -820,6 +912,12 @@ int launch_bwd(const BwdArgs &a, hipStream_t stream) {
 
 size_t bwd_workspace_bytes(int64_t B, int64_t Hq, int64_t Sq) {
   const size_t n = (size_t)(B * Hq * Sq) * sizeof(float);
+  return (n + 255) / 256 * 256;
+}
+
+size_t bwd_kv_part_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t Skv, int64_t D) {
+  if (Hkv <= 0 || Hq <= Hkv) return 0;
+  const size_t n = 2 * (size_t)(B * Hq * Skv * D) * sizeof(float);
   return (n + 255) / 256 * 256;
 }
 

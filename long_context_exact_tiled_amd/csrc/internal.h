@@ -83,6 +83,9 @@ struct BwdArgs {
   const float *lse;
   void *dq, *dk, *dv;
   float *delta;  // workspace: D_i = rowsum(dout * o), [B, Hq, Sq] contiguous
+  // workspace, or null: with grouped heads, per-query-head fp32 partials of dK and dV
+  // ([2][B, Hq, Skv, D] contiguous, unscaled), summed over the group afterwards
+  float *kv_part;
   int64_t q_sb, q_sh, q_ss;
   int64_t k_sb, k_sh, k_ss;
   int64_t v_sb, v_sh, v_ss;
@@ -129,6 +132,9 @@ void quant_split(int64_t S, int64_t D, int32_t &nsplit, int32_t &rows_per_split)
 int launch_fp8_quantize(const QuantArgs &a, hipStream_t stream);
 
 size_t bwd_workspace_bytes(int64_t B, int64_t Hq, int64_t Sq);
+// Bytes of the grouped-head dK/dV partials (0 without grouped heads); they follow the
+// D_i rows in the bf16 backward's workspace.
+size_t bwd_kv_part_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t Skv, int64_t D);
 int launch_attn_bwd(const BwdArgs &a, int D, int causal, hipStream_t stream);
 int launch_attn_bwd_varlen(const BwdArgs &a, int D, int causal, hipStream_t stream);
 // One ring step: dq, dk, dv point at fp32 accumulators that receive += contributions.

@@ -203,7 +203,12 @@ def test_bwd_validation(ra):
     assert val(f(q), f(k), f(v), f(o), f(do), lse, dq, f(dk), f(dv)) == "RA_ERR_DTYPE"
     assert val(f(q)[..., :64], f(k)[..., :64], f(v)[..., :64], f(o)[..., :64], f(do)[..., :64],
                lse, f(dq)[..., :64], f(dk)[..., :64], f(dv)[..., :64]) == "RA_OK"  # D = 64
-    assert ra.attn_bwd_workspace_size(q, k) >= 4 * 64 * 4
+    # the D_i rows (B*Hq*Sq fp32, 256-byte rounded); with bf16 grouped heads then the
+    # per-query-head fp32 dk/dv partials, 2*B*Hq*Skv*D*4 bytes
+    delta = 4 * 64 * 4
+    assert ra.attn_bwd_workspace_size(q, k) == delta + 2 * 4 * 64 * 128 * 4
+    assert ra.attn_bwd_workspace_size(f(q), f(k)) == delta  # fp32: no partials
+    assert ra.attn_bwd_workspace_size(q, _t((1, 4, 64, 128))) == delta  # one head per group
     assert ra.attn_bwd_workspace_size(q, _t((1, 3, 64, 128))) == 0
 
 
