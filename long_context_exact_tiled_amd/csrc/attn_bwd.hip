@@ -50,6 +50,9 @@ static_assert(TN <= kMaxTileRows, "tile offsets are 32-bit");
 #ifndef RA_BWD_DQ_LOADERS
 #define RA_BWD_DQ_LOADERS (RA_BWD_DQ_NW / 2)  // dQ: waves (the last ones) that load K/V tiles
 #endif
+#ifndef RA_BWD_DKDV_NW
+#define RA_BWD_DKDV_NW 4  // dK/dV: waves (32 keys each) per workgroup, one per SIMD
+#endif
 #ifndef RA_BWD_DKDV_LOADERS
 #define RA_BWD_DKDV_LOADERS 2  // dK/dV: waves that issue the Q/dO tile loads (the last ones)
 #endif
@@ -430,9 +433,9 @@ bwd_dq_kernel(BwdArgs a, int num_q_tiles) {
 //   dV^T += dO^T P, dK^T += Q^T dS          (A: transposed reads of dO / Q)
 // ---------------------------------------------------------------------------------
 template <int D, bool CAUSAL, bool VARLEN, bool ACC>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ void __launch_bounds__(64 * RA_BWD_DKDV_NW) __attribute__((amdgpu_waves_per_eu(1, 1)))
 bwd_dkdv_kernel(BwdArgs a, int num_kv_tiles) {
-  constexpr int NW = 4, BK = 32 * NW;
+  constexpr int NW = RA_BWD_DKDV_NW, BK = 32 * NW;
   using Tile = STile<D, NW>;
   // per slot: Q tile, dO tile, lse2[TN], delta[TN]
   constexpr int SLOT = 2 * Tile::BYTES + 2 * TN * 4;
@@ -882,11 +885,13 @@ int launch_bwd(const BwdArgs &a, hipStream_t stream) {
   }
   // 2. dK, dV (with grouped heads and a partials buffer: per query head, then summed)
   {
-    const int nkt = (a.Skv + 127) / 128;
+    constexpr int BK = 32 * RA_BWD_DKDV_NW;
+    const int nkt = (a.Skv + BK - 1) / BK;
     const bool split = a.kv_part != nullptr;
     const int64_t blocks = (int64_t)nkt * (split ? a.Hq : a.Hkv) * a.B;
     if (blocks > 0)
-      hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, VARLEN, ACC>), dim3((unsigned)blocks), dim3(256), 0,
+      hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, VARLEN, ACC>), dim3((unsigned)blocks),
+                         dim3(64 * RA_BWD_DKDV_NW), 0,
                          stream, a, nkt);
     const int64_t nchunks = (int64_t)a.B * a.Hkv * a.Skv * (D / 8);
     if (split && nchunks > 0) {
