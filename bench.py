@@ -14,8 +14,9 @@ Prints ONE JSON line.  ``value`` is the algorithmic attention TFLOP/s of the who
 runs on; ``cpu_baseline`` times the fp64 CPU oracle on whole heads of the same workload's
 own seeded inputs, for a bounded time.  The default run also times the other workloads
 of the same hot path (the 8K Llama-7B-shaped causal layer, one rank's share of an 8-way
-ring at 32K -- fused and chunk by chunk with the merge -- and the 16K causal backward)
-and reports each as extra keys.  ``--workload`` selects another workload as the
+ring at 32K -- fused and chunk by chunk with the merge -- the 16K causal backward, the
+FP8 forward of the 32K GQA shape, and the packed-document forward and backward) and
+reports each as extra keys.  ``--workload`` selects another workload as the
 headline of the line instead.
 """
 from __future__ import annotations
@@ -424,6 +425,9 @@ SECONDARY = [
     ("ring8_rank3_32k_fused_fwd", "ring8_rank3_32k", False),
     ("ring8_rank3_32k_chunked_fwd", "ring8_rank3_32k", True),
     ("llama7b_16k_bwd", "llama7b_causal_bwd_16k", False),
+    ("qwen7b_gqa_32k_fp8_fwd", "qwen7b_gqa_32k_fp8", False),
+    ("qwen7b_packed_32k_fwd", "qwen7b_packed_32k", False),
+    ("qwen7b_packed_32k_bwd", "qwen7b_packed_bwd_32k", False),
 ]
 
 
