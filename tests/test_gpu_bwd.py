@@ -66,11 +66,18 @@ def test_small_bwd(case):
          seed=sum(map(ord, str(case))) % 991)
 
 
-def test_bwd_deterministic():
-    say("bwd determinism")
-    q, k, v, do = (torch.randn(1, 4, 400, 128, device="cuda").bfloat16() for _ in range(4))
+@pytest.mark.parametrize("Hkv", [4, 1])
+def test_bwd_deterministic(Hkv):
+    """Bitwise the same gradients on repeated calls: one key/value head per query head,
+    and grouped heads (per-query-head partials summed in head order; the workspace is
+    filled with garbage first, so nothing may depend on its old contents)."""
+    say(f"bwd determinism Hkv={Hkv}")
+    q, do = (torch.randn(1, 4, 400, 128, device="cuda").bfloat16() for _ in range(2))
+    k, v = (torch.randn(1, Hkv, 400, 128, device="cuda").bfloat16() for _ in range(2))
     o, lse = ra.attn_fwd(q, k, v, causal=True)
-    a = ra.attn_bwd(q, k, v, o, do, lse, causal=True)
+    need = ra.attn_bwd_workspace_size(q, k, causal=True)
+    ws = torch.full((need,), 0x7F, dtype=torch.uint8, device="cuda")
+    a = ra.attn_bwd(q, k, v, o, do, lse, causal=True, workspace=ws)
     b = ra.attn_bwd(q, k, v, o, do, lse, causal=True)
     torch.cuda.synchronize()
     for x, y in zip(a, b):
