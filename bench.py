@@ -509,26 +509,35 @@ def main():
         extra["permute_ms_per_step"] = float(np.mean(side_ms))
         extra["permute_GBps"] = moved / (np.mean(side_ms) * 1e-3) / 1e9
         # cold-cache rate: reading 1 GiB evicts the 256 MB Infinity Cache (and the L2s)
-        # before each pass.  The flush reads: a flush by writing would leave the caches
-        # full of dirty lines whose write-back then runs inside the timed pass.
+        # before each pass.  A flush by writing 1 GiB evicts them too but leaves them full
+        # of dirty lines whose write-back then runs inside the timed pass; that rate is
+        # reported beside it (permute_cold_write_flush_*).
         scratch = torch.zeros(1 << 27, dtype=torch.int64, device=dev)
-        cold = []
-        for _ in range(5):
-            scratch.sum()
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            s["pre"]()
-            e1.record(stream)
-            scratch.sum()
-            e2, e3 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e2.record(stream)
-            s["post"]()
-            e3.record(stream)
-            torch.cuda.synchronize()
-            cold.append(e0.elapsed_time(e1) + e2.elapsed_time(e3))
+
+        def cold_passes(flush):
+            cold = []
+            for _ in range(5):
+                flush()
+                e0, e1 = (torch.cuda.Event(enable_timing=True) for _ in range(2))
+                e0.record(stream)
+                s["pre"]()
+                e1.record(stream)
+                flush()
+                e2, e3 = (torch.cuda.Event(enable_timing=True) for _ in range(2))
+                e2.record(stream)
+                s["post"]()
+                e3.record(stream)
+                torch.cuda.synchronize()
+                cold.append(e0.elapsed_time(e1) + e2.elapsed_time(e3))
+            return float(np.median(cold))
+
+        ms_r = cold_passes(lambda: scratch.sum())
+        ms_w = cold_passes(lambda: scratch.zero_())
         del scratch
-        extra["permute_cold_ms_per_step"] = float(np.median(cold))
-        extra["permute_cold_GBps"] = moved / (np.median(cold) * 1e-3) / 1e9
+        extra["permute_cold_ms_per_step"] = ms_r
+        extra["permute_cold_GBps"] = moved / (ms_r * 1e-3) / 1e9
+        extra["permute_cold_write_flush_ms_per_step"] = ms_w
+        extra["permute_cold_write_flush_GBps"] = moved / (ms_w * 1e-3) / 1e9
     merge = extra.pop("_merge", None)
     if merge is not None:
         fn, mbytes, nparts = merge
