@@ -45,6 +45,7 @@ extern "C" {
 #define RA_VERSION 100 /* 0.1.0 */
 #define RA_MAX_MERGE_PARTS 64
 #define RA_MAX_PERMUTE_TENSORS 4
+#define RA_MAX_QUANT_TENSORS 4
 #define RA_MAX_DOCS (1 << 24)
 
 typedef enum {
@@ -364,6 +365,23 @@ int ra_fp8_quantize_validate(const ra_tensor *src, const ra_tensor *dst,
                              const ra_tensor *descale, int32_t transpose);
 /* Bytes of workspace ra_fp8_quantize needs for src (0 if src is invalid). */
 size_t ra_fp8_quantize_workspace_size(const ra_tensor *src);
+
+/*
+ * ra_fp8_quantize_n -- ra_fp8_quantize of n tensors (1 <= n <= RA_MAX_QUANT_TENSORS; q, k
+ * and v of a layer, each with its own transpose flag) in two launches instead of 2n.
+ * Each tensor's codes and descales are those ra_fp8_quantize gives it.  srcs, dsts,
+ * descales: arrays of n descriptors; transpose: n flags.  No destination (codes or
+ * descales) may overlap a source or another destination (RA_ERR_STRIDE).  workspace:
+ * at least ra_fp8_quantize_n_workspace_size bytes, 256-byte aligned, overwritten.
+ * Errors as for ra_fp8_quantize, and RA_ERR_RANGE for n outside 1..4.
+ */
+int ra_fp8_quantize_n(int32_t n, const ra_tensor *srcs, ra_tensor *dsts, ra_tensor *descales,
+                      const int32_t *transpose, void *workspace, size_t workspace_bytes,
+                      ra_stream stream);
+int ra_fp8_quantize_n_validate(int32_t n, const ra_tensor *srcs, const ra_tensor *dsts,
+                               const ra_tensor *descales, const int32_t *transpose);
+/* Bytes of workspace ra_fp8_quantize_n needs for these sources (0 if any is invalid). */
+size_t ra_fp8_quantize_n_workspace_size(int32_t n, const ra_tensor *srcs);
 
 /*
  * ra_attn_fwd_fp8 -- ra_attn_fwd over e4m3 inputs: exact softmax attention of the

@@ -30,7 +30,8 @@ __all__ = [
     "attn_bwd_accum", "attn_bwd_accum_validate", "ring_attn_bwd_chunked",
     "fp8_quantize", "fp8_quantize_validate", "attn_fwd_fp8", "attn_fwd_fp8_validate",
     "ring_attn_fp8_chunked", "ulysses_permute_multi", "ulysses_permute_multi_validate",
-    "attn_bwd_noalloc", "noalloc_scratch_bytes",
+    "attn_bwd_noalloc", "noalloc_scratch_bytes", "fp8_quantize_multi",
+    "fp8_quantize_multi_validate",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libra.so")
@@ -117,6 +118,9 @@ def lib() -> ctypes.CDLL:
             "ra_fp8_quantize": [T, T, T, i32, vp, sz, vp],
             "ra_fp8_quantize_validate": [T, T, T, i32],
             "ra_fp8_quantize_workspace_size": [T],
+            "ra_fp8_quantize_n": [i32, T, T, T, vp, vp, sz, vp],
+            "ra_fp8_quantize_n_validate": [i32, T, T, T, vp],
+            "ra_fp8_quantize_n_workspace_size": [i32, T],
             "ra_attn_fwd_fp8": [T, T, T, T, T, T, PP, T, T, vp],
             "ra_attn_fwd_fp8_validate": [T, T, T, T, T, T, PP, T, T],
             "ra_status_string": [ctypes.c_int],
@@ -128,6 +132,7 @@ def lib() -> ctypes.CDLL:
             fn.restype = ctypes.c_int
         L.ra_attn_bwd_workspace_size.restype = ctypes.c_size_t
         L.ra_fp8_quantize_workspace_size.restype = ctypes.c_size_t
+        L.ra_fp8_quantize_n_workspace_size.restype = ctypes.c_size_t
         L.ra_noalloc_scratch_bytes.restype = ctypes.c_size_t
         L.ra_status_string.restype = ctypes.c_char_p
         _LIB = L
@@ -234,6 +239,50 @@ def fp8_quantize(x: torch.Tensor, *, transpose: bool = False, out=None, descale=
     _check(lib().ra_fp8_quantize(desc(x), desc(out), desc(descale), int(bool(transpose)),
                                  workspace.data_ptr(), workspace.numel(), _stream(x)))
     return out, descale
+
+
+def _quant_outs(xs, transposes):
+    outs, descs = [], []
+    for x, t in zip(xs, transposes):
+        B, H, S, D = x.shape
+        shape = (B, H, D, (S + 15) // 16 * 16) if t else (B, H, S, D)
+        outs.append(torch.empty(shape, dtype=torch.float8_e4m3fn, device=x.device))
+        descs.append(torch.empty(B, H, dtype=torch.float32, device=x.device))
+    return outs, descs
+
+
+def fp8_quantize_multi(xs: Sequence[torch.Tensor], transposes: Sequence[bool], *, outs=None,
+                       descales=None, workspace: Optional[torch.Tensor] = None):
+    """fp8_quantize of several tensors (q, k, v of a layer, each with its own transpose
+    flag) in two launches.  Returns (codes list, descale list)."""
+    xs, transposes = list(xs), [int(bool(t)) for t in transposes]
+    if not xs or len(transposes) != len(xs):
+        raise RaError(-6, "RA_ERR_RANGE: xs and transposes must be non-empty and of equal length")
+    if outs is None or descales is None:
+        o2, d2 = _quant_outs(xs, transposes)
+        outs = o2 if outs is None else list(outs)
+        descales = d2 if descales is None else list(descales)
+    n = len(xs)
+    sa = (RaTensor * n)(*[desc(t) for t in xs])
+    oa = (RaTensor * n)(*[desc(t) for t in outs])
+    da = (RaTensor * n)(*[desc(t) for t in descales])
+    ta = (ctypes.c_int32 * n)(*transposes)
+    if workspace is None:
+        need = int(lib().ra_fp8_quantize_n_workspace_size(n, sa))
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=xs[0].device)
+    _check(lib().ra_fp8_quantize_n(n, sa, oa, da, ctypes.cast(ta, ctypes.c_void_p),
+                                   workspace.data_ptr(), workspace.numel(), _stream(xs[0])))
+    return list(outs), list(descales)
+
+
+def fp8_quantize_multi_validate(xs, outs, descales, transposes) -> int:
+    n = len(xs)
+    m = max(n, 1)
+    sa = (RaTensor * m)(*[desc(t) for t in xs])
+    oa = (RaTensor * m)(*[desc(t) for t in outs])
+    da = (RaTensor * m)(*[desc(t) for t in descales])
+    ta = (ctypes.c_int32 * m)(*[int(bool(t)) for t in transposes])
+    return int(lib().ra_fp8_quantize_n_validate(n, sa, oa, da, ctypes.cast(ta, ctypes.c_void_p)))
 
 
 def fp8_quantize_validate(x, out, descale, *, transpose=False) -> int:

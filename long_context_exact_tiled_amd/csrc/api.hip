@@ -348,6 +348,24 @@ size_t quant_workspace_bytes(const ra_tensor *src) {
   return (n + 255) / 256 * 256;
 }
 
+QuantArgs quant_args(const ra_tensor *src, ra_tensor *dst, ra_tensor *descale, int32_t transpose,
+                     void *workspace) {
+  QuantArgs a{};
+  a.src = (const uint16_t *)src->data;
+  a.dst = (uint8_t *)dst->data;
+  a.descale = (float *)descale->data;
+  a.partial = (float *)workspace;
+  a.s_sb = src->stride[0]; a.s_sh = src->stride[1]; a.s_ss = src->stride[2];
+  a.d_sb = dst->stride[0]; a.d_sh = dst->stride[1]; a.d_s2 = dst->stride[2];
+  a.ds_sb = descale->stride[0]; a.ds_sh = descale->stride[1];
+  a.B = (int32_t)src->shape[0]; a.H = (int32_t)src->shape[1];
+  a.S = (int32_t)src->shape[2]; a.D = (int32_t)src->shape[3];
+  a.S_pad = (a.S + 15) / 16 * 16;
+  a.transpose = transpose;
+  quant_split(a.S, a.D, a.nsplit, a.rows_per_split);
+  return a;
+}
+
 BwdArgs bwd_args(const ra_tensor *q, const ra_tensor *k, const ra_tensor *v, const ra_tensor *o,
                  const ra_tensor *dout, const ra_tensor *lse, const ra_attn_params *p,
                  ra_tensor *dq, ra_tensor *dk, ra_tensor *dv, void *workspace) {
@@ -592,6 +610,71 @@ int ra_ulysses_permute_n_validate(int32_t n, const ra_tensor *srcs, const ra_ten
   return permute_n_validate(n, srcs, dsts, P, rank, dir);
 }
 
+namespace {
+
+int quant_n_validate(int32_t n, const ra_tensor *srcs, const ra_tensor *dsts,
+                     const ra_tensor *descales, const int32_t *transpose) {
+  if (!srcs || !dsts || !descales || !transpose) return RA_ERR_NULL;
+  if (n < 1 || n > RA_MAX_QUANT_TENSORS) return RA_ERR_RANGE;
+  int64_t blocks = 0;
+  for (int i = 0; i < n; ++i) {
+    RA_TRY(quant_validate(&srcs[i], &dsts[i], &descales[i], transpose[i]));
+    int32_t nsplit, rps;
+    quant_split(srcs[i].shape[2], srcs[i].shape[3], nsplit, rps);
+    const int64_t tiles = (srcs[i].shape[2] + 15) / 16 * 16 / 64 + 1;
+    blocks += srcs[i].shape[0] * srcs[i].shape[1] * (nsplit > tiles ? nsplit : tiles);
+  }
+  if (blocks > (int64_t)INT32_MAX) return RA_ERR_SHAPE;  // one grid covers all tensors
+  for (int i = 0; i < n; ++i)
+    for (int j = 0; j < n; ++j) {
+      if (overlaps(&dsts[i], &srcs[j]) || overlaps(&descales[i], &srcs[j]) ||
+          overlaps(&descales[i], &dsts[j]))
+        return RA_ERR_STRIDE;
+      if (i != j && (overlaps(&dsts[i], &dsts[j]) || overlaps(&descales[i], &descales[j])))
+        return RA_ERR_STRIDE;
+    }
+  return RA_OK;
+}
+
+// each tensor's partial maxima at a 256-byte aligned offset of the workspace
+size_t quant_n_offsets(int32_t n, const ra_tensor *srcs, size_t *off) {
+  size_t total = 0;
+  for (int i = 0; i < n; ++i) {
+    if (off) off[i] = total;
+    total += quant_workspace_bytes(&srcs[i]);
+  }
+  return total;
+}
+
+}  // namespace
+
+int ra_fp8_quantize_n_validate(int32_t n, const ra_tensor *srcs, const ra_tensor *dsts,
+                               const ra_tensor *descales, const int32_t *transpose) {
+  return quant_n_validate(n, srcs, dsts, descales, transpose);
+}
+
+size_t ra_fp8_quantize_n_workspace_size(int32_t n, const ra_tensor *srcs) {
+  if (!srcs || n < 1 || n > RA_MAX_QUANT_TENSORS) return 0;
+  for (int i = 0; i < n; ++i)
+    if (check_tensor(&srcs[i], 4, 16, false) != RA_OK) return 0;
+  return quant_n_offsets(n, srcs, nullptr);
+}
+
+int ra_fp8_quantize_n(int32_t n, const ra_tensor *srcs, ra_tensor *dsts, ra_tensor *descales,
+                      const int32_t *transpose, void *workspace, size_t workspace_bytes,
+                      ra_stream stream) {
+  RA_TRY(quant_n_validate(n, srcs, dsts, descales, transpose));
+  size_t off[RA_MAX_QUANT_TENSORS];
+  const size_t need = quant_n_offsets(n, srcs, off);
+  if (!workspace || workspace_bytes < need || ((uintptr_t)workspace) % 256)
+    return RA_ERR_WORKSPACE;
+  QuantArgs a[RA_MAX_QUANT_TENSORS];
+  for (int i = 0; i < n; ++i)
+    a[i] = quant_args(&srcs[i], &dsts[i], &descales[i], transpose[i],
+                      (char *)workspace + off[i]);
+  return launch_fp8_quantize_n(a, n, (hipStream_t)stream);
+}
+
 int ra_ulysses_permute_n(int32_t n, const ra_tensor *srcs, ra_tensor *dsts, int32_t P,
                          int32_t rank, int32_t dir, ra_stream stream) {
   RA_TRY(permute_n_validate(n, srcs, dsts, P, rank, dir));
@@ -713,19 +796,7 @@ int ra_fp8_quantize(const ra_tensor *src, ra_tensor *dst, ra_tensor *descale, in
   const size_t need = quant_workspace_bytes(src);
   if (!workspace || workspace_bytes < need || ((uintptr_t)workspace) % 256)
     return RA_ERR_WORKSPACE;
-  QuantArgs a{};
-  a.src = (const uint16_t *)src->data;
-  a.dst = (uint8_t *)dst->data;
-  a.descale = (float *)descale->data;
-  a.partial = (float *)workspace;
-  a.s_sb = src->stride[0]; a.s_sh = src->stride[1]; a.s_ss = src->stride[2];
-  a.d_sb = dst->stride[0]; a.d_sh = dst->stride[1]; a.d_s2 = dst->stride[2];
-  a.ds_sb = descale->stride[0]; a.ds_sh = descale->stride[1];
-  a.B = (int32_t)src->shape[0]; a.H = (int32_t)src->shape[1];
-  a.S = (int32_t)src->shape[2]; a.D = (int32_t)src->shape[3];
-  a.S_pad = (a.S + 15) / 16 * 16;
-  a.transpose = transpose;
-  quant_split(a.S, a.D, a.nsplit, a.rows_per_split);
+  const QuantArgs a = quant_args(src, dst, descale, transpose, workspace);
   return launch_fp8_quantize(a, (hipStream_t)stream);
 }
 

@@ -11,7 +11,8 @@
 // Two passes, both bound by HBM bandwidth and deterministic (a max does not depend on
 // the order it is taken in): partial maxima per (head, row range) into the workspace,
 // then every block folds its head's partials and converts its rows (or, transposed,
-// a 64-token x D tile through LDS).
+// a 64-token x D tile through LDS).  Up to four tensors (q, k and v of a layer) share the
+// two launches: each tensor owns a contiguous range of either grid's blocks.
 #include <math.h>
 
 #include "common.h"
@@ -44,9 +45,26 @@ __device__ __forceinline__ float absmax8(const u32x4 &x) {
   return m;
 }
 
-__global__ void __launch_bounds__(kThreads) quant_amax_kernel(QuantArgs a) {
-  __shared__ float red[4];
-  const int bh = blockIdx.x / a.nsplit, sp = blockIdx.x % a.nsplit;
+// The tensors of one launch: tensor i owns blocks [amax0[i], amax0[i+1]) of the max pass
+// and [conv0[i], conv0[i+1]) of the conversion pass.
+constexpr int kMaxQuant = RA_MAX_QUANT_TENSORS;
+struct QuantMulti {
+  QuantArgs t[kMaxQuant];
+  int32_t amax0[kMaxQuant + 1];
+  int32_t conv0[kMaxQuant + 1];
+  int32_t ntiles[kMaxQuant];  // transposed tensors: 64-token tiles per head
+  int32_t n;
+};
+
+// the tensor owning block `bid` of a pass whose block ranges start at `base` (uniform)
+__device__ __forceinline__ int owner(const int32_t *base, int n, int bid) {
+  int i = 0;
+  while (i + 1 < n && bid >= base[i + 1]) ++i;
+  return i;
+}
+
+__device__ __forceinline__ void amax_block(const QuantArgs &a, int blk, float *red) {
+  const int bh = blk / a.nsplit, sp = blk % a.nsplit;
   const int b = bh / a.H, h = bh % a.H;
   const int r0 = sp * a.rows_per_split, r1 = min(a.S, r0 + a.rows_per_split);
   const int ppr = a.D / 8;  // 16-byte pieces per row
@@ -57,7 +75,13 @@ __global__ void __launch_bounds__(kThreads) quant_amax_kernel(QuantArgs a) {
     m = fmaxf(m, absmax8(*(const u32x4 *)(src + (int64_t)r * a.s_ss + 8 * c)));
   }
   m = block_max(m, red);
-  if (threadIdx.x == 0) a.partial[blockIdx.x] = m;
+  if (threadIdx.x == 0) a.partial[blk] = m;
+}
+
+__global__ void __launch_bounds__(kThreads) quant_amax_kernel(QuantMulti m) {
+  __shared__ float red[4];
+  const int i = owner(m.amax0, m.n, (int)blockIdx.x);
+  amax_block(m.t[i], (int)blockIdx.x - m.amax0[i], red);
 }
 
 // The head's max from its partials; r = 448 / a (fp32, correctly rounded division).
@@ -93,9 +117,8 @@ __device__ __forceinline__ u32x2 cvt8(const u32x4 &x, float r) {
   return u32x2{out[0], out[1]};
 }
 
-__global__ void __launch_bounds__(kThreads) quant_convert_kernel(QuantArgs a) {
-  __shared__ float red[4];
-  const int bh = blockIdx.x / a.nsplit, sp = blockIdx.x % a.nsplit;
+__device__ __forceinline__ void convert_block(const QuantArgs &a, int blk, float *red) {
+  const int bh = blk / a.nsplit, sp = blk % a.nsplit;
   const int b = bh / a.H, h = bh % a.H;
   const float r = head_ratio(a, bh, sp == 0, red);
   const int r0 = sp * a.rows_per_split, r1 = min(a.S, r0 + a.rows_per_split);
@@ -115,10 +138,9 @@ __global__ void __launch_bounds__(kThreads) quant_convert_kernel(QuantArgs a) {
 constexpr int kTT = 64;           // tokens per tile
 constexpr int kTRow = kTT + 4;    // LDS row bytes (4-byte aligned, spreads banks)
 
-__global__ void __launch_bounds__(kThreads) quant_convert_t_kernel(QuantArgs a, int ntiles) {
-  __shared__ float red[4];
-  __shared__ __attribute__((aligned(16))) uint8_t tile[256 * kTRow];
-  const int bh = blockIdx.x / ntiles, tt = blockIdx.x % ntiles;
+__device__ __forceinline__ void convert_t_block(const QuantArgs &a, int blk, int ntiles,
+                                                float *red, uint8_t *tile) {
+  const int bh = blk / ntiles, tt = blk % ntiles;
   const int b = bh / a.H, h = bh % a.H;
   const float r = head_ratio(a, bh, tt == 0, red);
   const int t0 = tt * kTT;
@@ -144,6 +166,18 @@ __global__ void __launch_bounds__(kThreads) quant_convert_t_kernel(QuantArgs a, 
   }
 }
 
+// second pass of every tensor of the launch, transposed or not (a block-uniform branch)
+__global__ void __launch_bounds__(kThreads) quant_convert_kernel(QuantMulti m) {
+  __shared__ float red[4];
+  __shared__ __attribute__((aligned(16))) uint8_t tile[256 * kTRow];
+  const int i = owner(m.conv0, m.n, (int)blockIdx.x);
+  const int blk = (int)blockIdx.x - m.conv0[i];
+  if (m.t[i].transpose)
+    convert_t_block(m.t[i], blk, m.ntiles[i], red, tile);
+  else
+    convert_block(m.t[i], blk, red);
+}
+
 }  // namespace
 
 // Row ranges of the first pass: about 128 KiB of bf16 per block, at most 1024 per head.
@@ -155,21 +189,32 @@ void quant_split(int64_t S, int64_t D, int32_t &nsplit, int32_t &rows_per_split)
   rows_per_split = (int32_t)rps;
 }
 
-int launch_fp8_quantize(const QuantArgs &a, hipStream_t stream) {
-  const int64_t nbh = (int64_t)a.B * a.H;
-  if (nbh == 0) return RA_OK;
-  hipLaunchKernelGGL(quant_amax_kernel, dim3((unsigned)(nbh * a.nsplit)), dim3(kThreads), 0,
-                     stream, a);
-  if (a.transpose) {
-    // at least one tile per head, so that an empty head still gets its descale
-    const int ntiles = a.S_pad > 0 ? (a.S_pad + kTT - 1) / kTT : 1;
-    hipLaunchKernelGGL(quant_convert_t_kernel, dim3((unsigned)(nbh * ntiles)), dim3(kThreads),
-                         0, stream, a, ntiles);
-  } else {
-    hipLaunchKernelGGL(quant_convert_kernel, dim3((unsigned)(nbh * a.nsplit)), dim3(kThreads), 0,
-                       stream, a);
+int launch_fp8_quantize_n(const QuantArgs *a, int n, hipStream_t stream) {
+  QuantMulti m{};
+  int k = 0;
+  int64_t na = 0, nc = 0;
+  m.amax0[0] = m.conv0[0] = 0;
+  for (int i = 0; i < n; ++i) {
+    const int64_t nbh = (int64_t)a[i].B * a[i].H;
+    if (nbh == 0) continue;  // nothing to quantize, no descale to write
+    m.t[k] = a[i];
+    // transposed: at least one tile per head, so that an empty head gets its descale
+    m.ntiles[k] = a[i].transpose ? (a[i].S_pad > 0 ? (a[i].S_pad + kTT - 1) / kTT : 1) : 0;
+    na += nbh * a[i].nsplit;
+    nc += nbh * (a[i].transpose ? m.ntiles[k] : a[i].nsplit);
+    m.amax0[k + 1] = (int32_t)na;
+    m.conv0[k + 1] = (int32_t)nc;
+    ++k;
   }
+  if (k == 0) return RA_OK;
+  m.n = k;
+  hipLaunchKernelGGL(quant_amax_kernel, dim3((unsigned)na), dim3(kThreads), 0, stream, m);
+  hipLaunchKernelGGL(quant_convert_kernel, dim3((unsigned)nc), dim3(kThreads), 0, stream, m);
   return hipGetLastError() == hipSuccess ? RA_OK : RA_ERR_HIP;
+}
+
+int launch_fp8_quantize(const QuantArgs &a, hipStream_t stream) {
+  return launch_fp8_quantize_n(&a, 1, stream);
 }
 
 }  // namespace ra

@@ -130,6 +130,9 @@ struct QuantArgs {
 
 void quant_split(int64_t S, int64_t D, int32_t &nsplit, int32_t &rows_per_split);
 int launch_fp8_quantize(const QuantArgs &a, hipStream_t stream);
+// Several tensors (each with its own workspace partials) in one max launch and one
+// conversion launch.
+int launch_fp8_quantize_n(const QuantArgs *a, int n, hipStream_t stream);
 
 size_t bwd_workspace_bytes(int64_t B, int64_t Hq, int64_t Sq);
 // Bytes of the grouped-head dK/dV partials (0 without grouped heads); they follow the

@@ -283,6 +283,28 @@ def test_fp8_quantize_validation(ra):
     assert ra.lib().ra_fp8_quantize_workspace_size(ra.desc(x)) >= 3 * 4
 
 
+def test_fp8_quantize_multi_validation(ra):
+    """Several tensors in one call: each checked as alone; destinations (codes and
+    descales) may overlap no source and no other destination; n within 1..4."""
+    as8 = lambda t: t.view(torch.float8_e4m3fn)
+    q, k, v = _t((1, 4, 40, 128)), _t((1, 2, 40, 128)), _t((1, 2, 40, 128))
+    qc, kc = as8(torch.zeros(1, 4, 40, 128, dtype=torch.uint8)), \
+        as8(torch.zeros(1, 2, 40, 128, dtype=torch.uint8))
+    vt = as8(torch.zeros(1, 2, 128, 48, dtype=torch.uint8))
+    qd, kd, vd = torch.zeros(1, 4), torch.zeros(1, 2), torch.zeros(1, 2)
+    val = lambda *a: ra.STATUS[ra.fp8_quantize_multi_validate(*a)]
+    assert val([q, k, v], [qc, kc, vt], [qd, kd, vd], [0, 0, 1]) == "RA_OK"
+    assert val([q, k, v], [qc, kc, vt], [qd, kd, vd], [0, 0, 0]) == "RA_ERR_SHAPE"
+    assert val([q, k], [qc, kc], [qd, qd[:, :2]], [0, 0]) == "RA_ERR_STRIDE"  # shared descale
+    assert val([q, k], [qc, qc[:, :2]], [qd, kd], [0, 0]) == "RA_ERR_STRIDE"  # shared codes
+    assert val([q] * 5, [qc] * 5, [qd] * 5, [0] * 5) == "RA_ERR_RANGE"
+    assert val([], [], [], []) == "RA_ERR_RANGE"
+    sa = (ra.RaTensor * 3)(*[ra.desc(t) for t in (q, k, v)])
+    total = ra.lib().ra_fp8_quantize_n_workspace_size(3, sa)
+    singles = sum(ra.lib().ra_fp8_quantize_workspace_size(ra.desc(t)) for t in (q, k, v))
+    assert total == singles and total % 256 == 0
+
+
 def test_params_versions_and_work_counter(ra):
     """ra_attn_params: the version-1 block (no work counter) and the version-2 block are
     both accepted; a smaller struct_size is out of range; a work counter must be 8-byte

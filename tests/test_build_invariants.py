@@ -27,7 +27,7 @@ from long_context_exact_tiled_amd import build as B
 
 HOT = ("attn_fwd_direct_kernel", "attn_fwd_fp8_kernel", "bwd_dq_kernel", "bwd_dkdv_kernel",
        "lse_merge_kernel", "permute_kernel", "permute_rows_kernel", "quant_amax_kernel",
-       "quant_convert_kernel", "quant_convert_t_kernel", "bwd_delta_kernel")
+       "quant_convert_kernel", "bwd_delta_kernel")
 
 
 def _asm(src):

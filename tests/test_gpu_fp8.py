@@ -78,6 +78,33 @@ def test_quantize_bit_exact(case):
     assert bad.size == 0, f"{len(bad)} codes differ, first at {bad[:3].tolist()}"
 
 
+def test_quantize_multi_bit_exact():
+    """q, k (rows) and v (transposed) of different shapes in one two-launch call: every
+    code and descale bitwise the oracle's, and the same as three single calls."""
+    say("fp8 quantize multi")
+    rng = np.random.default_rng(5)
+    shapes = [((1, 7, 300, 128), False), ((1, 1, 300, 128), False), ((1, 1, 300, 128), True),
+              ((2, 3, 37, 64), True)]
+    xs, refs = [], []
+    for shape, t in shapes:
+        x = rng.standard_normal(shape).astype(np.float32) * rng.uniform(0.1, 30.0)
+        bits = si.bf16_bits(x)
+        c, d = ofp8.quantize_heads(si.bf16_bits_to_f32(bits))
+        refs.append((ofp8.transpose_codes(c) if t else c, d))
+        xs.append(_bf16_dev(bits))
+    outs = [torch.full(r[0].shape, 0x55, dtype=torch.uint8, device="cuda").view(
+        torch.float8_e4m3fn) for r in refs]
+    descs = [torch.full(r[1].shape, float("nan"), device="cuda") for r in refs]
+    ra.fp8_quantize_multi(xs, [t for _, t in shapes], outs=outs, descales=descs)
+    singles = [ra.fp8_quantize(x, transpose=t) for x, (_, t) in zip(xs, shapes)]
+    torch.cuda.synchronize()
+    for o, d, (cref, dref), (so, sd) in zip(outs, descs, refs, singles):
+        assert np.array_equal(d.cpu().numpy(), dref)
+        assert np.array_equal(_codes_np(o), cref)
+        assert torch.equal(o.view(torch.uint8), so.view(torch.uint8))
+        assert torch.equal(d, sd)
+
+
 def test_quantize_strided_source():
     """A [B, S, H, D] buffer viewed as [B, H, S, D] quantizes like its contiguous copy."""
     say("fp8 quantize strided source")
