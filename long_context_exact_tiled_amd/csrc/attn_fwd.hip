@@ -599,6 +599,9 @@ attn_fwd_direct_kernel(FwdArgs a) {
   for (int dt = 0; dt < D / 32; ++dt) o[dt] = f32x16{};
   float m_run = -INFINITY;
   float l_run = 0.f;
+  // exp2 offset -m_run (0 while m_run is -inf) and the rescale test's
+  // -(m_run + kLazyRescale), both changed only when m_run is
+  float mneg = 0.f, nthr = INFINITY;
 
   const int64_t vis_lim = a.q_offset + qlast - a.kv_offset + 1;
   int t = -1, kb = 0, kend = 0, cend = 0;
@@ -675,16 +678,19 @@ attn_fwd_direct_kernel(FwdArgs a) {
       for (int mt = 1; mt < NMT; ++mt)
 #pragma unroll
         for (int i = 0; i < 16; i += 2) mx = fmaxf(fmaxf(mx, s[mt][i]), s[mt][i + 1]);
-      mx = halves_max(mx) * c;
-      if (__builtin_amdgcn_ballot_w64(mx > m_run + kLazyRescale) != 0) {
-        const float m_new = fmaxf(m_run, mx);
+      mx = halves_max(mx);
+      // c mx > m_run + kLazyRescale, as one FMA against the loop-carried
+      // -(m_run + kLazyRescale)
+      if (__builtin_amdgcn_ballot_w64(fmaf(mx, c, nthr) > 0.f) != 0) {
+        const float m_new = fmaxf(m_run, mx * c);
         const float alpha = m_new == -INFINITY ? 1.f : fast_exp2(m_run - m_new);
         l_run *= alpha;
 #pragma unroll
         for (int dt = 0; dt < D / 32; ++dt) o[dt] *= alpha;
         m_run = m_new;
+        mneg = m_new == -INFINITY ? 0.f : -m_new;
+        nthr = -(m_new + kLazyRescale);
       }
-      const float mneg = m_run == -INFINITY ? 0.f : -m_run;
       typename Path::PFrag pf;
       l_run += Path::exp_pack(s, c, mneg, pf);
       Path::pv(o, pf, L, cur);

@@ -296,6 +296,9 @@ attn_fwd_fp8_kernel(Fp8Args a) {
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt) o[dt] = f32x16{};
   float m_run = -INFINITY;
+  // exp2 offset -m_run + kP8Shift (kP8Shift while m_run is -inf) and the rescale test's
+  // -(m_run + kLazyFp8), both changed only when m_run is
+  float mneg = kP8Shift, nthr = INFINITY;
   float l_run = 0.f;
 
   const int64_t vis_lim = f.q_offset + qlast - f.kv_offset + 1;
@@ -357,16 +360,18 @@ attn_fwd_fp8_kernel(Fp8Args a) {
       for (int mt = 1; mt < NMT; ++mt)
 #pragma unroll
         for (int i = 0; i < 16; i += 2) mx = fmaxf(fmaxf(mx, s[mt][i]), s[mt][i + 1]);
-      mx = halves_max(mx) * c;
-      if (__builtin_amdgcn_ballot_w64(mx > m_run + kLazyFp8) != 0) {
-        const float m_new = fmaxf(m_run, mx);
+      mx = halves_max(mx);
+      // c mx > m_run + kLazyFp8, as one FMA against the loop-carried -(m_run + kLazyFp8)
+      if (__builtin_amdgcn_ballot_w64(fmaf(mx, c, nthr) > 0.f) != 0) {
+        const float m_new = fmaxf(m_run, mx * c);
         const float alpha = m_new == -INFINITY ? 1.f : fast_exp2(m_run - m_new);
         l_run *= alpha;
 #pragma unroll
         for (int dt = 0; dt < D / 32; ++dt) o[dt] *= alpha;
         m_run = m_new;
+        mneg = (m_new == -INFINITY ? 0.f : -m_new) + kP8Shift;
+        nthr = -(m_new + kLazyFp8);
       }
-      const float mneg = (m_run == -INFINITY ? 0.f : -m_run) + kP8Shift;
       // P' -> e4m3, two values per conversion.  The first conversion of a dword fills its
       // low half and keeps the high half of its `old` operand, which the second
       // conversion overwrites: `old` is a score that is dead by then, so no register has
