@@ -49,6 +49,13 @@ QCASES = [  # shape, transpose, per-head magnitudes
     ((1, 1, 4096, 128), True, (3.0,)),
     ((1, 2, 1, 16), True, (1.0, 2.0)),
     ((1, 2, 0, 64), True, (1.0, 1.0)),              # no tokens: descale 1, nothing else
+    # row lengths whose 16-byte pieces do not divide a block's threads (48: 6 per row,
+    # 42 rows per pass, 4 threads idle) or fill it with few rows (256: 8 rows per pass),
+    # with several row ranges per head and ragged last passes
+    ((1, 2, 3001, 48), False, (2.0, 0.5)),
+    ((1, 2, 3001, 48), True, (2.0, 0.5)),
+    ((1, 1, 701, 256), False, (7.0,)),
+    ((1, 1, 701, 256), True, (7.0,)),
 ]
 
 
