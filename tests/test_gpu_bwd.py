@@ -84,6 +84,31 @@ def test_bwd_deterministic(Hkv):
         assert torch.equal(x, y)
 
 
+def test_qwen_gqa_causal_bwd_8k_whole_kv_head():
+    """Grouped heads at full width (Qwen2.5-7B heads, 28 query over 4 key/value heads,
+    8K causal): the workspace path (per-query-head dK/dV partials and their group sum).
+    Every element of one key/value head's dK, dV and of its 7 query heads' dQ is checked."""
+    q_shape, kv_shape = (1, 28, 8192, 128), (1, 4, 8192, 128)
+    say(f"gqa bwd 8k q {q_shape} kv {kv_shape}")
+    q, k, v, do = si.draw_qkv(1011, q_shape, kv_shape, "bf16", with_dout=True)
+    qd, kd, vd, dod = (to_dev(x, "bf16") for x in (q, k, v, do))
+    o, lse = ra.attn_fwd(qd, kd, vd, causal=True)
+    assert ra.attn_bwd_workspace_size(qd, kd, causal=True) > ra.attn_bwd_workspace_size(
+        qd, qd, causal=True)  # the partials are in use
+    dq, dk, dv = ra.attn_bwd(qd, kd, vd, o, dod, lse, causal=True)
+    torch.cuda.synchronize()
+    for t in (dq, dk, dv):
+        assert torch.isfinite(t).all()
+    g = 2
+    q64, k64, v64, do64 = (si.as_f64(x, "bf16") for x in (q, k, v, do))
+    ref = oracle.attention_bwd_heads(q64, k64, v64, do64, [(0, g)], causal=True, row_block=512)
+    rq, rk, rv = ref[(0, g)]
+    dq_n, dk_n, dv_n = (to_np64(t) for t in (dq, dk, dv))
+    check_grad(dq_n[0, 7 * g:7 * g + 7], rq, "dq heads 14-20")
+    check_grad(dk_n[0, g], rk, f"dk head {g}")
+    check_grad(dv_n[0, g], rv, f"dv head {g}")
+
+
 def test_llama_causal_bwd_16k_workload_sampled_heads():
     """Full-size backward; every element of three whole heads checked against the oracle."""
     w = si.WORKLOADS["llama7b_causal_bwd_16k"]
