@@ -69,26 +69,41 @@ static_assert(TN <= kMaxTileRows, "tile offsets are 32-bit");
 // not see these MFMAs, so every consumer is placed where no wait states are needed: a
 // score chain's results are first read two MFMAs (≥64 clk) after its last step, the
 // P/dS operands are written at least eight MFMAs before their use, chained
-// accumulators overlap exactly, and the epilogue waits explicitly.
+// accumulators overlap exactly, and the epilogue waits explicitly.  With D = 64 (about
+// 330 registers, well inside one wave's 512) the written-out forms only made the
+// register allocator copy the accumulators out of AGPRs inside the loop, so there W is
+// false and the compiler's own MFMAs (and hazard handling) are used.
 // dK or dV += A B (accumulator in AGPRs, A and B in VGPRs)
+template <bool W>
 __device__ __forceinline__ void mfma_grad(f32x16 &acc, const bf16x8 &a, const bf16x8 &b) {
-  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+  if constexpr (W)
+    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+  else
+    acc = mfma_bf16(a, b, acc);
 }
 // S or dP: first step of a chain (C = 0) and further steps; the B operand (the key/value
 // rows kept for the whole workgroup) is read straight from AGPRs, the result is a VGPR.
+template <bool W>
 __device__ __forceinline__ f32x16 mfma_score0_ab(const bf16x8 &a, const bf16x8 &b) {
+  if constexpr (!W) return mfma_bf16(a, b, f32x16{});
   f32x16 d;
   asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "a"(b));
   return d;
 }
+template <bool W>
 __device__ __forceinline__ f32x16 mfma_score_c_ab(const bf16x8 &a, const bf16x8 &b,
                                                    const f32x16 &c) {
+  if constexpr (!W) return mfma_bf16(a, b, c);
   f32x16 d;
   asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %3" : "=&v"(d) : "v"(a), "a"(b), "v"(c));
   return d;
 }
+template <bool W>
 __device__ __forceinline__ void mfma_score_ab(f32x16 &acc, const bf16x8 &a, const bf16x8 &b) {
-  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "a"(b));
+  if constexpr (W)
+    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "a"(b));
+  else
+    acc = mfma_bf16(a, b, acc);
 }
 
 // 16-byte-chunk swizzle of a tile row: for 16 consecutive rows at one chunk the physical
@@ -477,11 +492,14 @@ bwd_dkdv_kernel(BwdArgs a, int num_kv_tiles) {
     kf[ks] = as_bf16x8(*(const u32x4 *)(kb_ + (int64_t)kr * a.k_ss + 16 * ks + 8 * h));
     vf[ks] = as_bf16x8(*(const u32x4 *)(vb_ + (int64_t)kr * a.v_ss + 16 * ks + 8 * h));
   }
+  constexpr bool kW = D == 128;  // written-out MFMAs (see mfma_grad)
   // K^T and V^T are only ever MFMA B operands from here on: keep them in AGPRs
+  if (kW) {
 #pragma unroll
-  for (int ks = 0; ks < D / 16; ++ks) {
-    asm volatile("" : "+a"(kf[ks]));
-    asm volatile("" : "+a"(vf[ks]));
+    for (int ks = 0; ks < D / 16; ++ks) {
+      asm volatile("" : "+a"(kf[ks]));
+      asm volatile("" : "+a"(vf[ks]));
+    }
   }
 
   f32x16 dk[D / 32], dv[D / 32];
@@ -489,8 +507,10 @@ bwd_dkdv_kernel(BwdArgs a, int num_kv_tiles) {
   for (int dt = 0; dt < D / 32; ++dt) {
     dk[dt] = f32x16{};
     dv[dt] = f32x16{};
-    asm volatile("" : "+a"(dk[dt]));  // the accumulators live in AGPRs from the start
-    asm volatile("" : "+a"(dv[dt]));
+    if (kW) {
+      asm volatile("" : "+a"(dk[dt]));  // the accumulators live in AGPRs from the start
+      asm volatile("" : "+a"(dv[dt]));
+    }
   }
 
   // Q/dO tile loads by the last two waves only: issuing them holds those waves back, so
@@ -707,9 +727,9 @@ bwd_dkdv_kernel(BwdArgs a, int num_kv_tiles) {
       for (int i = 0; i < NST; ++i) {
         const bf16x8 A = as_bf16x8(op[i % kDep]);
         if (i < 2) {
-          if (i & 1) dp0 = mfma_score_c_ab(A, vf[0], nd0); else s0 = mfma_score0_ab(A, kf[0]);
+          if (i & 1) dp0 = mfma_score_c_ab<kW>(A, vf[0], nd0); else s0 = mfma_score0_ab<kW>(A, kf[0]);
         } else {
-          if (i & 1) mfma_score_ab(dp0, A, vf[i >> 1]); else mfma_score_ab(s0, A, kf[i >> 1]);
+          if (i & 1) mfma_score_ab<kW>(dp0, A, vf[i >> 1]); else mfma_score_ab<kW>(s0, A, kf[i >> 1]);
         }
         op[i % kDep] = operand(i + kDep);
         // the MFMA reads its C operand over several cycles: the -D registers are not
@@ -725,9 +745,9 @@ bwd_dkdv_kernel(BwdArgs a, int num_kv_tiles) {
         const int i = NST + j;
         const bf16x8 A = as_bf16x8(op[i % kDep]);
         if (j < 2) {
-          if (j & 1) dp1 = mfma_score_c_ab(A, vf[0], nd1); else s1 = mfma_score0_ab(A, kf[0]);
+          if (j & 1) dp1 = mfma_score_c_ab<kW>(A, vf[0], nd1); else s1 = mfma_score0_ab<kW>(A, kf[0]);
         } else {
-          if (j & 1) mfma_score_ab(dp1, A, vf[j >> 1]); else mfma_score_ab(s1, A, kf[j >> 1]);
+          if (j & 1) mfma_score_ab<kW>(dp1, A, vf[j >> 1]); else mfma_score_ab<kW>(s1, A, kf[j >> 1]);
         }
         op[i % kDep] = operand(i + kDep);
         if (j == 3) asm volatile("" ::"v"(nd1));
@@ -740,8 +760,8 @@ bwd_dkdv_kernel(BwdArgs a, int num_kv_tiles) {
         const int i = 2 * NST + j;
         const bf16x8 A = as_bf16x8(op[i % kDep]);
         const int pj = j >> 1, s2 = pj / (D / 32), dt = pj % (D / 32);
-        if (j & 1) mfma_grad(dk[dt], A, as_bf16x8(dsf0[s2]));
-        else mfma_grad(dv[dt], A, as_bf16x8(pf0[s2]));
+        if (j & 1) mfma_grad<kW>(dk[dt], A, as_bf16x8(dsf0[s2]));
+        else mfma_grad<kW>(dv[dt], A, as_bf16x8(pf0[s2]));
         op[i % kDep] = operand(i + kDep);
         if (j % (NST / 4) == 1) pds(s1, dp1, nm1, qv1, qpos0 + 32, 1, j / (NST / 4), pf1, dsf1);
         __builtin_amdgcn_sched_barrier(0);
@@ -752,8 +772,8 @@ bwd_dkdv_kernel(BwdArgs a, int num_kv_tiles) {
         const int i = 3 * NST + j;
         const bf16x8 A = as_bf16x8(op[i % kDep]);
         const int pj = j >> 1, s2 = pj / (D / 32), dt = pj % (D / 32);
-        if (j & 1) mfma_grad(dk[dt], A, as_bf16x8(dsf1[s2]));
-        else mfma_grad(dv[dt], A, as_bf16x8(pf1[s2]));
+        if (j & 1) mfma_grad<kW>(dk[dt], A, as_bf16x8(dsf1[s2]));
+        else mfma_grad<kW>(dv[dt], A, as_bf16x8(pf1[s2]));
         if (i + kDep < 4 * NST) op[i % kDep] = operand(i + kDep);
         __builtin_amdgcn_sched_barrier(0);
       }

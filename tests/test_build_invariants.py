@@ -253,12 +253,16 @@ def test_hazard_checker_flags_short_distances(body, expect):
 
 
 def test_inline_mfma_distances(asm):
-    """Every written-out MFMA of the dK/dV kernels (all instantiations) keeps the ISA's
-    distances to its readers and to writers of its SrcC registers."""
+    """Every written-out MFMA of the dK/dV kernels (every D = 128 instantiation; D = 64
+    has none) keeps the ISA's distances to its readers and to writers of its SrcC
+    registers."""
     fns = {n: b for n, b in _functions(asm["attn_bwd.hip"]).items() if "bwd_dkdv_kernel" in n}
     assert len(fns) >= 8, list(fns)
     for name, body in fns.items():
         n_asm = sum(1 for x in _program(body)[0] if x["asm"] and _is_xdl(x["op"]))
+        if "kernelILi64E" in name:  # D = 64 uses the compiler's MFMAs and wait states
+            assert n_asm == 0, (name, n_asm)
+            continue
         assert n_asm >= 32, (name, n_asm)  # the check is not vacuous
         bad = mfma_hazards(body)
         assert not bad, (name, bad[:5])
