@@ -69,6 +69,32 @@ def test_small_parity(case):
     _run_case(dtype, D, causal, B, Hq, Hkv, Sq, Skv, P, start, q_off, kv_off, seed=sum(map(ord, str(case))) % 997)
 
 
+@pytest.mark.parametrize("D,causal,P,start", [(128, True, 1, 0), (64, False, 1, 0),
+                                             (128, True, 4, 2), (64, True, 3, 1)])
+def test_running_max_moves(D, causal, P, start):
+    """Scores that grow along the key axis (keys scaled up to 9x) after three keys scaled
+    6x at the start: a row's first tile max is far above most later scores, and later
+    tiles rise far above it, so the running max has to move many times (about one tile in
+    five of these rows, by a CPU count of the rule) and the rescaled tiles include masked
+    diagonal ones."""
+    dtype, Sq, Skv = "bf16", 400, 1200
+    q_off = Skv - Sq if causal else 0
+    say(f"fwd running max D={D} causal={causal} P={P} start={start}")
+    q, k, v = si.draw_qkv(77 + D, (1, 2, Sq, D), (1, 2, Skv, D), dtype)
+    kf = si.bf16_bits_to_f32(k)
+    kf = kf * (np.float32(1.0) + np.arange(Skv, dtype=np.float32) / np.float32(150.0))[:, None]
+    kf[:, :, :3] *= np.float32(6.0)
+    k = si.bf16_bits(kf)
+    qd, kd, vd = to_dev(q, dtype), to_dev(k, dtype), to_dev(v, dtype)
+    o, lse = ra.attn_fwd(qd, kd, vd, causal=causal, num_chunks=P, start_chunk=start,
+                         q_offset=q_off)
+    torch.cuda.synchronize()
+    o_ref, l_ref = oracle.full_attention(si.as_f64(q, dtype), si.as_f64(k, dtype),
+                                         si.as_f64(v, dtype), causal=causal, q_offset=q_off)
+    check_o(to_np64(o), o_ref, dtype)
+    check_lse(to_np64(lse), l_ref, dtype)
+
+
 def test_fp32_partial_output_from_bf16():
     _run_case("bf16", 128, True, 1, 2, 2, 200, 400, 2, 1, 200, 0, seed=5, out_f32=True)
 
