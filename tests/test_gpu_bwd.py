@@ -56,6 +56,9 @@ CASES = [
     (1, 2, 2, 200, 200, 128, True, 1, 0, 0, 100),
     (1, 7, 1, 333, 333, 128, True, 1, 0, 0, 0),
     (1, 2, 2, 1, 1, 64, True, 1, 0, 0, 0),
+    (1, 3, 3, 700, 700, 64, True, 1, 0, 0, 0),     # 64-dim heads: several tiles, ragged tail
+    (1, 6, 2, 523, 523, 64, True, 1, 0, 0, 0),     # 64-dim grouped heads (partials)
+    (1, 2, 2, 300, 900, 64, True, 3, 2, 600, 0),   # 64-dim causal ring share
 ]
 
 
@@ -128,3 +131,25 @@ def test_llama_causal_bwd_16k_workload_sampled_heads():
         check_grad(dq_n[b, g:g + 1], rq, f"dq head {g}")
         check_grad(dk_n[b, g], rk, f"dk head {g}")
         check_grad(dv_n[b, g], rv, f"dv head {g}")
+
+
+def test_d64_causal_bwd_16k_whole_head():
+    """64-dim heads at full size (32 heads, 16K causal: the dK/dV kernel's two-waves-per-
+    SIMD form): every element of one head's dq, dk and dv against the oracle."""
+    q_shape = (1, 32, 16384, 64)
+    say(f"d64 bwd 16k {q_shape}")
+    q, k, v, do = si.draw_qkv(1012, q_shape, q_shape, "bf16", with_dout=True)
+    qd, kd, vd, dod = (to_dev(x, "bf16") for x in (q, k, v, do))
+    o, lse = ra.attn_fwd(qd, kd, vd, causal=True)
+    dq, dk, dv = ra.attn_bwd(qd, kd, vd, o, dod, lse, causal=True)
+    torch.cuda.synchronize()
+    for t in (dq, dk, dv):
+        assert torch.isfinite(t).all()
+    g = 21
+    q64, k64, v64, do64 = (si.as_f64(x, "bf16") for x in (q, k, v, do))
+    rq, rk, rv = oracle.attention_bwd_heads(q64, k64, v64, do64, [(0, g)], causal=True,
+                                            row_block=512)[(0, g)]
+    dq_n, dk_n, dv_n = (to_np64(t) for t in (dq, dk, dv))
+    check_grad(dq_n[0, g:g + 1], rq, f"dq head {g}")
+    check_grad(dk_n[0, g], rk, f"dk head {g}")
+    check_grad(dv_n[0, g], rv, f"dv head {g}")
