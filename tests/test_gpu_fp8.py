@@ -166,6 +166,8 @@ CASES = [
     (1, 2, 2, 200, 200, 128, True, 1, 0, 0, 100),   # rows with no visible key
     (1, 2, 2, 1, 1, 64, True, 1, 0, 0, 0),
     (1, 2, 2, 64, 0, 128, False, 1, 0, 0, 0),       # no keys at all
+    (1, 6, 2, 700, 700, 64, True, 1, 0, 0, 0),      # 64-dim grouped heads, several tiles
+    (1, 2, 2, 256, 768, 64, True, 3, 1, 256, 0),    # 64-dim causal ring share, fused
 ]
 
 
