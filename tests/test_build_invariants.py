@@ -176,11 +176,11 @@ def mfma_hazards(fn_text):
             if d >= need or best.get(j, 1 << 30) <= d:
                 continue
             best[j] = d
-            verdict = hit(ins[j])
-            if verdict == "bad":
+            kind = hit(ins[j])
+            if kind == "bad":
                 found.append((d, ins[j]["text"]))
                 continue
-            if verdict == "stop":
+            if kind == "stop":
                 continue
             stack.extend((s, d + _cost(ins[j])) for s in succ(j))
         return found
