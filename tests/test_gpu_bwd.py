@@ -59,6 +59,7 @@ CASES = [
     (1, 3, 3, 700, 700, 64, True, 1, 0, 0, 0),     # 64-dim heads: several tiles, ragged tail
     (1, 6, 2, 523, 523, 64, True, 1, 0, 0, 0),     # 64-dim grouped heads (partials)
     (1, 2, 2, 300, 900, 64, True, 3, 2, 600, 0),   # 64-dim causal ring share
+    (2, 4, 1, 300, 300, 128, True, 1, 0, 0, 0),    # two batches of grouped heads (partials)
 ]
 
 

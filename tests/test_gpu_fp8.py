@@ -168,6 +168,7 @@ CASES = [
     (1, 2, 2, 64, 0, 128, False, 1, 0, 0, 0),       # no keys at all
     (1, 6, 2, 700, 700, 64, True, 1, 0, 0, 0),      # 64-dim grouped heads, several tiles
     (1, 2, 2, 256, 768, 64, True, 3, 1, 256, 0),    # 64-dim causal ring share, fused
+    (2, 3, 1, 250, 250, 128, True, 1, 0, 0, 0),     # two batches, work-counter order
 ]
 
 
